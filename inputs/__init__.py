@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs for the routed-expert MoE layer.
+
+This module is shared by the tests, the oracle harness and bench.py.  It holds
+none of the layer's arithmetic (no decode, no router, no softmax, no expert):
+it only draws numbers and encodes them into the formats the layer consumes.
+
+Expert blobs come from a counter-based generator so that the host (this file,
+numpy) and the device (inputs/fill.hip) produce identical bytes for any
+(seed, blob id) without transferring 34 GB:
+
+  SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom number
+  generators", OOPSLA 2014; constants of Vigna's splitmix64.c):
+      mix(z)  = z ^= z >> 30; z *= 0xBF58476D1CE4E5B9;
+                z ^= z >> 27; z *= 0x94D049BB133111EB; z ^ (z >> 31)
+      out(state, i) = mix(state + (i + 1) * 0x9E3779B97F4A7C15)   (i >= 0)
+
+  blob key    k(seed, b) = out(out(seed, 0), b),  b = layer * E + expert
+  blob word   W(seed, b, i) = out(k(seed, b), i)
+  block n of a blob (byte offset 18 n, gate then up then down):
+      bytes 2..9   = little-endian W(3n),  bytes 10..17 = little-endian W(3n+1)
+      bytes 0..1   = SCALE_TABLE[W(3n+2) >> 48]   (little-endian fp16)
+
+SCALE_TABLE[i] = fp16_rne(0.01 * Q((i + 0.5) / 65536) + 1e-4), Q the half-normal
+quantile, i.e. a 16-bit inverse-CDF draw of |N(0, 0.01)| + 1e-4 (the scale law
+of the workload); the table is computed here once and handed to the device.
+
+x, routers and Zipf biases use numpy's PCG64 streams spawned from
+SeedSequence(seed): [x, routers, bias, x redraws, router redraws].
+"""
+import numpy as np
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+M1 = np.uint64(0xBF58476D1CE4E5B9)
+M2 = np.uint64(0x94D049BB133111EB)
+
+# Layer geometry of the workload (48 layers x 512 experts, top-10, H=2560, FF=640).
+H, FF, E, K, L = 2560, 640, 512, 10, 48
+QK, BB = 64, 18
+
+
+def _mix(z):
+    z = (z ^ (z >> np.uint64(30))) * M1
+    z = (z ^ (z >> np.uint64(27))) * M2
+    return z ^ (z >> np.uint64(31))
+
+
+def splitmix64(state, idx):
+    """Outputs number idx (array, 0-based) of the SplitMix64 stream at `state`."""
+    with np.errstate(over="ignore"):
+        st = np.uint64(state)
+        i = np.asarray(idx, dtype=np.uint64)
+        return _mix(st + (i + np.uint64(1)) * GAMMA)
+
+
+def blob_key(seed, blob_id):
+    base = splitmix64(np.uint64(seed), np.array([0], dtype=np.uint64))[0]
+    return splitmix64(base, np.array([blob_id], dtype=np.uint64))[0]
+
+
+_TABLE = None
+
+
+def scale_table():
+    """uint16[65536] fp16 bit patterns of the scale law (see module doc)."""
+    global _TABLE
+    if _TABLE is None:
+        from scipy.special import ndtri
+        u = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
+        z = ndtri(0.5 + 0.5 * u)  # half-normal quantile
+        _TABLE = (0.01 * z + 1e-4).astype(np.float16).view(np.uint16).copy()
+    return _TABLE
+
+
+def blob_bytes(h=H, ff=FF):
+    return 3 * (h * ff * BB // QK)
+
+
+def gen_blob(seed, blob_id, h=H, ff=FF):
+    """The bytes of blob `blob_id` (= layer * E + expert) as uint8[blob_bytes]."""
+    nblk = 3 * h * ff // QK
+    key = blob_key(seed, blob_id)
+    n = np.arange(nblk, dtype=np.uint64)
+    w0 = splitmix64(key, np.uint64(3) * n)
+    w1 = splitmix64(key, np.uint64(3) * n + np.uint64(1))
+    w2 = splitmix64(key, np.uint64(3) * n + np.uint64(2))
+    out = np.empty((nblk, BB), dtype=np.uint8)
+    sc = scale_table()[(w2 >> np.uint64(48)).astype(np.int64)]
+    out[:, 0:2] = sc.astype("<u2").view(np.uint8).reshape(nblk, 2)
+    out[:, 2:10] = w0.astype("<u8").view(np.uint8).reshape(nblk, 8)
+    out[:, 10:18] = w1.astype("<u8").view(np.uint8).reshape(nblk, 8)
+    return out.reshape(-1)
+
+
+def f32_to_bf16_bits(a):
+    """Round-to-nearest-even of float32 values to bfloat16 bit patterns."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+class Streams:
+    """The five numpy streams of one seed, in the fixed spawn order."""
+
+    def __init__(self, seed):
+        ch = np.random.SeedSequence(seed).spawn(5)
+        self.x, self.router, self.bias, self.x_redraw, self.router_redraw = (
+            np.random.Generator(np.random.PCG64(c)) for c in ch)
+
+
+def draw_x(rng, T, h=H):
+    return rng.standard_normal((T, h)).astype(np.float32)
+
+
+def draw_router(rng, e=E, h=H):
+    """bf16(N(0, 0.02)) router [E][H] as uint16 bit patterns."""
+    return f32_to_bf16_bits((rng.standard_normal((e, h)) * 0.02).astype(np.float32))
+
+
+def draw_zipf_bias(rng, e=E, s=1.1):
+    """b_e = -s * ln(rank_e), rank = a seeded permutation of 1..E (fp32)."""
+    rank = rng.permutation(e).astype(np.float64) + 1.0
+    return (-s * np.log(rank)).astype(np.float32)
+
+
+# The five workload configurations: tokens, layers, seed, stack flags.
+CONFIGS = {
+    0: dict(name="layer-T1", T=1, layers=1, seed=0, stack=False, zipf=False, chunk=1),
+    1: dict(name="layer-T4-window", T=4, layers=1, seed=1, stack=False, zipf=False, chunk=4),
+    2: dict(name="stack48-T1", T=1, layers=48, seed=2, stack=True, zipf=False, chunk=1),
+    3: dict(name="layer-T2048-prefill", T=2048, layers=1, seed=3, stack=False, zipf=False,
+            chunk=2048),
+    4: dict(name="stack48-T32768-zipf", T=32768, layers=48, seed=4, stack=True, zipf=True,
+            chunk=2048),
+}
