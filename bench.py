@@ -1,0 +1,273 @@
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+Default workload: one MoE layer, T = 4 verify-window tokens (1 committed +
+3 drafts), 512 Q2_0 experts, top-10 -- the decode-window configuration the
+headline metric (routed-expert GB/s and tok/s per MoE layer) is quoted on.
+A step is one whole layer call: RMSNorm-free router GEMV, softmax/top-10,
+grouping, the experts (each distinct expert's 1,382,400-byte blob read once)
+and the combine.  The working set of one layer (~54 MB) would sit in the
+256 MB Infinity Cache on repeats, so the timed steps cycle over 48 copies of
+the layer's store (and router) at distinct HBM addresses; every step reads
+cold memory and computes the same result.
+
+Other workloads (--workload): token (T = 1 layer), stack-decode (48-layer
+T = 1 stack on the full 34 GB store), prefill (T = 2048 layer), stack-prefill
+(one 2048-token chunk through 48 Zipf-biased layers).
+
+Prints one JSON line.  With --gpus > 1 it exits: this build measures one GPU.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
+FLOP_PER_SLOT = 3 * 2 * 2560 * 640
+
+WORKLOADS = {
+    "window": dict(cfg=1, T=4, layers=1, copies=48),
+    "token": dict(cfg=0, T=1, layers=1, copies=48),
+    "stack-decode": dict(cfg=2, T=1, layers=48, copies=1),
+    "prefill": dict(cfg=3, T=2048, layers=1, copies=4),
+    "stack-prefill": dict(cfg=4, T=2048, layers=48, copies=1),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--warmup", type=int, default=48)
+    ap.add_argument("--workload", default="window", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--eager", action="store_true", help="time eager calls instead of graphs")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="only run a device copy of this many MB (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the layer shards by tokens with no collective; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if a.calibrate_copy_mb:
+        n = a.calibrate_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
+        return
+    import inputs
+    import quantized_routed_expert_router_amd as m
+    m.lib()
+    wl = WORKLOADS[a.workload]
+    cfg = inputs.CONFIGS[wl["cfg"]]
+    T, L, seed = wl["T"], wl["layers"], cfg["seed"]
+    stack = L > 1
+    flags = (m.RMSNORM | m.RESIDUAL) if stack else 0
+    st = inputs.Streams(seed)
+    x = inputs.draw_x(st.x, T)
+    routers = [inputs.draw_router(st.router) for _ in range(L)]
+    biases = [inputs.draw_zipf_bias(st.bias) for _ in range(L)] if cfg["zipf"] else None
+    blob = inputs.blob_bytes()
+    per_layer = 512 * blob
+
+    # Device state: stores (copies of the same layer for single-layer runs,
+    # the 48 distinct layers for stacks), routers, workspace, outputs.
+    copies = wl["copies"] if not stack else 1
+    n_store = L if stack else copies
+    store = torch.empty(n_store * per_layer, dtype=torch.uint8, device="cuda")
+    for i in range(n_store):
+        inputs.fill_blobs_device(store[i * per_layer:(i + 1) * per_layer], seed,
+                                 (i if stack else 0) * 512, 512)
+    Rd = [torch.from_numpy(R.view(np.int16)).cuda() for R in routers]
+    if not stack:
+        Rd = [Rd[0].clone() for _ in range(copies)]
+    bd = None if biases is None else [torch.from_numpy(b).cuda() for b in biases]
+    x0 = torch.from_numpy(x).cuda()
+    xd = x0.clone()
+    ws = m.workspace(T)
+    y = torch.empty_like(xd)
+    ids = torch.empty((T, 10), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 10), device="cuda")
+    torch.cuda.synchronize()
+
+    def one_step(i, stream=None):
+        if stack:
+            for l in range(L):
+                m.strata_moe_layer(xd, Rd[l], store[l * per_layer:(l + 1) * per_layer], ws,
+                                   bias=None if bd is None else bd[l], flags=flags, y=y, ids=ids,
+                                   w=w, stream=stream)
+        else:
+            c = i % copies
+            m.strata_moe_layer(xd, Rd[c], store[c * per_layer:(c + 1) * per_layer], ws,
+                               bias=None, flags=flags, y=y, ids=ids, w=w, stream=stream)
+
+    # Routing facts of the workload (from the GPU's own ids).
+    one_step(0)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    distinct = int(np.unique(ids_h).size)
+    if stack:
+        xd.copy_(x0)
+
+    # Timed region: graphs of `chunk` steps replayed, or eager calls.
+    stream = torch.cuda.Stream()
+    chunk = copies if not stack else 1
+    graph = None
+    if not a.eager:
+        graph = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(chunk):
+                    one_step(i, stream=stream)
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+    steps = max(chunk, (a.steps // chunk) * chunk)
+    warm = max(chunk, (a.warmup // chunk) * chunk) if a.warmup > 0 else 0
+
+    def run(n):
+        with torch.cuda.stream(stream):
+            if graph is not None:
+                for _ in range(n // chunk):
+                    graph.replay()
+            else:
+                for i in range(n):
+                    one_step(i, stream=stream)
+
+    run(warm)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    run(steps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+
+    # Dominant stage, timed live with HIP events on its own stream: the experts
+    # (strata_moe_experts: activation prep + gate/up kernel + down kernel).
+    offsets = torch.empty(513, dtype=torch.int32, device="cuda")
+    slots = torch.empty(T * 10, dtype=torch.int32, device="cuda")
+    active = torch.empty(513, dtype=torch.int32, device="cuda")
+    out = torch.empty((T * 10, 2560), device="cuda")
+    xe = x0.clone()
+    with torch.cuda.stream(stream):
+        m.strata_moe_route(xe, Rd[0], ids, w, ws, bias=None if bd is None else bd[0],
+                           flags=flags & m.RMSNORM, stream=stream)
+        m.strata_moe_group(ids, offsets, slots, active, ws, stream=stream)
+    torch.cuda.synchronize()
+    d_layer0 = int(np.unique(ids.cpu().numpy()).size)
+    n_ex = max(copies * 4, 48)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ex)]
+    with torch.cuda.stream(stream):
+        for i in range(n_ex):
+            c = i % copies
+            evs[i][0].record(stream)
+            m.strata_moe_experts(xe, store[c * per_layer:(c + 1) * per_layer], offsets, slots,
+                                 active, out, ws, flags=flags & m.RMSNORM, stream=stream)
+            evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ex_ms = float(np.mean([s.elapsed_time(e) for s, e in evs[copies:]] or
+                          [s.elapsed_time(e) for s, e in evs]))
+    ex_bytes = d_layer0 * blob
+
+    # Throughput of the whole step.
+    if stack:
+        step_bytes = None
+        tok_s = T / (ms / 1e3)
+        layer_ms = ms / L
+    else:
+        step_bytes = distinct * blob
+        tok_s = T / (ms / 1e3)
+        layer_ms = ms
+    prefill = T > 16
+    if prefill:
+        flops = T * 10 * FLOP_PER_SLOT
+        roof = {"bound": "mfma", "achieved": flops / (ex_ms / 1e3) / 1e12,
+                "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": ex_bytes / (ex_ms / 1e3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "experts stage (prep_kernel + dec_gateup + dec_down)" if not prefill else \
+        "experts stage (prep_kernel + plan_kernel + pf_gateup + pf_down)"
+    roof["ms_per_launch"] = ex_ms
+
+    if stack:
+        value, unit, metric = tok_s, "tok/s", "routed-expert tok/s, 48-layer stack"
+    elif prefill:
+        value, unit, metric = tok_s, "tok/s", "routed-expert tok/s per MoE layer (prefill)"
+    else:
+        value = step_bytes / (ms / 1e3) / 1e9
+        unit, metric = "GB/s", "routed-expert GB/s per MoE layer (decode)"
+
+    res = {
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16-mfma/f32-acc" if prefill else "i4dot-16bit/f32-acc",
+        "data": "synthetic (seeded generator; no trained weights)",
+        "config": {"workload": f"{a.workload}: config {wl['cfg']} ({cfg['name']}), T={T}, "
+                               f"layers={L}, 512 Q2_0 experts, top-10",
+                   "global_batch": T, "seq_len": 1 if not prefill else T,
+                   "parallelism": "single GPU", "timing": "eager" if a.eager else "hipGraph replay",
+                   "store_copies": copies},
+        "tok_per_s": tok_s, "layer_ms": layer_ms, "distinct_experts": distinct,
+        "expert_bytes_per_step": step_bytes, "wall_s": wall,
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(a, x, routers, biases, seed, stack, T, blob)
+    print(json.dumps(res))
+
+
+def cpu_baseline(a, x, routers, biases, seed, stack, T, blob):
+    """The oracle timed on the host cores on a bounded sample of the same
+    workload: whole layers (route, experts, combine) for the workload's first
+    layer, repeated until --cpu-seconds have passed (at most 64 tokens)."""
+    import oracle
+    import oracle.screen as scr
+    n = min(T, 64 if T > 16 else T)
+    xs = x[:n]
+    R = routers[0]
+    b = None if biases is None else biases[0]
+    src = scr.BlobSource(seed)
+    ids, _, _ = oracle.route(xs, R, 10, bias=b, rmsnorm_flag=stack)
+    src.get_many(np.unique(ids))          # input generation, not timed
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ids, w, y = scr.oracle_layer(xs, R, src, 0, bias=b, rmsnorm=stack)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= a.cpu_seconds or reps >= 1000:
+            break
+    distinct = int(np.unique(ids).size)
+    per_rep = el / reps
+    if T <= 16 and not stack:
+        value, unit = distinct * blob / per_rep / 1e9, "GB/s"
+    else:
+        value, unit = n / per_rep, "tok/s (one layer)"
+    return {"value": value, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} x one layer on {n} token(s) of the workload ({distinct} distinct "
+                      f"experts), {el:.1f} s", "seconds_per_layer": per_rep}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+/*
+ * strata_moe.h -- C ABI of the routed-expert MoE layer on MI355X (gfx950).
+ *
+ * One MoE layer of a 48-layer, 512-expert, top-10 model with H = 2560 and
+ * FF = 640.  The pages this follows are cited by title and section:
+ *
+ *  [SRC]  "Strata in the source: one verify window, three workers and a cache
+ *          that learns" (ai.thesatyajit.com).
+ *  [ZW]   "MoE 遇上消费级显卡动态路由专家权重12GB 怎么装下 125B 不爆显存"
+ *          (zwxr.cn), the passage that follows one token through one layer
+ *          (算 logits / 选 top-10 / 命中与未命中拆分 / Combine).
+ *  [MY]   the momoyeyu.github.io Strata explainer (ai-infra-strata),
+ *          section 提示词处理 (prompt processing).
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers unless stated otherwise, row-major, owned by
+ *    the caller.  The library never allocates or frees inside these calls and
+ *    keeps no pointer after it returns; enqueued kernels use the buffers until
+ *    the stream passes them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *  - Arguments are validated on the host before anything is enqueued: a call
+ *    that returns an error enqueued nothing.  No call synchronises the host,
+ *    reads device memory from the host, or uses memset, so calls may be
+ *    captured into a HIP graph.  Device faults surface at the caller's next
+ *    synchronisation.
+ *  - Results are deterministic: the same inputs and T give the same bits
+ *    (no floating-point atomics anywhere).
+ *  - Alignment: `blobs` and `ws` 256 bytes; x, y, out and router 16 bytes;
+ *    every other array 4 bytes.  A violation returns STRATA_E_ALIGN.
+ */
+#ifndef STRATA_MOE_H_INCLUDED
+#define STRATA_MOE_H_INCLUDED
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define STRATA_API __attribute__((visibility("default")))
+#else
+#define STRATA_API
+#endif
+
+/* Layer geometry, fixed at compile time ([SRC] "The byte budget, in code";
+ * [ZW] 48 x 512 experts, top-10). */
+#define STRATA_MOE_H 2560      /* hidden size */
+#define STRATA_MOE_FF 640      /* expert intermediate width */
+#define STRATA_MOE_E 512       /* routed experts per layer */
+#define STRATA_MOE_K 10        /* experts per token */
+#define STRATA_MOE_QK 64       /* weights per Q2_0 block */
+#define STRATA_MOE_BB 18       /* bytes per Q2_0 block: fp16 scale, 16 code bytes */
+#define STRATA_MOE_BLOB 1382400 /* bytes per expert blob: gate, up, down */
+#define STRATA_MOE_T_MAX 8192  /* largest token count per call (one prefill chunk) */
+
+/* Status codes. */
+#define STRATA_OK 0
+#define STRATA_E_ARG (-1)       /* NULL pointer or bad flag */
+#define STRATA_E_SHAPE (-2)     /* T outside 1..STRATA_MOE_T_MAX */
+#define STRATA_E_WORKSPACE (-3) /* workspace missing or smaller than required */
+#define STRATA_E_HIP (-4)       /* the HIP runtime reported a launch error */
+#define STRATA_E_ALIGN (-5)     /* a pointer breaks the alignment rule above */
+
+/* Flags. */
+#define STRATA_RMSNORM 1  /* normalise x first: x / sqrt(mean(x^2) + 1e-6), unit gain */
+#define STRATA_RESIDUAL 2 /* combine adds into its output (x += y) instead of storing */
+
+/* Bytes of one Q2_0 expert blob (1,382,400): the gate [FF][H], up [FF][H] and
+ * down [H][FF] matrices in that order, each row a run of 18-byte blocks along
+ * the matrix's input dimension; a block is a little-endian fp16 scale d
+ * followed by 16 bytes holding 64 two-bit codes, code i at bits 2i..2i+1 of
+ * the little-endian 128-bit field; code c means weight (c - 1) * d
+ * ([SRC] "The byte budget, in code" and "The CPU kernels").  A layer's store
+ * is 512 blobs back to back, expert e at e * STRATA_MOE_BLOB. */
+STRATA_API size_t strata_moe_blob_bytes(void);
+
+/* Workspace bytes a call with T tokens needs (0 if T is out of range).  Every
+ * entry point below that takes `ws` needs at least this much for its T. */
+STRATA_API size_t strata_moe_workspace_bytes(int T);
+
+/* Router ([ZW] 算 logits, 选 top-10): per token, logits = xhat . R^T (+ bias)
+ * with R in bf16 and fp32 accumulation, softmax over all 512 experts, a stable
+ * descending sort (equal probabilities keep the lower expert id first), the
+ * first 10 ids, and weights p_k / max(sum of the 10 p, 2^-14).
+ *   x      [T][H] fp32 activations; xhat = x, or RMSNorm(x) with STRATA_RMSNORM.
+ *   router [E][H] bf16 bit patterns.
+ *   bias   [E] fp32 added to the logits before the softmax, or NULL.
+ *   ids    [T][K] int32 out: expert ids in descending-weight order.
+ *   w      [T][K] fp32 out: renormalised weights (sum 1 per token).
+ * Returns STRATA_OK or an error code. */
+STRATA_API int strata_moe_route(const float *x, int T, const uint16_t *router, const float *bias,
+                     int flags, int32_t *ids, float *w, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Token -> expert grouping ([MY] 提示词处理: collect tokens per expert so one
+ * weight read serves every token routed to it; [SRC] "The plan: three
+ * destinations per expert": a window's routed ids are deduplicated first).
+ *   ids     [T][K] int32 in, values in 0..511 (others are dropped).
+ *   offsets [E+1] int32 out: exclusive prefix sum of per-expert slot counts.
+ *   slots   [T*K] int32 out: flat slot ids t*K+k ordered by expert, stable
+ *           (ascending slot id within an expert).
+ *   active  [1+E] int32 out: active[0] = number of experts with at least one
+ *           slot, active[1..] those expert ids in ascending order. */
+STRATA_API int strata_moe_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
+                     int32_t *active, void *ws, size_t ws_bytes, void *stream);
+
+/* Expert FFNs (SwiGLU): for every grouped slot s = t*K+k of expert e,
+ *   out[s] = W_d (silu(W_g xhat_t) * (W_u xhat_t)),  silu(z) = z / (1 + e^-z),
+ * reading each active expert's blob once for all of its tokens.
+ *   x       [T][H] fp32; xhat as in strata_moe_route (STRATA_RMSNORM).
+ *   blobs   [E][BLOB] bytes, one layer's store (256-byte aligned).
+ *   offsets, slots, active: as written by strata_moe_group for the same T.
+ *   out     [T*K][H] fp32 out, unweighted expert outputs by flat slot id.
+ * Decode-sized T uses a bandwidth-bound dot-product kernel with 16-bit
+ * activations per 32-value segment; larger T uses fp16 MFMA grouped GEMMs
+ * with exactly dequantised weights; both accumulate in fp32. */
+STRATA_API int strata_moe_experts(const float *x, int T, const uint8_t *blobs, const int32_t *offsets,
+                       const int32_t *slots, const int32_t *active, int flags, float *out,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Weighted combine ([ZW] Combine: sum of w[i] * parts[i]):
+ *   y[t] = sum over k = 0..9 in routing order of w[t][k] * out[t*K+k];
+ * with STRATA_RESIDUAL, y[t] += that sum instead.
+ *   out [T*K][H] fp32 in, w [T][K] fp32 in, y [T][H] fp32 out (or in/out). */
+STRATA_API int strata_moe_combine(const float *out, const float *w, int T, int flags, float *y,
+                       void *stream);
+
+/* The whole layer in one call: route -> group -> experts -> combine.
+ *   x      [T][H] fp32 in; with STRATA_RESIDUAL also out (x += layer output).
+ *   y      [T][H] fp32 out (layer output without residual), or NULL; must not
+ *          be NULL unless STRATA_RESIDUAL is set.
+ *   ids, w [T][K] out, or NULL to keep them in the workspace.
+ * Other arguments as above.  Results equal the four-call composition. */
+STRATA_API int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
+                     const uint8_t *blobs, int flags, float *y, int32_t *ids, float *w,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Human-readable text of a status code (static storage). */
+STRATA_API const char *strata_moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STRATA_MOE_H_INCLUDED */

@@ -133,3 +133,51 @@ CONFIGS = {
     4: dict(name="stack48-T32768-zipf", T=32768, layers=48, seed=4, stack=True, zipf=True,
             chunk=2048),
 }
+
+
+# ---------------------------------------------------------------- device side
+_fill_lib = None
+_tables = {}
+
+
+def _fill_library():
+    global _fill_lib
+    if _fill_lib is None:
+        import ctypes
+        import os
+        from . import build as _b
+        if not os.path.exists(_b.LIB):
+            raise RuntimeError(f"{_b.LIB} is missing: run __graft_entry__.build()")
+        L = ctypes.CDLL(_b.LIB)
+        L.strata_inputs_fill_blobs.restype = ctypes.c_int
+        L.strata_inputs_fill_blobs.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_void_p, ctypes.c_void_p]
+        _fill_lib = L
+    return _fill_lib
+
+
+def fill_blobs_device(dst, seed, first_blob, n_blobs, h=H, ff=FF, stream=None):
+    """Write blobs first_blob .. first_blob+n_blobs-1 of `seed` into the uint8
+    CUDA tensor dst (at its start), byte-identical to gen_blob()."""
+    import torch
+    need = n_blobs * blob_bytes(h, ff)
+    if dst.numel() < need or dst.dtype != torch.uint8 or not dst.is_cuda:
+        raise ValueError("destination too small or not a uint8 GPU tensor")
+    key = str(dst.device)
+    if key not in _tables:
+        _tables[key] = torch.from_numpy(scale_table().view(np.int16).copy()).to(dst.device)
+    s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    rc = _fill_library().strata_inputs_fill_blobs(dst.data_ptr(), int(seed), int(first_blob),
+                                                  int(n_blobs), h, ff, _tables[key].data_ptr(), s)
+    if rc != 0:
+        raise RuntimeError(f"strata_inputs_fill_blobs failed with {rc}")
+
+
+def layer_store(seed, layer, device="cuda", n_layers=1, e=E):
+    """A device tensor holding n_layers consecutive layer stores (layer-major,
+    e blobs each) starting at `layer`, generated on the device."""
+    import torch
+    store = torch.empty(n_layers * e * blob_bytes(), dtype=torch.uint8, device=device)
+    fill_blobs_device(store, seed, layer * e, n_layers * e)
+    return store

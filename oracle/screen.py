@@ -1,0 +1,126 @@
+"""Oracle-side harness for the workload configurations -- TEST INFRASTRUCTURE.
+
+Near-tie protocol: expert ids must be compared bit-exactly, which is only
+well posed when no two of the 11 largest router logits of a token lie within
+a margin (1e-4 for single layers; stacks use a wider margin because the GPU's
+residual stream drifts from the fp64 one by rounding).  Rows (or, for the T=1
+stack, routers) that fail are redrawn from the dedicated redraw streams of
+inputs.Streams.  The screen needs logits only to decide which inputs to keep,
+so it uses a numpy fp64 matmul; everything compared against the GPU comes from
+the oracle library.
+"""
+import concurrent.futures
+
+import numpy as np
+
+import inputs
+
+from . import experts as _experts, route as _route, combine as _combine
+
+TIE_MARGIN = 1e-4
+
+
+def bf16_values(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def rms_np(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + 1e-6)
+
+
+def logits_np(xhat, R_bits, bias=None):
+    lg = np.asarray(xhat, dtype=np.float64) @ bf16_values(R_bits).astype(np.float64).T
+    if bias is not None:
+        lg = lg + np.asarray(bias, dtype=np.float64)
+    return lg
+
+
+def top11_gap(lg):
+    """Smallest gap between consecutive values among the 11 largest, per row."""
+    s = -np.sort(-np.atleast_2d(lg), axis=1)[:, :11]
+    return np.min(s[:, :-1] - s[:, 1:], axis=1)
+
+
+def screened_x(st, T, R_bits, bias=None, rmsnorm=False, margin=TIE_MARGIN, h=inputs.H):
+    """x [T][H] from st.x; rows whose top-11 gap is within `margin` are redrawn
+    from st.x_redraw, in row order.  Returns (x, number of redrawn rows)."""
+    x = inputs.draw_x(st.x, T, h=h)
+    redrawn = 0
+    for _ in range(1000):
+        xh = rms_np(x) if rmsnorm else x.astype(np.float64)
+        bad = np.nonzero(top11_gap(logits_np(xh, R_bits, bias)) <= margin)[0]
+        if bad.size == 0:
+            return x, redrawn
+        for t in bad:
+            x[t] = inputs.draw_x(st.x_redraw, 1, h=h)[0]
+            redrawn += 1
+    raise RuntimeError("near-tie screen did not converge")
+
+
+class BlobSource:
+    """Host blobs of one seed, generated on demand (threaded) and cached."""
+
+    def __init__(self, seed, e=inputs.E, cache=4096):
+        self.seed, self.e, self.cache, self.store = seed, e, cache, {}
+
+    def get_many(self, blob_ids):
+        need = [b for b in set(int(b) for b in blob_ids) if b not in self.store]
+        if need:
+            with concurrent.futures.ThreadPoolExecutor(8) as ex:
+                for b, arr in zip(need, ex.map(lambda b: inputs.gen_blob(self.seed, b), need)):
+                    self.store[b] = arr
+            if len(self.store) > self.cache:
+                for b in list(self.store)[: len(self.store) - self.cache]:
+                    del self.store[b]
+        return {int(b): self.store[int(b)] for b in blob_ids}
+
+
+def oracle_layer(x, R_bits, src, layer, bias=None, rmsnorm=False, e=inputs.E, K=inputs.K):
+    """The oracle's layer on rows x (float32): returns (ids, w, y) in fp64."""
+    ids, w, xhat = _route(x, R_bits, K, bias=bias, rmsnorm_flag=rmsnorm)
+    got = src.get_many(layer * e + np.unique(ids))
+    blobs = {b - layer * e: arr for b, arr in got.items()}
+    o = _experts(xhat, ids, blobs, e, inputs.H, inputs.FF)
+    return ids, w, _combine(o, w)
+
+
+def stack_trajectory(x0, routers, src, biases=None, margin=TIE_MARGIN, verbose=True):
+    """Run rows x0 [n][H] through len(routers) stacked layers (RMSNorm, router,
+    experts, combine, residual) in the oracle.  Returns per-layer lists of ids,
+    w, y, the input x of every layer, and the per-row top-11 gap per layer."""
+    x = np.asarray(x0, dtype=np.float64)
+    out = dict(ids=[], w=[], y=[], x_in=[], gap=[])
+    for l, R in enumerate(routers):
+        b = None if biases is None else biases[l]
+        xf = x.astype(np.float32)
+        out["gap"].append(top11_gap(logits_np(rms_np(xf), R, b)))
+        ids, w, y = oracle_layer(xf, R, src, l, bias=b, rmsnorm=True)
+        out["x_in"].append(xf)
+        out["ids"].append(ids)
+        out["w"].append(w)
+        out["y"].append(y)
+        x = x + y
+        if verbose and (l % 8 == 7 or l == len(routers) - 1):
+            print(f"  oracle trajectory: layer {l + 1}/{len(routers)} done", flush=True)
+    out["x_out"] = x
+    return out
+
+
+def screened_stack_routers(st, x0, src, n_layers, margin):
+    """Routers for a T=1 stack drawn layer by layer on the oracle trajectory;
+    router l is redrawn (st.router_redraw) until the row clears the margin."""
+    x = np.asarray(x0, dtype=np.float64)
+    routers, redraws = [], 0
+    for l in range(n_layers):
+        R = inputs.draw_router(st.router)
+        xf = x.astype(np.float32)
+        while top11_gap(logits_np(rms_np(xf), R))[0] <= margin:
+            R = inputs.draw_router(st.router_redraw)
+            redraws += 1
+        routers.append(R)
+        _, _, y = oracle_layer(xf, R, src, l, rmsnorm=True)
+        x = x + y
+        if l % 8 == 7:
+            print(f"  router screen: layer {l + 1}/{n_layers} done", flush=True)
+    return routers, redraws

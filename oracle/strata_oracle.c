@@ -191,8 +191,10 @@ static double q2_row_dot(const uint8_t *mat, int r, int n, const double *v)
     double acc = 0.0;
     for (int b = 0; b < nb; ++b) {
         const uint8_t *blk = mat + ((size_t)r * nb + b) * ORC_BB;
+        /* the block's scale, decoded once; weight i is (code_i - 1) * d */
+        double d = orc_half_to_double((uint16_t)(blk[0] | ((uint16_t)blk[1] << 8)));
         for (int i = 0; i < ORC_QK; ++i)
-            acc += orc_q2_value(blk, i) * v[b * ORC_QK + i];
+            acc += (double)(orc_q2_code(blk, i) - 1) * d * v[b * ORC_QK + i];
     }
     return acc;
 }

@@ -1,0 +1,169 @@
+"""Routed-expert MoE layer on MI355X: Python binding of libstrata_moe.so.
+
+Argument marshalling only -- every step of the layer runs in the HIP kernels
+behind the C ABI of include/strata_moe.h.  Functions carry the C names and take
+torch tensors on the GPU (their device pointers are passed through) plus an
+optional hipStream_t handle (default: torch's current stream).  If the library
+is not built, importing works but the first call raises: there is no CPU
+fallback.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libstrata_moe.so")
+
+H, FF, E, K, QK, BB = 2560, 640, 512, 10, 64, 18
+BLOB = 1382400
+T_MAX = 8192
+RMSNORM, RESIDUAL = 1, 2
+OK, E_ARG, E_SHAPE, E_WORKSPACE, E_HIP, E_ALIGN = 0, -1, -2, -3, -4, -5
+
+EXPORTS = ("strata_moe_blob_bytes", "strata_moe_workspace_bytes", "strata_moe_route",
+           "strata_moe_group", "strata_moe_experts", "strata_moe_combine", "strata_moe_layer",
+           "strata_moe_status_string")
+
+_lib = None
+
+
+class StrataError(RuntimeError):
+    def __init__(self, fn, rc):
+        super().__init__(f"{fn} failed: {rc} ({strata_moe_status_string(rc)})")
+        self.rc = rc
+
+
+def lib():
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(the layer has no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.strata_moe_blob_bytes.restype = sz
+        L.strata_moe_blob_bytes.argtypes = []
+        L.strata_moe_workspace_bytes.restype = sz
+        L.strata_moe_workspace_bytes.argtypes = [i32]
+        L.strata_moe_route.restype = i32
+        L.strata_moe_route.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.strata_moe_group.restype = i32
+        L.strata_moe_group.argtypes = [vp, i32, vp, vp, vp, vp, sz, vp]
+        L.strata_moe_experts.restype = i32
+        L.strata_moe_experts.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+        L.strata_moe_combine.restype = i32
+        L.strata_moe_combine.argtypes = [vp, vp, i32, i32, vp, vp]
+        L.strata_moe_layer.restype = i32
+        L.strata_moe_layer.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.strata_moe_status_string.restype = ctypes.c_char_p
+        L.strata_moe_status_string.argtypes = [i32]
+        _lib = L
+    return _lib
+
+
+def _p(t, dtype=None):
+    """Device pointer of a tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _p_router(t):
+    import torch
+    if t is not None and t.dtype not in (torch.int16, torch.bfloat16):
+        raise TypeError("router must hold bf16 bit patterns (int16 or bfloat16 tensor)")
+    return _p(t)
+
+
+def _s(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _check(fn, rc):
+    if rc != OK:
+        raise StrataError(fn, rc)
+
+
+def strata_moe_status_string(rc):
+    return lib().strata_moe_status_string(int(rc)).decode()
+
+
+def strata_moe_blob_bytes():
+    return int(lib().strata_moe_blob_bytes())
+
+
+def strata_moe_workspace_bytes(T):
+    return int(lib().strata_moe_workspace_bytes(int(T)))
+
+
+def workspace(T, device="cuda"):
+    """A workspace tensor sized for T tokens (torch allocations are 256-aligned)."""
+    import torch
+    n = strata_moe_workspace_bytes(T)
+    if n == 0:
+        raise StrataError("strata_moe_workspace_bytes", E_SHAPE)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def strata_moe_route(x, router, ids, w, ws, bias=None, flags=0, stream=None):
+    import torch
+    T = x.shape[0]
+    rc = lib().strata_moe_route(_p(x, torch.float32), T, _p_router(router),
+                                _p(bias, torch.float32), flags, _p(ids, torch.int32),
+                                _p(w, torch.float32), _p(ws), _nbytes(ws), _s(stream))
+    _check("strata_moe_route", rc)
+
+
+def strata_moe_group(ids, offsets, slots, active, ws, stream=None):
+    import torch
+    T = ids.shape[0]
+    rc = lib().strata_moe_group(_p(ids, torch.int32), T, _p(offsets, torch.int32),
+                                _p(slots, torch.int32), _p(active, torch.int32), _p(ws),
+                                _nbytes(ws), _s(stream))
+    _check("strata_moe_group", rc)
+
+
+def strata_moe_experts(x, blobs, offsets, slots, active, out, ws, flags=0, stream=None):
+    import torch
+    T = x.shape[0]
+    rc = lib().strata_moe_experts(_p(x, torch.float32), T, _p(blobs, torch.uint8),
+                                  _p(offsets, torch.int32), _p(slots, torch.int32),
+                                  _p(active, torch.int32), flags, _p(out, torch.float32), _p(ws),
+                                  _nbytes(ws), _s(stream))
+    _check("strata_moe_experts", rc)
+
+
+def strata_moe_combine(out, w, y, flags=0, stream=None):
+    import torch
+    T = y.shape[0]
+    rc = lib().strata_moe_combine(_p(out, torch.float32), _p(w, torch.float32), T, flags,
+                                  _p(y, torch.float32), _s(stream))
+    _check("strata_moe_combine", rc)
+
+
+def strata_moe_layer(x, router, blobs, ws, bias=None, flags=0, y=None, ids=None, w=None,
+                     stream=None):
+    import torch
+    T = x.shape[0]
+    rc = lib().strata_moe_layer(_p(x, torch.float32), T, _p_router(router),
+                                _p(bias, torch.float32), _p(blobs, torch.uint8), flags,
+                                _p(y, torch.float32), _p(ids, torch.int32), _p(w, torch.float32),
+                                _p(ws), _nbytes(ws), _s(stream))
+    _check("strata_moe_layer", rc)

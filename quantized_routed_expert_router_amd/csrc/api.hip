@@ -1,0 +1,239 @@
+// api.hip -- the extern "C" entry points declared in include/strata_moe.h:
+// host-side argument validation, workspace carving and kernel launches.
+// Nothing here synchronises, allocates or reads device memory.
+#include "common.hpp"
+
+namespace strata {
+hipError_t launch_prep(const float *x, int T, int rmsnorm, float *xhat, ActQ xq, __half *xperm,
+                       hipStream_t st);
+hipError_t launch_logits(const float *xhat, int T, const uint16_t *R, const float *bias,
+                         float *logits, hipStream_t st);
+hipError_t launch_topk(const float *logits, int T, int32_t *ids, float *w, hipStream_t st);
+hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
+                        int32_t *active, hipStream_t st);
+hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_items,
+                       int32_t *mlist, int32_t *nitems, hipStream_t st);
+hipError_t launch_decode_experts(const uint8_t *blobs, const int32_t *offsets,
+                                 const int32_t *slots, const int32_t *active, ActQ xq, ActQ hq,
+                                 float *out, int T, hipStream_t st);
+hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
+                                  const int32_t *slots, const int32_t *active,
+                                  const int32_t *mlist, const int32_t *nitems, int max_items,
+                                  const __half *xperm, __half *hperm, float *out, int T,
+                                  hipStream_t st);
+hipError_t launch_combine(const float *out, const float *w, int T, float *y, float *res,
+                          int accumulate_y, hipStream_t st);
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_T(int T) { return (T >= 1 && T <= T_MAX) ? STRATA_OK : STRATA_E_SHAPE; }
+
+int check_ws(void *ws, size_t ws_bytes, int T)
+{
+    if (!ws || ws_bytes < ws_layout(T).total)
+        return STRATA_E_WORKSPACE;
+    if (!aligned(ws, 256))
+        return STRATA_E_ALIGN;
+    return STRATA_OK;
+}
+
+template <class P> P *at(void *ws, size_t off) { return reinterpret_cast<P *>((uint8_t *)ws + off); }
+
+struct Carve {
+    Ws L;
+    float *xhat;
+    ActQ xq, hq;
+    __half *xperm, *hperm;
+    float *logits, *w, *out;
+    int32_t *offsets, *slots, *active, *ids, *mlist, *nitems;
+};
+
+Carve carve(void *ws, int T)
+{
+    Carve c;
+    c.L = ws_layout(T);
+    const Ws &L = c.L;
+    c.xhat = at<float>(ws, L.xhat);
+    const bool dec = is_decode(T);
+    c.xq = ActQ{dec ? at<uint32_t>(ws, L.xq_dig) : nullptr, at<float>(ws, L.xq_scale),
+                at<int32_t>(ws, L.xq_sum)};
+    c.hq = ActQ{dec ? at<uint32_t>(ws, L.hq_dig) : nullptr, at<float>(ws, L.hq_scale),
+                at<int32_t>(ws, L.hq_sum)};
+    c.xperm = dec ? nullptr : at<__half>(ws, L.xperm);
+    c.hperm = dec ? nullptr : at<__half>(ws, L.hperm);
+    c.logits = at<float>(ws, L.logits);
+    c.offsets = at<int32_t>(ws, L.offsets);
+    c.slots = at<int32_t>(ws, L.slots);
+    c.active = at<int32_t>(ws, L.active);
+    c.ids = at<int32_t>(ws, L.ids);
+    c.w = at<float>(ws, L.w);
+    c.mlist = at<int32_t>(ws, L.mlist);
+    c.nitems = at<int32_t>(ws, L.nitems);
+    c.out = at<float>(ws, L.out);
+    return c;
+}
+
+#define STRATA_TRY(expr)                                                                           \
+    do {                                                                                           \
+        hipError_t e_ = (expr);                                                                    \
+        if (e_ != hipSuccess)                                                                      \
+            return STRATA_E_HIP;                                                                   \
+    } while (0)
+
+int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
+                const int32_t *slots, const int32_t *active, float *out, int T, hipStream_t st)
+{
+    if (is_decode(T)) {
+        STRATA_TRY(launch_decode_experts(blobs, offsets, slots, active, c.xq, c.hq, out, T, st));
+    } else {
+        STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
+        STRATA_TRY(launch_prefill_experts(blobs, offsets, slots, active, c.mlist, c.nitems,
+                                          c.L.max_items, c.xperm, c.hperm, out, T, st));
+    }
+    return STRATA_OK;
+}
+
+} // namespace
+} // namespace strata
+
+using namespace strata;
+
+extern "C" {
+
+size_t strata_moe_blob_bytes(void) { return BLOB; }
+
+size_t strata_moe_workspace_bytes(int T)
+{
+    if (check_T(T) != STRATA_OK)
+        return 0;
+    return ws_layout(T).total;
+}
+
+int strata_moe_route(const float *x, int T, const uint16_t *router, const float *bias,
+                     int flags, int32_t *ids, float *w, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_T(T);
+    if (rc)
+        return rc;
+    if (!x || !router || !ids || !w || (flags & ~(STRATA_RMSNORM | STRATA_RESIDUAL)))
+        return STRATA_E_ARG;
+    if ((rc = check_ws(ws, ws_bytes, T)))
+        return rc;
+    if (!aligned(x, 16) || !aligned(router, 16) || !aligned(ids, 4) || !aligned(w, 4) ||
+        !aligned(bias, 4))
+        return STRATA_E_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    Carve c = carve(ws, T);
+    STRATA_TRY(launch_prep(x, T, flags & STRATA_RMSNORM, c.xhat, ActQ{nullptr, nullptr, nullptr},
+                           nullptr, st));
+    STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
+    STRATA_TRY(launch_topk(c.logits, T, ids, w, st));
+    return STRATA_OK;
+}
+
+int strata_moe_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
+                     int32_t *active, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_T(T);
+    if (rc)
+        return rc;
+    if (!ids || !offsets || !slots || !active)
+        return STRATA_E_ARG;
+    if ((rc = check_ws(ws, ws_bytes, T)))
+        return rc;
+    if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(slots, 4) || !aligned(active, 4))
+        return STRATA_E_ALIGN;
+    STRATA_TRY(launch_group(ids, T, offsets, slots, active, (hipStream_t)stream));
+    return STRATA_OK;
+}
+
+int strata_moe_experts(const float *x, int T, const uint8_t *blobs, const int32_t *offsets,
+                       const int32_t *slots, const int32_t *active, int flags, float *out,
+                       void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_T(T);
+    if (rc)
+        return rc;
+    if (!x || !blobs || !offsets || !slots || !active || !out ||
+        (flags & ~(STRATA_RMSNORM | STRATA_RESIDUAL)))
+        return STRATA_E_ARG;
+    if ((rc = check_ws(ws, ws_bytes, T)))
+        return rc;
+    if (!aligned(x, 16) || !aligned(blobs, 256) || !aligned(out, 16) || !aligned(offsets, 4) ||
+        !aligned(slots, 4) || !aligned(active, 4))
+        return STRATA_E_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    Carve c = carve(ws, T);
+    STRATA_TRY(launch_prep(x, T, flags & STRATA_RMSNORM, c.xhat, c.xq, c.xperm, st));
+    return run_experts(c, blobs, offsets, slots, active, out, T, st);
+}
+
+int strata_moe_combine(const float *out, const float *w, int T, int flags, float *y,
+                       void *stream)
+{
+    int rc = check_T(T);
+    if (rc)
+        return rc;
+    if (!out || !w || !y || (flags & ~(STRATA_RMSNORM | STRATA_RESIDUAL)))
+        return STRATA_E_ARG;
+    if (!aligned(out, 16) || !aligned(y, 16) || !aligned(w, 4))
+        return STRATA_E_ALIGN;
+    STRATA_TRY(launch_combine(out, w, T, y, nullptr, (flags & STRATA_RESIDUAL) ? 1 : 0,
+                              (hipStream_t)stream));
+    return STRATA_OK;
+}
+
+int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
+                     const uint8_t *blobs, int flags, float *y, int32_t *ids, float *w,
+                     void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_T(T);
+    if (rc)
+        return rc;
+    if (!x || !router || !blobs || (flags & ~(STRATA_RMSNORM | STRATA_RESIDUAL)))
+        return STRATA_E_ARG;
+    if (!y && !(flags & STRATA_RESIDUAL))
+        return STRATA_E_ARG;
+    if ((rc = check_ws(ws, ws_bytes, T)))
+        return rc;
+    if (!aligned(x, 16) || !aligned(router, 16) || !aligned(blobs, 256) || !aligned(y, 16) ||
+        !aligned(ids, 4) || !aligned(w, 4) || !aligned(bias, 4))
+        return STRATA_E_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    Carve c = carve(ws, T);
+    int32_t *ids_o = ids ? ids : c.ids;
+    float *w_o = w ? w : c.w;
+    STRATA_TRY(launch_prep(x, T, flags & STRATA_RMSNORM, c.xhat, c.xq, c.xperm, st));
+    STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
+    STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
+    STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, st));
+    if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st)))
+        return rc;
+    const bool res = flags & STRATA_RESIDUAL;
+    STRATA_TRY(launch_combine(c.out, w_o, T, y, res ? x : nullptr, 0, st));
+    return STRATA_OK;
+}
+
+const char *strata_moe_status_string(int status)
+{
+    switch (status) {
+    case STRATA_OK:
+        return "ok";
+    case STRATA_E_ARG:
+        return "invalid argument (NULL pointer or unknown flag)";
+    case STRATA_E_SHAPE:
+        return "T outside 1..8192";
+    case STRATA_E_WORKSPACE:
+        return "workspace missing or too small";
+    case STRATA_E_HIP:
+        return "HIP launch error";
+    case STRATA_E_ALIGN:
+        return "pointer alignment violated";
+    default:
+        return "unknown status";
+    }
+}
+
+} // extern "C"

@@ -1,0 +1,177 @@
+// group.hip -- token -> expert grouping and the prefill work list.
+//
+// Collecting the tokens of a chunk per expert lets one read of an expert's
+// weights serve all of them (the momoyeyu.github.io Strata explainer, section
+// 提示词处理: four tokens of one expert read its weights once, W X with
+// X = [x1..x4]); for a verify window it is the dedup of routed ids ("Strata in
+// the source...", section "The plan: three destinations per expert").
+//
+// group_kernel is one 1024-thread workgroup: per-wave histograms in LDS
+// (integer atomics, so the counts are exact), an exclusive scan to offsets, the
+// ascending active-expert list, then a stable scatter in which each wave walks
+// its contiguous slice of slots in order and ranks equal experts inside a
+// 64-slot step with ballots.  Every output is a pure function of ids.
+#include "common.hpp"
+
+namespace strata {
+
+constexpr int GR_THREADS = 1024;
+constexpr int GR_WAVES = GR_THREADS / 64;
+
+__device__ inline int block_exclusive_scan_512(int v, int tid, int *tmp, int *total)
+{
+    // tid < 512 contribute v; returns the exclusive prefix for tid < 512.
+    // tmp holds 8 wave sums.  Called by all threads of the block.
+    const int lane = tid & 63, wave = tid >> 6;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(inc, d, 64);
+        if (lane >= d)
+            inc += o;
+    }
+    if (tid < 512 && lane == 63)
+        tmp[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    if (tid < 512)
+        for (int w = 0; w < wave; ++w)
+            base += tmp[w];
+    if (tid == 0) {
+        int s = 0;
+        for (int w = 0; w < 8; ++w)
+            s += tmp[w];
+        *total = s;
+    }
+    __syncthreads();
+    return base + inc - v;
+}
+
+__global__ __launch_bounds__(GR_THREADS) void group_kernel(const int32_t *__restrict__ ids,
+                                                           int T, int32_t *__restrict__ offsets,
+                                                           int32_t *__restrict__ slots,
+                                                           int32_t *__restrict__ active)
+{
+    __shared__ int hist[GR_WAVES][E];
+    __shared__ int tmp[8];
+    __shared__ int tot;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int N = T * K;
+    const int S = (N + GR_WAVES - 1) / GR_WAVES;   // slots per wave
+    const int beg = min(wave * S, N), end = min(beg + S, N);
+
+    for (int i = tid; i < GR_WAVES * E; i += GR_THREADS)
+        (&hist[0][0])[i] = 0;
+    __syncthreads();
+    for (int i = beg + lane; i < end; i += 64) {
+        const int e = ids[i];
+        if (e >= 0 && e < E)
+            atomicAdd(&hist[wave][e], 1);
+    }
+    __syncthreads();
+    // Per expert: each wave's start within the expert, and the expert total.
+    int count = 0;
+    if (tid < E) {
+        int run = 0;
+        for (int w = 0; w < GR_WAVES; ++w) {
+            const int c = hist[w][tid];
+            hist[w][tid] = run;
+            run += c;
+        }
+        count = run;
+    }
+    const int off = block_exclusive_scan_512(count, tid, tmp, &tot);
+    if (tid < E) {
+        offsets[tid] = off;
+        for (int w = 0; w < GR_WAVES; ++w)
+            hist[w][tid] += off;   // now the wave's cursor for expert tid
+    }
+    if (tid == 0)
+        offsets[E] = tot;
+    const int flag = (tid < E && count > 0) ? 1 : 0;
+    const int pos = block_exclusive_scan_512(flag, tid, tmp, &tot);
+    if (flag)
+        active[1 + pos] = tid;
+    if (tid == 0)
+        active[0] = tot;
+    __syncthreads();
+
+    // Stable scatter: every wave takes the same number of 64-slot steps.
+    const int steps = (S + 63) / 64;
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+    for (int it = 0; it < steps; ++it) {
+        const int i = beg + it * 64 + lane;
+        int e = -1;
+        if (i < end) {
+            e = ids[i];
+            if (e < 0 || e >= E)
+                e = -1;
+        }
+        unsigned long long same = __ballot(e >= 0);
+        if (e < 0)
+            same = 0;
+#pragma unroll
+        for (int b = 0; b < 9; ++b) {
+            const unsigned long long bits = __ballot(e >= 0 && ((e >> b) & 1));
+            same &= ((e >> b) & 1) ? bits : ~bits;
+        }
+        if (e >= 0) {
+            const int rank = __popcll(same & lt_mask);
+            const int cur = hist[wave][e];
+            slots[cur + rank] = i;
+            if ((same >> lane) == 1ull)   // highest lane of its group
+                hist[wave][e] = cur + __popcll(same);
+        }
+        __syncthreads();
+    }
+}
+
+// Prefill work list: one item per (active expert, 64-token chunk), in active
+// order; nitems[0] = item count.
+__global__ __launch_bounds__(512) void plan_kernel(const int32_t *__restrict__ offsets,
+                                                   const int32_t *__restrict__ active,
+                                                   int max_items, int32_t *__restrict__ mlist,
+                                                   int32_t *__restrict__ nitems)
+{
+    __shared__ int tmp[8];
+    __shared__ int tot;
+    const int tid = threadIdx.x;
+    const int na = active[0];
+    int nch = 0;
+    if (tid < na) {
+        const int e = active[1 + tid];
+        if (e >= 0 && e < E) {
+            const int n = offsets[e + 1] - offsets[e];
+            nch = n > 0 ? (n + PF_M - 1) / PF_M : 0;
+        }
+    }
+    const int base = block_exclusive_scan_512(nch, tid, tmp, &tot);
+    for (int c = 0; c < nch; ++c) {
+        const int it = base + c;
+        if (it < max_items) {
+            mlist[2 * it] = tid;
+            mlist[2 * it + 1] = c * PF_M;
+        }
+    }
+    if (tid == 0)
+        nitems[0] = min(tot, max_items);
+}
+
+hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
+                        int32_t *active, hipStream_t st)
+{
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(GR_THREADS), 0, st, ids, T, offsets, slots,
+                       active);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_items,
+                       int32_t *mlist, int32_t *nitems, hipStream_t st)
+{
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(512), 0, st, offsets, active, max_items, mlist,
+                       nitems);
+    return hipGetLastError();
+}
+
+} // namespace strata

@@ -1,0 +1,276 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: expert ids bit-exact as ordered lists, |dw| <= 1e-5, and
+max|dy| <= 2e-3 * max|y| over the compared tensor, on seeded inputs screened
+for router near-ties (no two of a token's 11 largest logits within 1e-4).
+"""
+import numpy as np
+import pytest
+
+import harness as hz
+import inputs
+import oracle.screen as scr
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hz.qm().lib()
+    yield
+    hz.drop_stores()
+    torch.cuda.empty_cache()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def test_device_fill_matches_host_generator():
+    _say("case: device fill vs host generator, seed 0 layer 0 and seed 2 layer 47")
+    s = hz.store(0, 0).view(512, -1)
+    for e in (0, 1, 255, 511):
+        assert np.array_equal(s[e].cpu().numpy(), inputs.gen_blob(0, e)), e
+    import torch
+    one = torch.empty(inputs.blob_bytes(), dtype=torch.uint8, device="cuda")
+    inputs.fill_blobs_device(one, 2, 47 * 512 + 5, 1)
+    assert np.array_equal(one.cpu().numpy(), inputs.gen_blob(2, 47 * 512 + 5))
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_decode_configs(cfg):
+    c = inputs.CONFIGS[cfg]
+    _say(f"case: config {cfg} ({c['name']}), T={c['T']}, seed {c['seed']}")
+    x, R, _ = hz.single_layer_case(c["seed"], c["T"])
+    ids, w, y, _ = hz.gpu_layer(x, R, hz.store(c["seed"]))
+    oids, ow, oy = hz.oracle_rows(x, R, c["seed"], np.arange(c["T"]))
+    hz.check(f"config {cfg}", ids, w, y, oids, ow, oy)
+
+
+@pytest.mark.parametrize("T", [2, 3, 5, 8, 16])
+def test_decode_sizes(T):
+    seed = 1000 + T
+    _say(f"case: decode T={T}, seed {seed}")
+    x, R, _ = hz.single_layer_case(seed, T)
+    ids, w, y, _ = hz.gpu_layer(x, R, hz.store(seed))
+    oids, ow, oy = hz.oracle_rows(x, R, seed, np.arange(T))
+    hz.check(f"decode T={T}", ids, w, y, oids, ow, oy)
+
+
+@pytest.mark.parametrize("T", [17, 64, 100, 257])
+def test_prefill_sizes(T):
+    seed = 2000 + T
+    _say(f"case: prefill T={T}, seed {seed}")
+    x, R, _ = hz.single_layer_case(seed, T)
+    ids, w, y, _ = hz.gpu_layer(x, R, hz.store(seed))
+    oids, ow, oy = hz.oracle_rows(x, R, seed, np.arange(T))
+    hz.check(f"prefill T={T}", ids, w, y, oids, ow, oy)
+
+
+def test_prefill_skewed_multi_chunk_experts():
+    """A Zipf-biased router sends more than 64 tokens to the hottest experts,
+    so their rows span several 64-token chunks with a ragged last chunk."""
+    seed, T = 3001, 300
+    st = inputs.Streams(seed)
+    R = inputs.draw_router(st.router)
+    bias = inputs.draw_zipf_bias(st.bias)
+    x, _ = scr.screened_x(st, T, R, bias=bias)
+    _say(f"case: skewed prefill T={T}, seed {seed}")
+    ids, w, y, _ = hz.gpu_layer(x, R, hz.store(seed), bias=bias)
+    counts = np.bincount(ids.ravel(), minlength=512)
+    assert counts.max() > 64, counts.max()
+    oids, ow, oy = hz.oracle_rows(x, R, seed, np.arange(T), bias=bias)
+    hz.check("skewed prefill", ids, w, y, oids, ow, oy)
+
+
+@pytest.mark.timeout(600)
+def test_config3_prefill_sampled():
+    c = inputs.CONFIGS[3]
+    _say(f"case: config 3 T={c['T']} seed {c['seed']}")
+    x, R, redrawn = hz.single_layer_case(c["seed"], c["T"])
+    ids, w, y, _ = hz.gpu_layer(x, R, hz.store(c["seed"]))
+    import oracle
+    oids, ow, _ = oracle.route(x, R, 10)
+    assert np.array_equal(ids, oids), np.nonzero(np.any(ids != oids, axis=1))[0][:8]
+    assert np.max(np.abs(w - ow)) <= hz.W_TOL
+    rows = np.random.default_rng(3).choice(c["T"], 64, replace=False)
+    rows = np.sort(np.concatenate([rows, [0, c["T"] - 1]]))
+    sids, sw, sy = hz.oracle_rows(x, R, c["seed"], rows)
+    hz.check("config 3 sampled", ids[rows], w[rows], y[rows], sids, sw, sy)
+    load = np.bincount(ids.ravel(), minlength=512)
+    _say(f"config 3: {redrawn} rows redrawn; tokens per expert {load.min()}..{load.max()}")
+
+
+@pytest.mark.timeout(600)
+def test_max_T_sampled():
+    T, seed = 8192, 8192
+    _say(f"case: T={T} (largest chunk) seed {seed}")
+    st = inputs.Streams(seed)
+    R = inputs.draw_router(st.router)
+    x, _ = scr.screened_x(st, T, R)
+    ids, w, y, _ = hz.gpu_layer(x, R, hz.store(seed))
+    rows = np.sort(np.random.default_rng(5).choice(T, 48, replace=False))
+    sids, sw, sy = hz.oracle_rows(x, R, seed, rows)
+    hz.check("T=8192 sampled", ids[rows], w[rows], y[rows], sids, sw, sy)
+
+
+@pytest.mark.parametrize("T", [4, 100])
+def test_layer_equals_composition_and_is_deterministic(T):
+    seed = 4000 + T
+    _say(f"case: layer vs composition T={T}")
+    x, R, _ = hz.single_layer_case(seed, T)
+    st = hz.store(seed)
+    ids, w, y, _ = hz.gpu_layer(x, R, st)
+    ids2, w2, y2, _ = hz.gpu_layer(x, R, st)
+    comp = hz.gpu_composed(x, R, st)
+    assert np.array_equal(ids, ids2) and np.array_equal(w, w2) and np.array_equal(y, y2)
+    assert np.array_equal(ids, comp["ids"]) and np.array_equal(w, comp["w"])
+    assert np.array_equal(y, comp["y"])
+
+
+def test_decode_batch_invariance():
+    """Each token of a T=4 window gets bitwise the T=1 result."""
+    seed = 4100
+    x, R, _ = hz.single_layer_case(seed, 4)
+    st = hz.store(seed)
+    _say("case: batch invariance T=4 vs T=1")
+    ids, w, y, _ = hz.gpu_layer(x, R, st)
+    for t in range(4):
+        i1, w1, y1, _ = hz.gpu_layer(x[t:t + 1], R, st)
+        assert np.array_equal(i1[0], ids[t]) and np.array_equal(w1[0], w[t])
+        assert np.array_equal(y1[0], y[t]), t
+
+
+def test_group_matches_cpu_counting_sort():
+    import torch
+    m = hz.qm()
+    rng = np.random.default_rng(9)
+    for T in (1, 4, 37, 2048, 8192):
+        _say(f"case: group T={T}")
+        ids = rng.integers(0, 512, (T, 10)).astype(np.int32)
+        if T == 37:
+            ids[3, 4] = 600     # out-of-range ids are dropped
+            ids[5, 0] = -1
+        idd = hz.cuda(ids)
+        offsets = torch.empty(513, dtype=torch.int32, device="cuda")
+        slots = torch.full((T * 10,), -7, dtype=torch.int32, device="cuda")
+        active = torch.empty(513, dtype=torch.int32, device="cuda")
+        m.strata_moe_group(idd, offsets, slots, active, m.workspace(T))
+        torch.cuda.synchronize()
+        flat = ids.ravel()
+        ok = (flat >= 0) & (flat < 512)
+        cnt = np.bincount(flat[ok], minlength=512)
+        ref_off = np.concatenate([[0], np.cumsum(cnt)])
+        assert np.array_equal(offsets.cpu().numpy(), ref_off)
+        order = np.nonzero(ok)[0]
+        order = order[np.argsort(flat[order], kind="stable")]
+        assert np.array_equal(slots.cpu().numpy()[: order.size], order)
+        act = np.nonzero(cnt)[0]
+        a = active.cpu().numpy()
+        assert a[0] == act.size and np.array_equal(a[1:1 + act.size], act)
+
+
+def test_error_codes():
+    import torch
+    m = hz.qm()
+    x = torch.zeros((2, 2560), device="cuda")
+    R = torch.zeros((512, 2560), dtype=torch.int16, device="cuda")
+    ids = torch.empty((2, 10), dtype=torch.int32, device="cuda")
+    w = torch.empty((2, 10), device="cuda")
+    ws = m.workspace(2)
+    L = m.lib()
+    s = torch.cuda.current_stream().cuda_stream
+    assert L.strata_moe_route(None, 2, R.data_ptr(), None, 0, ids.data_ptr(), w.data_ptr(),
+                              ws.data_ptr(), ws.numel(), s) == m.E_ARG
+    assert L.strata_moe_route(x.data_ptr(), 0, R.data_ptr(), None, 0, ids.data_ptr(),
+                              w.data_ptr(), ws.data_ptr(), ws.numel(), s) == m.E_SHAPE
+    assert L.strata_moe_route(x.data_ptr(), 8193, R.data_ptr(), None, 0, ids.data_ptr(),
+                              w.data_ptr(), ws.data_ptr(), ws.numel(), s) == m.E_SHAPE
+    assert L.strata_moe_route(x.data_ptr(), 2, R.data_ptr(), None, 0, ids.data_ptr(),
+                              w.data_ptr(), ws.data_ptr(), 100, s) == m.E_WORKSPACE
+    assert L.strata_moe_route(x.data_ptr() + 4, 2, R.data_ptr(), None, 0, ids.data_ptr(),
+                              w.data_ptr(), ws.data_ptr(), ws.numel(), s) == m.E_ALIGN
+    assert L.strata_moe_route(x.data_ptr(), 2, R.data_ptr(), None, 8, ids.data_ptr(),
+                              w.data_ptr(), ws.data_ptr(), ws.numel(), s) == m.E_ARG
+    with pytest.raises(m.StrataError):
+        m.strata_moe_layer(x, R, torch.zeros(16, dtype=torch.uint8, device="cuda")[1:], ws, y=x)
+
+
+def _tie_router(x, R, rmsnorm=False):
+    """Duplicate the top expert's router row into two higher ids, and the
+    10th-ranked row into a higher id, so ties sit at ranks 1-3 and 10-11."""
+    xh = scr.rms_np(x) if rmsnorm else x.astype(np.float64)
+    lg = scr.logits_np(xh[:1], R)[0]
+    order = np.argsort(-lg, kind="stable")
+    R = R.copy()
+    top, tenth = order[0], order[9]
+    higher = [e for e in order[20:] if e > max(top, tenth)][:3]
+    R[higher[0]] = R[top]
+    R[higher[1]] = R[top]
+    R[higher[2]] = R[tenth]
+    return R, top, tenth, higher
+
+
+@pytest.mark.parametrize("T", [2, 20])
+def test_stable_tie_order(T):
+    seed = 5000 + T
+    st = inputs.Streams(seed)
+    R = inputs.draw_router(st.router)
+    x, _ = scr.screened_x(st, T, R)
+    R2, top, tenth, higher = _tie_router(x, R)
+    _say(f"case: tie order T={T}, tie {top}={higher[:2]}, {tenth}={higher[2]}")
+    ids, w, y, _ = hz.gpu_layer(x, R2, hz.store(seed))
+    oids, ow, oy = hz.oracle_rows(x[:1], R2, seed, np.arange(1))
+    assert np.array_equal(ids[0], oids[0]), (ids[0], oids[0])
+    assert list(ids[0][:3]) == [top] + sorted(higher[:2]) and ids[0][9] == tenth
+    assert w[0][0] == w[0][1] == w[0][2]
+
+
+def test_zero_input_and_zero_experts():
+    import torch
+    T = 3
+    _say("case: zero activations; all-zero-weight experts")
+    R = inputs.draw_router(np.random.default_rng(1))
+    zero_store = torch.full((512 * inputs.blob_bytes(),), 0x55, dtype=torch.uint8, device="cuda")
+    x = np.zeros((T, 2560), dtype=np.float32)
+    for flags in (0, 1):
+        ids, w, y, _ = hz.gpu_layer(x, R, hz.store(0), flags=flags)
+        assert np.all(ids == np.arange(10)) and np.allclose(w, 0.1, atol=1e-7)
+        assert np.all(y == 0.0)
+    xr = np.random.default_rng(2).standard_normal((20, 2560)).astype(np.float32)
+    for T2 in (2, 20):
+        _, _, y, _ = hz.gpu_layer(xr[:T2], R, zero_store)
+        assert np.all(y == 0.0)
+
+
+def test_graph_capture_replays_match_eager():
+    import torch
+    m = hz.qm()
+    seed, T = 6000, 4
+    x, R, _ = hz.single_layer_case(seed, T)
+    st = hz.store(seed)
+    _say("case: HIP graph capture of the layer, 3 replays")
+    xd, Rd = hz.cuda(x), hz.router_dev(R)
+    ws = m.workspace(T)
+    y = torch.empty_like(xd)
+    ids = torch.empty((T, 10), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 10), device="cuda")
+    m.strata_moe_layer(xd, Rd, st, ws, y=y, ids=ids, w=w)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            m.strata_moe_layer(xd, Rd, st, ws, y=y, ids=ids, w=w, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(3):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), i
+        _ = (xd * 2).sum().item()   # eager work between replays

@@ -1,0 +1,121 @@
+"""48-layer stacks (RMSNorm -> router -> experts -> combine -> residual) at
+the workload's full sizes, compared with full oracle trajectories of the same
+tokens (never teacher-forced: the oracle only sees generator inputs)."""
+import numpy as np
+import pytest
+
+import harness as hz
+import inputs
+import oracle.screen as scr
+
+pytestmark = pytest.mark.gpu
+
+# The GPU's fp32 residual stream drifts from the fp64 one by rounding over 48
+# layers, so stacked runs keep a wider router margin than single layers.
+STACK_MARGIN_T1 = 1e-3
+STACK_MARGIN_PREFILL = 3e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hz.qm().lib()
+    yield
+    hz.drop_stores()
+    torch.cuda.empty_cache()
+
+
+def _run_stack_gpu(x, routers, store, biases=None, rows=None):
+    """All layers on the GPU for x [T][H]; returns per-layer ids, w, y of `rows`."""
+    import torch
+    m = hz.qm()
+    T = x.shape[0]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    ridx = torch.from_numpy(rows).cuda()
+    xd = hz.cuda(x)
+    ws = m.workspace(T)
+    y = torch.empty_like(xd)
+    ids = torch.empty((T, 10), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 10), device="cuda")
+    got = dict(ids=[], w=[], y=[])
+    Rd = [hz.router_dev(R) for R in routers]
+    bd = None if biases is None else [hz.cuda(b) for b in biases]
+    per = 512 * inputs.blob_bytes()
+    for l in range(len(routers)):
+        m.strata_moe_layer(xd, Rd[l], store[l * per:(l + 1) * per], ws,
+                           bias=None if bd is None else bd[l], flags=m.RMSNORM | m.RESIDUAL,
+                           y=y, ids=ids, w=w)
+        got["ids"].append(ids.index_select(0, ridx).cpu().numpy())
+        got["w"].append(w.index_select(0, ridx).cpu().numpy())
+        got["y"].append(y.index_select(0, ridx).cpu().numpy())
+    got["x"] = xd.index_select(0, ridx).cpu().numpy()
+    return got
+
+
+@pytest.mark.timeout(900)
+def test_config2_stack_t1():
+    c = inputs.CONFIGS[2]
+    seed = c["seed"]
+    st = inputs.Streams(seed)
+    x0 = inputs.draw_x(st.x, 1)
+    src = scr.BlobSource(seed)
+    print("case: config 2 screening routers on the oracle trajectory", flush=True)
+    routers, redraws = scr.screened_stack_routers(st, x0, src, 48, STACK_MARGIN_T1)
+    traj = scr.stack_trajectory(x0, routers, src)
+    print(f"config 2: {redraws} router redraws; min gap {min(g.min() for g in traj['gap']):.2e}",
+          flush=True)
+    store = inputs.layer_store(seed, 0, n_layers=48)
+    print("case: config 2 GPU stack (48 layers, 34 GB store)", flush=True)
+    got = _run_stack_gpu(x0, routers, store)
+    worst = 0.0
+    for l in range(48):
+        worst = max(worst, hz.check(f"config 2 layer {l}", got["ids"][l], got["w"][l], got["y"][l],
+                                    traj["ids"][l], traj["w"][l], traj["y"][l]))
+    dx = np.max(np.abs(got["x"] - traj["x_out"])) / np.max(np.abs(traj["x_out"]))
+    print(f"config 2: worst layer {worst:.3e}, final x {dx:.3e}", flush=True)
+    assert dx <= hz.Y_TOL
+    # the byte budget: 48 x 10 distinct blobs were read for the token
+    assert sum(len(set(i.ravel())) for i in got["ids"]) == 480
+
+
+@pytest.mark.timeout(1200)
+def test_config4_stack_sampled():
+    c = inputs.CONFIGS[4]
+    seed, T, chunk = c["seed"], c["T"], c["chunk"]
+    st = inputs.Streams(seed)
+    x = inputs.draw_x(st.x, T)
+    routers = [inputs.draw_router(st.router) for _ in range(48)]
+    biases = [inputs.draw_zipf_bias(st.bias) for _ in range(48)]
+    cand = np.sort(np.random.default_rng(44).choice(T, 24, replace=False))
+    store = inputs.layer_store(seed, 0, n_layers=48)
+    print("case: config 4 GPU, 16 chunks x 48 layers", flush=True)
+    got = {k: [[] for _ in range(48)] for k in ("ids", "w", "y")}
+    gx = []
+    for ch in range(T // chunk):
+        lo, hi = ch * chunk, (ch + 1) * chunk
+        rows = cand[(cand >= lo) & (cand < hi)] - lo
+        r = _run_stack_gpu(x[lo:hi], routers, store, biases, rows=rows)
+        for k in ("ids", "w", "y"):
+            for l in range(48):
+                got[k][l].append(r[k][l])
+        gx.append(r["x"])
+    for k in ("ids", "w", "y"):
+        got[k] = [np.concatenate(v) for v in got[k]]
+    gx = np.concatenate(gx)
+    print("case: config 4 oracle trajectories of 24 sampled tokens", flush=True)
+    src = scr.BlobSource(seed, cache=20000)
+    traj = scr.stack_trajectory(x[cand], routers, src, biases)
+    gaps = np.min(np.stack(traj["gap"]), axis=0)
+    keep = np.nonzero(gaps > STACK_MARGIN_PREFILL)[0]
+    print(f"config 4: {keep.size}/24 tokens clear the {STACK_MARGIN_PREFILL} margin at all 48 "
+          f"layers", flush=True)
+    assert keep.size >= 6
+    for l in range(48):
+        hz.check(f"config 4 layer {l}", got["ids"][l][keep], got["w"][l][keep],
+                 got["y"][l][keep], traj["ids"][l][keep], traj["w"][l][keep],
+                 traj["y"][l][keep])
+    dx = np.max(np.abs(gx[keep] - traj["x_out"][keep])) / np.max(np.abs(traj["x_out"][keep]))
+    print(f"config 4: final x {dx:.3e}", flush=True)
+    assert dx <= hz.Y_TOL
