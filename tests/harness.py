@@ -78,13 +78,13 @@ def gpu_composed(x, R_bits, blobs_dev, bias=None, flags=0):
                 active=active.cpu().numpy(), out=out.cpu().numpy())
 
 
-def check(tag, ids, w, y, oids, ow, oy):
+def check(tag, ids, w, y, oids, ow, oy, w_tol=W_TOL):
     """Assert parity and return diagnostics."""
     assert ids.shape == oids.shape
     bad = np.nonzero(np.any(ids != oids, axis=1))[0]
     assert bad.size == 0, f"{tag}: ids differ on rows {bad[:8]}: {ids[bad[:2]]} vs {oids[bad[:2]]}"
     dw = float(np.max(np.abs(w.astype(np.float64) - ow)))
-    assert dw <= W_TOL, f"{tag}: |dw| = {dw}"
+    assert dw <= w_tol, f"{tag}: |dw| = {dw}"
     ymax = float(np.max(np.abs(oy)))
     dy = np.abs(y.astype(np.float64) - oy)
     rel = float(dy.max() / ymax) if ymax > 0 else float(dy.max())

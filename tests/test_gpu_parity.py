@@ -200,13 +200,14 @@ def test_error_codes():
 
 
 def _tie_router(x, R, rmsnorm=False):
-    """Duplicate the top expert's router row into two higher ids, and the
-    10th-ranked row into a higher id, so ties sit at ranks 1-3 and 10-11."""
+    """Duplicate the top expert's router row into two higher ids (a tie at
+    ranks 1-3), and the 8th-ranked row -- rank 10 once the two copies sit
+    above it -- into a higher id, so a tie straddles ranks 10 and 11."""
     xh = scr.rms_np(x) if rmsnorm else x.astype(np.float64)
     lg = scr.logits_np(xh[:1], R)[0]
     order = np.argsort(-lg, kind="stable")
     R = R.copy()
-    top, tenth = order[0], order[9]
+    top, tenth = order[0], order[7]
     higher = [e for e in order[20:] if e > max(top, tenth)][:3]
     R[higher[0]] = R[top]
     R[higher[1]] = R[top]

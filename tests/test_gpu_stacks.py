@@ -1,6 +1,17 @@
 """48-layer stacks (RMSNorm -> router -> experts -> combine -> residual) at
 the workload's full sizes, compared with full oracle trajectories of the same
-tokens (never teacher-forced: the oracle only sees generator inputs)."""
+tokens.  The oracle only ever sees generator inputs.
+
+Two checks per stack:
+ * per layer, on identical inputs: the GPU layer l is run on the oracle's own
+   layer-l input (uploaded), and must meet the single-layer bar (ids exact,
+   |dw| <= 1e-5, max|dy| <= 2e-3 max|y|);
+ * end to end: the GPU stack runs on its own residual stream.  Ids must still
+   match at every layer (the tokens are screened with a margin wider than the
+   drift), y and the final x stay within 2e-3 of max|.|; w inherits the fp32
+   residual stream's drift from earlier layers, so it gets the wider bound
+   W_TOL_STACK.
+"""
 import numpy as np
 import pytest
 
@@ -14,6 +25,7 @@ pytestmark = pytest.mark.gpu
 # layers, so stacked runs keep a wider router margin than single layers.
 STACK_MARGIN_T1 = 1e-3
 STACK_MARGIN_PREFILL = 3e-4
+W_TOL_STACK = 5e-4
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -71,13 +83,21 @@ def test_config2_stack_t1():
     got = _run_stack_gpu(x0, routers, store)
     worst = 0.0
     for l in range(48):
-        worst = max(worst, hz.check(f"config 2 layer {l}", got["ids"][l], got["w"][l], got["y"][l],
-                                    traj["ids"][l], traj["w"][l], traj["y"][l]))
+        worst = max(worst, hz.check(f"config 2 e2e layer {l}", got["ids"][l], got["w"][l],
+                                    got["y"][l], traj["ids"][l], traj["w"][l], traj["y"][l],
+                                    w_tol=W_TOL_STACK))
     dx = np.max(np.abs(got["x"] - traj["x_out"])) / np.max(np.abs(traj["x_out"]))
-    print(f"config 2: worst layer {worst:.3e}, final x {dx:.3e}", flush=True)
+    print(f"config 2: worst end-to-end layer {worst:.3e}, final x {dx:.3e}", flush=True)
     assert dx <= hz.Y_TOL
     # the byte budget: 48 x 10 distinct blobs were read for the token
     assert sum(len(set(i.ravel())) for i in got["ids"]) == 480
+    # per layer on the oracle's own inputs: the single-layer bar
+    per = 512 * inputs.blob_bytes()
+    for l in range(48):
+        ids, w, y, xo = hz.gpu_layer(traj["x_in"][l], routers[l], store[l * per:(l + 1) * per],
+                                     flags=3)
+        hz.check(f"config 2 forced layer {l}", ids, w, y, traj["ids"][l], traj["w"][l],
+                 traj["y"][l])
 
 
 @pytest.mark.timeout(1200)
@@ -113,9 +133,21 @@ def test_config4_stack_sampled():
           f"layers", flush=True)
     assert keep.size >= 6
     for l in range(48):
-        hz.check(f"config 4 layer {l}", got["ids"][l][keep], got["w"][l][keep],
+        hz.check(f"config 4 e2e layer {l}", got["ids"][l][keep], got["w"][l][keep],
                  got["y"][l][keep], traj["ids"][l][keep], traj["w"][l][keep],
-                 traj["y"][l][keep])
+                 traj["y"][l][keep], w_tol=W_TOL_STACK)
     dx = np.max(np.abs(gx[keep] - traj["x_out"][keep])) / np.max(np.abs(traj["x_out"][keep]))
     print(f"config 4: final x {dx:.3e}", flush=True)
     assert dx <= hz.Y_TOL
+    # per layer on the oracle's own inputs, inside a full 2048-token chunk (so
+    # the prefill kernels run as in the stack); the other rows are chunk 0's
+    # generator rows
+    per = 512 * inputs.blob_bytes()
+    k = keep.size
+    for l in range(48):
+        xin = x[:chunk].copy()
+        xin[:k] = traj["x_in"][l][keep]
+        ids, w, y, _ = hz.gpu_layer(xin, routers[l], store[l * per:(l + 1) * per],
+                                    bias=biases[l], flags=3)
+        hz.check(f"config 4 forced layer {l}", ids[:k], w[:k], y[:k], traj["ids"][l][keep],
+                 traj["w"][l][keep], traj["y"][l][keep])
