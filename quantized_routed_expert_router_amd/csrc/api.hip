@@ -2,9 +2,10 @@
 // host-side argument validation, workspace carving and kernel launches.
 // Nothing here synchronises, allocates or reads device memory.
 #include "common.hpp"
+#include "quant.hpp"
 
 namespace strata {
-hipError_t launch_prep(const float *x, int T, int rmsnorm, float *xhat, ActQ xq, __half *xperm,
+hipError_t launch_prep(const float *x, int T, int rmsnorm, float *xhat, __half *xperm,
                        hipStream_t st);
 hipError_t launch_logits(const float *xhat, int T, const uint16_t *R, const float *bias,
                          float *logits, hipStream_t st);
@@ -13,9 +14,14 @@ hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *sl
                         int32_t *active, hipStream_t st);
 hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_items,
                        int32_t *mlist, int32_t *nitems, hipStream_t st);
+hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
+                               int rmsnorm, float *lraw, XQ xq, bool prep, int32_t *ids,
+                               float *w, int group, int32_t *offsets, int32_t *slots,
+                               int32_t *active, hipStream_t st);
+hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, hipStream_t st);
 hipError_t launch_decode_experts(const uint8_t *blobs, const int32_t *offsets,
-                                 const int32_t *slots, const int32_t *active, ActQ xq, ActQ hq,
-                                 float *out, int T, hipStream_t st);
+                                 const int32_t *slots, const int32_t *active, XQ xq, HQ hq,
+                                 float *out, int T, int n_cu, hipStream_t st);
 hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
@@ -43,10 +49,10 @@ template <class P> P *at(void *ws, size_t off) { return reinterpret_cast<P *>((u
 
 struct Carve {
     Ws L;
-    float *xhat;
-    ActQ xq, hq;
+    float *xhat, *logits, *w, *out;
     __half *xperm, *hperm;
-    float *logits, *w, *out;
+    XQ xq;
+    HQ hq;
     int32_t *offsets, *slots, *active, *ids, *mlist, *nitems;
 };
 
@@ -56,14 +62,12 @@ Carve carve(void *ws, int T)
     c.L = ws_layout(T);
     const Ws &L = c.L;
     c.xhat = at<float>(ws, L.xhat);
-    const bool dec = is_decode(T);
-    c.xq = ActQ{dec ? at<uint32_t>(ws, L.xq_dig) : nullptr, at<float>(ws, L.xq_scale),
-                at<int32_t>(ws, L.xq_sum)};
-    c.hq = ActQ{dec ? at<uint32_t>(ws, L.hq_dig) : nullptr, at<float>(ws, L.hq_scale),
-                at<int32_t>(ws, L.hq_sum)};
-    c.xperm = dec ? nullptr : at<__half>(ws, L.xperm);
-    c.hperm = dec ? nullptr : at<__half>(ws, L.hperm);
+    c.xperm = at<__half>(ws, L.xperm);
     c.logits = at<float>(ws, L.logits);
+    c.xq = XQ{at<uint32_t>(ws, L.xq_dig), at<float>(ws, L.xq_scale), at<int32_t>(ws, L.xq_sum),
+              at<float>(ws, L.inv_rms)};
+    c.hq = HQ{at<uint32_t>(ws, L.hq_dig), at<float>(ws, L.hq_scale), at<int32_t>(ws, L.hq_sum)};
+    c.hperm = at<__half>(ws, L.hperm);
     c.offsets = at<int32_t>(ws, L.offsets);
     c.slots = at<int32_t>(ws, L.slots);
     c.active = at<int32_t>(ws, L.active);
@@ -75,6 +79,23 @@ Carve carve(void *ws, int T)
     return c;
 }
 
+// Compute units of the current device (cached per device).
+int n_cu()
+{
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 #define STRATA_TRY(expr)                                                                           \
     do {                                                                                           \
         hipError_t e_ = (expr);                                                                    \
@@ -82,16 +103,29 @@ Carve carve(void *ws, int T)
             return STRATA_E_HIP;                                                                   \
     } while (0)
 
+// The experts for T tokens of a grouped layer (activation prep already done).
 int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
                 const int32_t *slots, const int32_t *active, float *out, int T, hipStream_t st)
 {
     if (is_decode(T)) {
-        STRATA_TRY(launch_decode_experts(blobs, offsets, slots, active, c.xq, c.hq, out, T, st));
+        STRATA_TRY(launch_decode_experts(blobs, offsets, slots, active, c.xq, c.hq, out, T, n_cu(),
+                                         st));
     } else {
         STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
         STRATA_TRY(launch_prefill_experts(blobs, offsets, slots, active, c.mlist, c.nitems,
                                           c.L.max_items, c.xperm, c.hperm, out, T, st));
     }
+    return STRATA_OK;
+}
+
+// Activation prep for the experts (decode: inverse RMS and 16-bit blocks;
+// prefill: normalised fp32 and K-ordered fp16 copies).
+int run_prep(const Carve &c, const float *x, int T, int rms, hipStream_t st)
+{
+    if (is_decode(T))
+        STRATA_TRY(launch_prep_decode(x, T, rms, c.xq, st));
+    else
+        STRATA_TRY(launch_prep(x, T, rms, c.xhat, c.xperm, st));
     return STRATA_OK;
 }
 
@@ -126,10 +160,15 @@ int strata_moe_route(const float *x, int T, const uint16_t *router, const float 
         return STRATA_E_ALIGN;
     hipStream_t st = (hipStream_t)stream;
     Carve c = carve(ws, T);
-    STRATA_TRY(launch_prep(x, T, flags & STRATA_RMSNORM, c.xhat, ActQ{nullptr, nullptr, nullptr},
-                           nullptr, st));
-    STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
-    STRATA_TRY(launch_topk(c.logits, T, ids, w, st));
+    const int rms = flags & STRATA_RMSNORM;
+    if (is_decode(T)) {
+        STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, false, ids, w, 0,
+                                       nullptr, nullptr, nullptr, st));
+    } else {
+        STRATA_TRY(launch_prep(x, T, rms, c.xhat, nullptr, st));
+        STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
+        STRATA_TRY(launch_topk(c.logits, T, ids, w, st));
+    }
     return STRATA_OK;
 }
 
@@ -166,7 +205,8 @@ int strata_moe_experts(const float *x, int T, const uint8_t *blobs, const int32_
         return STRATA_E_ALIGN;
     hipStream_t st = (hipStream_t)stream;
     Carve c = carve(ws, T);
-    STRATA_TRY(launch_prep(x, T, flags & STRATA_RMSNORM, c.xhat, c.xq, c.xperm, st));
+    if ((rc = run_prep(c, x, T, flags & STRATA_RMSNORM, st)))
+        return rc;
     return run_experts(c, blobs, offsets, slots, active, out, T, st);
 }
 
@@ -205,10 +245,16 @@ int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
     Carve c = carve(ws, T);
     int32_t *ids_o = ids ? ids : c.ids;
     float *w_o = w ? w : c.w;
-    STRATA_TRY(launch_prep(x, T, flags & STRATA_RMSNORM, c.xhat, c.xq, c.xperm, st));
-    STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
-    STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
-    STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, st));
+    const int rms = flags & STRATA_RMSNORM;
+    if (is_decode(T)) {
+        STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, true, ids_o, w_o, 1,
+                                       c.offsets, c.slots, c.active, st));
+    } else {
+        STRATA_TRY(launch_prep(x, T, rms, c.xhat, c.xperm, st));
+        STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
+        STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
+        STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, st));
+    }
     if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st)))
         return rc;
     const bool res = flags & STRATA_RESIDUAL;

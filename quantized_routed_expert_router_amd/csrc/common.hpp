@@ -30,15 +30,6 @@ static_assert((size_t)H * ROW_D == MAT, "down matrix size");
 // Decode path: T up to this many tokens runs the dot-product kernels.
 constexpr int DECODE_T_MAX = 16;
 
-// 16-bit activation quantisation for the decode kernels: per 32-value segment
-// a scale s = max|v| / QMAX and integers q = rint(v / s), |q| <= QMAX, stored
-// as four signed base-16 digits packed for v_dot8_i32_i4 (see quant.hpp).
-constexpr int SEG = 32;
-constexpr int QMAX = 30000;
-constexpr int SEG_DWORDS = 16;                 // 32 values x 4 digits x 4 bits
-constexpr int XSEG = H / SEG;                  // 80 segments per token
-constexpr int HSEG = FF / SEG;                 // 20 segments per slot
-
 // Prefill path tiles.
 constexpr int PF_M = 64;                       // tokens per M-chunk
 constexpr int PF_NT_G = 128;                   // FF rows per gate/up work item
@@ -46,14 +37,16 @@ constexpr int PF_NT_D = 256;                   // output rows per down work item
 constexpr int PF_NTILES_G = FF / PF_NT_G;      // 5
 constexpr int PF_NTILES_D = H / PF_NT_D;       // 10
 
-// Workspace regions (byte offsets, 256-aligned) for a call with T tokens.
+// Workspace regions (byte offsets, 256-aligned) for a call with T tokens;
+// Td = T on the decode path (T <= DECODE_T_MAX) else 0, Tp the converse.
 struct Ws {
-    size_t xhat;       // f32 [T][H]
-    size_t xq_dig;     // u32 [Td][XSEG][16]
-    size_t xq_scale;   // f32 [Td][XSEG]
-    size_t xq_sum;     // i32 [Td][XSEG]
-    size_t xperm;      // f16 [Tp][H]
-    size_t logits;     // f32 [T][E]
+    size_t xhat;       // f32 [Tp][H]        router input (prefill)
+    size_t xperm;      // f16 [Tp][H]        MFMA-ordered activations (prefill)
+    size_t logits;     // f32 [T][E]         logits (prefill) / raw logits (decode)
+    size_t inv_rms;    // f32 [Td]
+    size_t xq_dig;     // u32 [Td][40][32]   16-bit x, one 64-block per block column
+    size_t xq_scale;   // f32 [Td][40]
+    size_t xq_sum;     // i32 [Td][40]
     size_t offsets;    // i32 [E+1]
     size_t slots;      // i32 [T*K]
     size_t active;     // i32 [1+E]
@@ -61,10 +54,10 @@ struct Ws {
     size_t w;          // f32 [T*K]
     size_t mlist;      // i32 [2][max items]
     size_t nitems;     // i32 [4]
-    size_t hq_dig;     // u32 [Td*K][HSEG][16]
-    size_t hq_scale;   // f32 [Td*K][HSEG]
-    size_t hq_sum;     // i32 [Td*K][HSEG]
-    size_t hperm;      // f16 [Tp*K][FF] (grouped order)
+    size_t hq_dig;     // u32 [Td*K][40][8]  16-bit h per 16 values
+    size_t hq_scale;   // f32 [Td*K][40]
+    size_t hq_sum;     // i32 [Td*K][40]
+    size_t hperm;      // f16 [Tp*K][FF]     (grouped order)
     size_t out;        // f32 [T*K][H]
     size_t total;
     int max_items;
@@ -87,12 +80,14 @@ inline Ws ws_layout(int T)
         o = align256(o + bytes);
         return at;
     };
-    L.xhat = take((size_t)T * H * 4);
-    L.xq_dig = take(Td * XSEG * SEG_DWORDS * 4);
-    L.xq_scale = take(Td * XSEG * 4);
-    L.xq_sum = take(Td * XSEG * 4);
+    const size_t nb = H / QK, ns = FF / 16;
+    L.xhat = take(Tp * H * 4);
     L.xperm = take(Tp * H * 2);
     L.logits = take((size_t)T * E * 4);
+    L.inv_rms = take(Td * 4);
+    L.xq_dig = take(Td * nb * 32 * 4);
+    L.xq_scale = take(Td * nb * 4);
+    L.xq_sum = take(Td * nb * 4);
     L.offsets = take((E + 1) * 4);
     L.slots = take((size_t)T * K * 4);
     L.active = take((1 + E) * 4);
@@ -101,21 +96,14 @@ inline Ws ws_layout(int T)
     L.max_items = pf_max_items(T);
     L.mlist = take((size_t)2 * L.max_items * 4);
     L.nitems = take(16);
-    L.hq_dig = take(Td * K * HSEG * SEG_DWORDS * 4);
-    L.hq_scale = take(Td * K * HSEG * 4);
-    L.hq_sum = take(Td * K * HSEG * 4);
+    L.hq_dig = take(Td * K * ns * 8 * 4);
+    L.hq_scale = take(Td * K * ns * 4);
+    L.hq_sum = take(Td * K * ns * 4);
     L.hperm = take(Tp * K * FF * 2);
     L.out = take((size_t)T * K * H * 4);
     L.total = o;
     return L;
 }
-
-// Quantised activations (decode path): one vector = nseg segments.
-struct ActQ {
-    uint32_t *dig;  // [vec][nseg][16]
-    float *scale;   // [vec][nseg]
-    int32_t *sum;   // [vec][nseg]
-};
 
 // ---------------------------------------------------------------- device helpers
 __device__ inline float half_bits_to_float(uint32_t bits)
@@ -144,6 +132,101 @@ __device__ inline float wave_max(float v)
     for (int m = 32; m >= 1; m >>= 1)
         v = fmaxf(v, __shfl_xor(v, m, 64));
     return v;
+}
+
+// ---------------------------------------------------------------- DPP lane exchange
+// dpp_ctrl encodings (GCN/CDNA): quad_perm 0x00-0xFF, row_shr:n 0x110+n,
+// row_mirror 0x140, row_half_mirror 0x141.  Lanes without a source get `old`.
+template <int CTRL> __device__ inline int dpp_i(int v, int old = 0)
+{
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ inline float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_HMIRROR = 0x141;  // lane i <- 7 - i within each 8
+constexpr int DPP_MIRROR = 0x140;   // lane i <- 15 - i within each 16
+constexpr int DPP_SHR4 = 0x114;
+constexpr int DPP_SHR8 = 0x118;
+
+// Sum / max over each group of 8 lanes; every lane of the group gets the
+// result, lanes of one group all computing it in the same order.
+__device__ inline float sum8(float v)
+{
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    return v + dpp_f<DPP_HMIRROR>(v);
+}
+__device__ inline float sum16(float v) { v = sum8(v); return v + dpp_f<DPP_MIRROR>(v); }
+__device__ inline float max16(float v)
+{
+    v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+    v = fmaxf(v, dpp_f<DPP_HMIRROR>(v));
+    return fmaxf(v, dpp_f<DPP_MIRROR>(v));
+}
+__device__ inline int isum16(int v)
+{
+    v += dpp_i<DPP_XOR1>(v);
+    v += dpp_i<DPP_XOR2>(v);
+    v += dpp_i<DPP_HMIRROR>(v);
+    return v + dpp_i<DPP_MIRROR>(v);
+}
+// Whole-wave results, uniform in every lane: rows of 16 reduced by DPP, then
+// the four row results combined in a fixed order from lanes 0, 16, 32, 48.
+__device__ inline float wave_sum_dpp(float v)
+{
+    v = sum16(v);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (a + b) + (c + d);
+}
+__device__ inline float wave_max_dpp(float v)
+{
+    v = max16(v);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Wave-wide argmax of (p desc, id asc); every lane returns the winner.
+__device__ inline void wave_argmax(float &bp, int &be)
+{
+    // within rows of 16 (all lanes of a row end with the row's winner)
+#define STRATA_ARGMAX_STEP(CTRL)                                                                   \
+    {                                                                                              \
+        const float op = dpp_f<CTRL>(bp);                                                          \
+        const int oe = dpp_i<CTRL>(be);                                                            \
+        if (op > bp || (op == bp && oe < be)) {                                                    \
+            bp = op;                                                                               \
+            be = oe;                                                                               \
+        }                                                                                          \
+    }
+    STRATA_ARGMAX_STEP(DPP_XOR1)
+    STRATA_ARGMAX_STEP(DPP_XOR2)
+    STRATA_ARGMAX_STEP(DPP_HMIRROR)
+    STRATA_ARGMAX_STEP(DPP_MIRROR)
+#undef STRATA_ARGMAX_STEP
+    float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bp), 0));
+    int id = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+    for (int rl = 16; rl < 64; rl += 16) {
+        const float op = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bp), rl));
+        const int oe = __builtin_amdgcn_readlane(be, rl);
+        if (op > p || (op == p && oe < id)) {
+            p = op;
+            id = oe;
+        }
+    }
+    bp = p;
+    be = id;
 }
 
 } // namespace strata

@@ -6,18 +6,15 @@
 //
 // Kernels:
 //  prep_kernel    one workgroup per token: optional RMSNorm (eps 1e-6, unit
-//                 gain), xhat in fp32 for the router, and either the 16-bit
-//                 segment quantisation (decode experts) or fp16 xhat in the
-//                 K order the prefill MFMA kernels consume.
-//  gemv_kernel    decode T: one wave per router row, all tokens; the row is
-//                 read once (5 KB), every lane owns the same 40 columns of
-//                 every row, so identical rows give identical logits.
-//  gemm_kernel    larger T: 64 x 64 fp32 tiles through LDS; each logit is a
-//                 sequential k = 0..2559 FMA chain, again row-independent.
+//                 gain), xhat in fp32 for the router and fp16 xhat in the K
+//                 order the prefill MFMA kernels consume.  (Decode-sized T
+//                 uses route_decode.hip.)
+//  gemm_kernel    64 x 64 fp32 tiles through LDS; each logit is a sequential
+//                 k = 0..2559 FMA chain, so identical router rows give
+//                 identical logits.
 //  topk_kernel    one wave per token: softmax in fp32, ten rounds of a
 //                 wave-wide argmax on (p desc, id asc), clamped renorm.
 #include "common.hpp"
-#include "quant.hpp"
 
 namespace strata {
 
@@ -32,7 +29,7 @@ __device__ inline int pf_col_of_pos(int pi)
 constexpr int PREP_THREADS = 256;
 
 __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
-    const float *__restrict__ x, int rmsnorm, float *__restrict__ xhat, ActQ xq,
+    const float *__restrict__ x, int rmsnorm, float *__restrict__ xhat,
     __half *__restrict__ xperm)
 {
     __shared__ float xs[H];
@@ -63,65 +60,11 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
         xhat[(size_t)t * H + tid + PREP_THREADS * i] = h;
     }
     __syncthreads();
-    if (xq.dig) {
-        const int wave = tid >> 6, lane = tid & 63;
-        for (int p = wave; p < XSEG / 2; p += PREP_THREADS / 64) {
-            const int seg = 2 * p + (lane >> 5);
-            const float h = xs[seg * SEG + (lane & 31)];
-            const size_t sg = (size_t)t * XSEG + seg;
-            quant_seg32(h, lane & 31, true, xq.dig + sg * SEG_DWORDS, xq.scale + sg, xq.sum + sg);
-        }
-    }
     if (xperm) {
         for (int pos = tid; pos < H; pos += PREP_THREADS) {
             const int b = pos >> 6;
             xperm[(size_t)t * H + pos] = __float2half_rn(xs[b * QK + pf_col_of_pos(pos & 63)]);
         }
-    }
-}
-
-// ---------------------------------------------------------------- router GEMV
-constexpr int GV_THREADS = 256;
-constexpr int GV_ROWS = GV_THREADS / 64;   // one router row per wave
-
-__global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
-    const float *__restrict__ xhat, int T, const uint16_t *__restrict__ R,
-    const float *__restrict__ bias, float *__restrict__ logits)
-{
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = blockIdx.x * GV_ROWS + wave;
-    const uint4 *row = reinterpret_cast<const uint4 *>(R + (size_t)e * H);
-    float rv[40];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        const uint4 q = row[lane + 64 * i];
-        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            rv[8 * i + 2 * j] = bf16_bits_to_float(u[j]);
-            rv[8 * i + 2 * j + 1] = bf16_bits_to_float(u[j] >> 16);
-        }
-    }
-    const float b = bias ? bias[e] : 0.f;
-    for (int t = 0; t < T; ++t) {
-        const float4 *xr = reinterpret_cast<const float4 *>(xhat + (size_t)t * H);
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const float4 a = xr[2 * (lane + 64 * i)];
-            const float4 c = xr[2 * (lane + 64 * i) + 1];
-            acc = fmaf(rv[8 * i + 0], a.x, acc);
-            acc = fmaf(rv[8 * i + 1], a.y, acc);
-            acc = fmaf(rv[8 * i + 2], a.z, acc);
-            acc = fmaf(rv[8 * i + 3], a.w, acc);
-            acc = fmaf(rv[8 * i + 4], c.x, acc);
-            acc = fmaf(rv[8 * i + 5], c.y, acc);
-            acc = fmaf(rv[8 * i + 6], c.z, acc);
-            acc = fmaf(rv[8 * i + 7], c.w, acc);
-        }
-        acc = wave_sum(acc);
-        if (lane == 0)
-            logits[(size_t)t * E + e] = acc + b;
     }
 }
 
@@ -212,7 +155,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 #pragma unroll
     for (int i = 1; i < 8; ++i)
         m = fmaxf(m, l[i]);
-    m = wave_max(m);
+    m = wave_max_dpp(m);
     float p[8];
     float s = 0.f;
 #pragma unroll
@@ -220,7 +163,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
         p[i] = expf(l[i] - m);
         s += p[i];
     }
-    s = wave_sum(s);
+    s = wave_sum_dpp(s);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         p[i] = p[i] / s;
@@ -240,17 +183,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
                 be = e;
             }
         }
-#pragma unroll
-        for (int x = 32; x >= 1; x >>= 1) {
-            const float op = __shfl_xor(bp, x, 64);
-            const int oe = __shfl_xor(be, x, 64);
-            if (op > bp || (op == bp && oe < be)) {
-                bp = op;
-                be = oe;
-            }
-        }
+        wave_argmax(bp, be);
         if ((be & 63) == lane)
-            taken |= 1u << (be >> 6);
+            taken |= 1u << ((be >> 6) & 7);
         if (lane == k) {
             my_id = be;
             my_p = bp;
@@ -264,23 +199,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     }
 }
 
-hipError_t launch_prep(const float *x, int T, int rmsnorm, float *xhat, ActQ xq, __half *xperm,
+hipError_t launch_prep(const float *x, int T, int rmsnorm, float *xhat, __half *xperm,
                        hipStream_t st)
 {
-    hipLaunchKernelGGL(prep_kernel, dim3(T), dim3(PREP_THREADS), 0, st, x, rmsnorm, xhat, xq,
-                       xperm);
+    hipLaunchKernelGGL(prep_kernel, dim3(T), dim3(PREP_THREADS), 0, st, x, rmsnorm, xhat, xperm);
     return hipGetLastError();
 }
 
 hipError_t launch_logits(const float *xhat, int T, const uint16_t *R, const float *bias,
                          float *logits, hipStream_t st)
 {
-    if (is_decode(T))
-        hipLaunchKernelGGL(gemv_kernel, dim3(E / GV_ROWS), dim3(GV_THREADS), 0, st, xhat, T, R,
-                           bias, logits);
-    else
-        hipLaunchKernelGGL(gemm_kernel, dim3((T + GM_TILE - 1) / GM_TILE, E / GM_TILE),
-                           dim3(256), 0, st, xhat, T, R, bias, logits);
+    hipLaunchKernelGGL(gemm_kernel, dim3((T + GM_TILE - 1) / GM_TILE, E / GM_TILE), dim3(256), 0,
+                       st, xhat, T, R, bias, logits);
     return hipGetLastError();
 }
 

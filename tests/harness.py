@@ -78,20 +78,20 @@ def gpu_composed(x, R_bits, blobs_dev, bias=None, flags=0):
                 active=active.cpu().numpy(), out=out.cpu().numpy())
 
 
-def check(tag, ids, w, y, oids, ow, oy, w_tol=W_TOL):
-    """Assert parity and return diagnostics."""
+def check(tag, ids, w, y, oids, ow, oy, w_tol=W_TOL, y_tol=Y_TOL):
+    """Assert parity and return max|dy|/max|y| (all metrics printed first)."""
     assert ids.shape == oids.shape
     bad = np.nonzero(np.any(ids != oids, axis=1))[0]
-    assert bad.size == 0, f"{tag}: ids differ on rows {bad[:8]}: {ids[bad[:2]]} vs {oids[bad[:2]]}"
     dw = float(np.max(np.abs(w.astype(np.float64) - ow)))
-    assert dw <= w_tol, f"{tag}: |dw| = {dw}"
     ymax = float(np.max(np.abs(oy)))
     dy = np.abs(y.astype(np.float64) - oy)
     rel = float(dy.max() / ymax) if ymax > 0 else float(dy.max())
     worst_tok = float(np.max(dy.max(axis=1) / np.maximum(np.abs(oy).max(axis=1), 1e-30)))
-    print(f"[{tag}] max|dy|/max|y| = {rel:.3e} (worst token {worst_tok:.3e}), max|dw| = {dw:.2e}",
-          flush=True)
-    assert rel <= Y_TOL, f"{tag}: max|dy|/max|y| = {rel}"
+    print(f"[{tag}] max|dy|/max|y| = {rel:.3e} (worst token {worst_tok:.3e}), max|dw| = {dw:.2e}, "
+          f"rows with other ids: {bad.size}", flush=True)
+    assert bad.size == 0, f"{tag}: ids differ on rows {bad[:8]}: {ids[bad[:2]]} vs {oids[bad[:2]]}"
+    assert dw <= w_tol, f"{tag}: |dw| = {dw}"
+    assert rel <= y_tol, f"{tag}: max|dy|/max|y| = {rel}"
     return rel
 
 
