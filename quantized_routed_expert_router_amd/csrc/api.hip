@@ -17,11 +17,12 @@ hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_it
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
                                int rmsnorm, float *lraw, XQ xq, bool prep, int32_t *ids,
                                float *w, int group, int32_t *offsets, int32_t *slots,
-                               int32_t *active, hipStream_t st);
-hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, hipStream_t st);
-hipError_t launch_decode_experts(const uint8_t *blobs, const int32_t *offsets,
-                                 const int32_t *slots, const int32_t *active, XQ xq, HQ hq,
-                                 float *out, int T, int n_cu, hipStream_t st);
+                               int32_t *active, int4 *erec, hipStream_t st);
+hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const int32_t *offsets,
+                              const int32_t *slots, const int32_t *active, int4 *erec,
+                              hipStream_t st);
+hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
+                                 XQ xq, HQ hq, float *out, int T, int n_cu, hipStream_t st);
 hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
@@ -54,6 +55,7 @@ struct Carve {
     XQ xq;
     HQ hq;
     int32_t *offsets, *slots, *active, *ids, *mlist, *nitems;
+    int4 *erec;
 };
 
 Carve carve(void *ws, int T)
@@ -71,6 +73,7 @@ Carve carve(void *ws, int T)
     c.offsets = at<int32_t>(ws, L.offsets);
     c.slots = at<int32_t>(ws, L.slots);
     c.active = at<int32_t>(ws, L.active);
+    c.erec = at<int4>(ws, L.erec);
     c.ids = at<int32_t>(ws, L.ids);
     c.w = at<float>(ws, L.w);
     c.mlist = at<int32_t>(ws, L.mlist);
@@ -108,8 +111,7 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
                 const int32_t *slots, const int32_t *active, float *out, int T, hipStream_t st)
 {
     if (is_decode(T)) {
-        STRATA_TRY(launch_decode_experts(blobs, offsets, slots, active, c.xq, c.hq, out, T, n_cu(),
-                                         st));
+        STRATA_TRY(launch_decode_experts(blobs, c.erec, slots, c.xq, c.hq, out, T, n_cu(), st));
     } else {
         STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
         STRATA_TRY(launch_prefill_experts(blobs, offsets, slots, active, c.mlist, c.nitems,
@@ -118,12 +120,14 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
     return STRATA_OK;
 }
 
-// Activation prep for the experts (decode: inverse RMS and 16-bit blocks;
-// prefill: normalised fp32 and K-ordered fp16 copies).
-int run_prep(const Carve &c, const float *x, int T, int rms, hipStream_t st)
+// Activation prep for the experts (decode: inverse RMS, 16-bit blocks and the
+// work records of the caller's grouping; prefill: normalised fp32 and
+// K-ordered fp16 copies).
+int run_prep(const Carve &c, const float *x, int T, int rms, const int32_t *offsets,
+             const int32_t *slots, const int32_t *active, hipStream_t st)
 {
     if (is_decode(T))
-        STRATA_TRY(launch_prep_decode(x, T, rms, c.xq, st));
+        STRATA_TRY(launch_prep_decode(x, T, rms, c.xq, offsets, slots, active, c.erec, st));
     else
         STRATA_TRY(launch_prep(x, T, rms, c.xhat, c.xperm, st));
     return STRATA_OK;
@@ -163,7 +167,7 @@ int strata_moe_route(const float *x, int T, const uint16_t *router, const float 
     const int rms = flags & STRATA_RMSNORM;
     if (is_decode(T)) {
         STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, false, ids, w, 0,
-                                       nullptr, nullptr, nullptr, st));
+                                       nullptr, nullptr, nullptr, nullptr, st));
     } else {
         STRATA_TRY(launch_prep(x, T, rms, c.xhat, nullptr, st));
         STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
@@ -205,7 +209,7 @@ int strata_moe_experts(const float *x, int T, const uint8_t *blobs, const int32_
         return STRATA_E_ALIGN;
     hipStream_t st = (hipStream_t)stream;
     Carve c = carve(ws, T);
-    if ((rc = run_prep(c, x, T, flags & STRATA_RMSNORM, st)))
+    if ((rc = run_prep(c, x, T, flags & STRATA_RMSNORM, offsets, slots, active, st)))
         return rc;
     return run_experts(c, blobs, offsets, slots, active, out, T, st);
 }
@@ -248,7 +252,7 @@ int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
     const int rms = flags & STRATA_RMSNORM;
     if (is_decode(T)) {
         STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, true, ids_o, w_o, 1,
-                                       c.offsets, c.slots, c.active, st));
+                                       c.offsets, c.slots, c.active, c.erec, st));
     } else {
         STRATA_TRY(launch_prep(x, T, rms, c.xhat, c.xperm, st));
         STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));

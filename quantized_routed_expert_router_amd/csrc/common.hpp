@@ -50,11 +50,12 @@ struct Ws {
     size_t offsets;    // i32 [E+1]
     size_t slots;      // i32 [T*K]
     size_t active;     // i32 [1+E]
+    size_t erec;       // i32x4 [1+E]        decode work records (header + one per active expert)
     size_t ids;        // i32 [T*K]
     size_t w;          // f32 [T*K]
     size_t mlist;      // i32 [2][max items]
     size_t nitems;     // i32 [4]
-    size_t hq_dig;     // u32 [Td*K][40][8]  16-bit h per 16 values
+    size_t hq_dig;     // u32 [Td*K][10][32] 16-bit h per 16 values (64-value blocks)
     size_t hq_scale;   // f32 [Td*K][40]
     size_t hq_sum;     // i32 [Td*K][40]
     size_t hperm;      // f16 [Tp*K][FF]     (grouped order)
@@ -91,12 +92,13 @@ inline Ws ws_layout(int T)
     L.offsets = take((E + 1) * 4);
     L.slots = take((size_t)T * K * 4);
     L.active = take((1 + E) * 4);
+    L.erec = take(Td ? (size_t)(1 + E) * 16 : 0);
     L.ids = take((size_t)T * K * 4);
     L.w = take((size_t)T * K * 4);
     L.max_items = pf_max_items(T);
     L.mlist = take((size_t)2 * L.max_items * 4);
     L.nitems = take(16);
-    L.hq_dig = take(Td * K * ns * 8 * 4);
+    L.hq_dig = take(Td * K * (FF / QK) * 32 * 4);
     L.hq_scale = take(Td * K * ns * 4);
     L.hq_sum = take(Td * K * ns * 4);
     L.hperm = take(Tp * K * FF * 2);

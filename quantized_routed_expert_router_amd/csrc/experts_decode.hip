@@ -7,89 +7,125 @@
 // expert's blob is read once per call however many tokens of the window chose
 // it (the window dedup of section "The plan: three destinations per expert").
 //
-// Both kernels are HBM streams over small work items with the next item's
-// bytes prefetched into registers while the current one is computed:
-//  dec_gateup  item = (active expert, 16-row FF slice): 16 gate rows and the
-//              same 16 up rows (23 KB) staged in LDS; 320 threads = 5 waves,
-//              wave w owns block columns 8w..8w+7 for 8 rows per pass; a
-//              block is 32 v_dot8_i32_i4 against the token's 16-bit
-//              activations; rows are reduced with DPP in fixed order, then
-//              h = silu(g) * u is quantised per 16 values for the down pass.
-//  dec_down    item = (active expert, 32 output rows): 320 threads = 32 rows
-//              x 10 block columns; writes the unweighted output per slot.
-// Workgroups take contiguous item ranges, so consecutive items of one
-// workgroup belong to the same expert.  Every reduction has a fixed order:
-// results are bitwise reproducible and independent of the other tokens.
+// Both kernels put one weight row on each lane.  A workgroup reads its rows
+// with coalesced 16-byte loads into LDS, then every lane walks its own row
+// block by block: the 16 code bytes give two nibble-masked dwords per 16
+// codes, and v_dot8 multiplies them with the token's 16-bit activation digits
+// (quant.hpp).  The activation operand is the same for the 16 lanes of a row,
+// so it reaches them by a DPP row broadcast inside the v_dot8: per lane, two
+// registers carry a whole 64-value block.
+//
+//  dec_gateup  item = (active expert, 16 FF rows): the 16 gate and 16 up rows
+//              (23 KB).  320 threads = 5 waves; lane (r = lane / 16, l) takes
+//              row l of gate (r even) or up (r odd) and block columns
+//              4 s .. 4 s + 3 with s = 2 w + r / 2.  Partial sums meet in a
+//              fixed order; wave 0 forms h = silu(g) * u for the 16 rows and
+//              quantises them as one 16-value segment.  The next item's bytes
+//              are loaded into registers while the current one is computed.
+//  dec_down    item = (active expert, 32 output rows), one wave: lane (r, l)
+//              takes row 16 (r % 2) + l and block columns 2 j + r / 2; the two
+//              halves of each row are added and the row's value written per
+//              slot.  Four items per workgroup.
+// Every sum has a fixed order, so results are bitwise reproducible and do not
+// depend on the other tokens of the call.
 #include "common.hpp"
 #include "quant.hpp"
 
 namespace strata {
 
+// ------------------------------------------------------------------ gate / up
 constexpr int DG_THREADS = 320;
-constexpr int DG_SLICE = 16;                       // FF rows per item
-constexpr int DG_SLICES = FF / DG_SLICE;           // 40
-constexpr int DG_ROWS = 2 * DG_SLICE;              // 16 gate + 16 up rows
-constexpr int DG_BYTES = DG_ROWS * ROW_G;          // 23,040
-constexpr int DG_CHUNKS = DG_BYTES / 16;           // 1,440
+constexpr int DG_SEG = 16;                          // FF rows per item (one h segment)
+constexpr int DG_SEGS = FF / DG_SEG;                // 40
+constexpr int DG_ROWS = 2 * DG_SEG;                 // 16 gate + 16 up rows
+constexpr int DG_CPR = ROW_G / 16;                  // 45 16-byte chunks per row
+constexpr int DG_CHUNKS = DG_ROWS * DG_CPR;         // 1,440
+constexpr int DG_RS = ROW_G / 4 + 1;                // LDS row stride in dwords (181, odd)
 constexpr int DG_LOADS = (DG_CHUNKS + DG_THREADS - 1) / DG_THREADS;   // 5
+static_assert(DG_LOADS == 5 && DG_CHUNKS > 4 * DG_THREADS, "five loads per thread");
+static_assert(5 * 2 * 4 == NB_G, "5 waves x 2 column streams x 4 block columns");
 
-struct ExpertRange {
-    int ok, e, beg, ntok;
+// Records of the grouping for the decode kernels: erec[0].x = number of active
+// experts, erec[1 + a] = {expert, first grouped slot, token count, first slot}.
+__device__ inline int active_count(const int4 *erec, int T)
+{
+    return min(max(erec[0].x, 0), min(T * K, E));
+}
+
+// Activation operands of one token for lane column stream s: per block column
+// 4 s + j the pair (dword l, dword 16 + l), the block scale times the inverse
+// RMS, and the sum of q.
+struct XOps {
+    uint2 d0, d1, d2, d3;
+    float4 sc;
+    int4 qs;
 };
 
-__device__ inline ExpertRange expert_of(int a, const int32_t *offsets, const int32_t *active,
-                                        int nslot)
+__device__ inline XOps load_xops(const XQ &xq, int t, int s, int l)
 {
-    ExpertRange r{0, 0, 0, 0};
-    const int e = active[1 + a];
-    if (e < 0 || e >= E)
-        return r;
-    r.ok = 1;
-    r.e = e;
-    r.beg = min(max(offsets[e], 0), nslot);
-    r.ntok = min(max(offsets[e + 1], r.beg), nslot) - r.beg;
-    return r;
+    XOps o;
+    const size_t xb = (size_t)t * XBLK + 4 * s;
+    const uint2 *dp = reinterpret_cast<const uint2 *>(xq.dig + xb * BLK_DWORDS) + l;
+    o.d0 = dp[0];
+    o.d1 = dp[16];
+    o.d2 = dp[32];
+    o.d3 = dp[48];
+    const float r = xq.inv_rms[t];
+    const float4 sc = *reinterpret_cast<const float4 *>(xq.scale + xb);
+    o.sc = make_float4(sc.x * r, sc.y * r, sc.z * r, sc.w * r);
+    o.qs = *reinterpret_cast<const int4 *>(xq.sum + xb);
+    return o;
 }
 
-// Item range [lo, hi) of workgroup b out of G over n items.
-__device__ inline void item_range(int n, int b, int G, int &lo, int &hi)
+// One block of a row held in LDS: the 5 dwords from p hold it; ODD (block
+// column parity) says where the scale and the codes sit in them.
+template <int ODD>
+__device__ inline float block_dot(const uint32_t *p, uint2 D, float sx, int qs)
 {
-    lo = (int)(((long long)n * b) / G);
-    hi = (int)(((long long)n * (b + 1)) / G);
+    const uint32_t v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3], v4 = p[4];
+    constexpr uint32_t sel = ODD ? 0x07060504u : 0x05040302u;
+    const uint32_t w0 = __builtin_amdgcn_perm(v1, v0, sel);
+    const uint32_t w1 = __builtin_amdgcn_perm(v2, v1, sel);
+    const uint32_t w2 = __builtin_amdgcn_perm(v3, v2, sel);
+    const uint32_t w3 = __builtin_amdgcn_perm(v4, v3, sel);
+    const float d = half_bits_to_float(ODD ? (v0 >> 16) : v0);
+    int a0 = -qs, a1 = 0, a2 = 0, a3 = 0;
+    STRATA_QUARTER_EVEN(w0, D.x, a0, a1, a2, a3)
+    STRATA_QUARTER_ODD(w1, D.x, a0, a1, a2, a3)
+    STRATA_QUARTER_EVEN(w2, D.y, a0, a1, a2, a3)
+    STRATA_QUARTER_ODD(w3, D.y, a0, a1, a2, a3)
+    return (d * sx) * (float)digits_combine(a0, a1, a2, a3);
 }
 
-__global__ __launch_bounds__(DG_THREADS) void dec_gateup(
-    const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ slots, const int32_t *__restrict__ active, XQ xq, HQ hq, int T)
+__global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restrict__ blobs,
+                                                         const int4 *__restrict__ erec,
+                                                         const int32_t *__restrict__ slots, XQ xq,
+                                                         HQ hq, int T)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t wlds[DG_BYTES];
-    __shared__ float red[5][DG_ROWS];
-    __shared__ float gu[DG_ROWS];
+    __shared__ uint32_t wl[DG_ROWS * DG_RS];
+    __shared__ float part[5][DG_ROWS];
 
     const int nslot = T * K;
-    const int na = min(max(active[0], 0), min(nslot, E));
-    int lo, hi;
-    item_range(na * DG_SLICES, blockIdx.x, gridDim.x, lo, hi);
-    if (lo >= hi)
+    const int nitems = active_count(erec, T) * DG_SEGS;
+    int item = blockIdx.x;
+    if (item >= nitems)
         return;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int c = 8 * wave + (lane & 7);   // block column
-    const int r = lane >> 3;               // row within a pass
-    const BlockCol bc = block_col(c);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int r = lane >> 4, l = lane & 15;
+    const int s = 2 * wave + (r >> 1);                       // column stream: columns 4s..4s+3
+    const uint32_t *myrow = wl + ((r & 1) * DG_SEG + l) * DG_RS + 18 * s;
 
-    // The next item's bytes are held in p0..p4 (registers) from the moment the
-    // current item is in LDS until the top of the next iteration.
-    static_assert(DG_LOADS == 5 && DG_CHUNKS > 4 * DG_THREADS, "five loads per thread");
+    // Chunk q of an item (q < 720: gate rows, else up rows) goes to LDS row
+    // q / 45 at dword 4 (q % 45).
     uint4 p0, p1, p2, p3, p4 = make_uint4(0, 0, 0, 0);
     const bool has4 = tid + 4 * DG_THREADS < DG_CHUNKS;
-#define STRATA_DG_LD(P, I) P = (tid + DG_THREADS * (I)) < DG_CHUNKS / 2 ? g_[tid + DG_THREADS * (I)] \
-                                : u_[tid + DG_THREADS * (I) - DG_CHUNKS / 2];
-#define STRATA_DG_FETCH(ITEM)                                                                      \
+#define STRATA_DG_LD(P, I)                                                                         \
+    P = (tid + DG_THREADS * (I)) < DG_CHUNKS / 2 ? g_[tid + DG_THREADS * (I)]                      \
+                                                 : u_[tid + DG_THREADS * (I) - DG_CHUNKS / 2];
+#define STRATA_DG_FETCH(E_, SEG_)                                                                  \
     {                                                                                              \
-        const int a_ = (ITEM) / DG_SLICES, s_ = (ITEM) % DG_SLICES;                                \
-        int e_ = active[1 + a_];                                                                   \
-        e_ = (e_ < 0 || e_ >= E) ? 0 : e_;                                                         \
-        const uint8_t *blob_ = blobs + (size_t)e_ * BLOB + (size_t)s_ * DG_SLICE * ROW_G;          \
+        const uint8_t *blob_ = blobs + (size_t)(E_) * BLOB + (size_t)(SEG_) * DG_SEG * ROW_G;      \
         const uint4 *g_ = reinterpret_cast<const uint4 *>(blob_);                                  \
         const uint4 *u_ = reinterpret_cast<const uint4 *>(blob_ + MAT);                            \
         STRATA_DG_LD(p0, 0)                                                                        \
@@ -99,202 +135,227 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(
         if (has4)                                                                                  \
             STRATA_DG_LD(p4, 4)                                                                    \
     }
-    int cache_a = -1, slot0 = -1, d_tok = -1, qs = 0;
-    ExpertRange er{0, 0, 0, 0};
-    uint32_t D[BLK_DWORDS];
-    float sx = 0.f;
-    STRATA_DG_FETCH(lo)
-    for (int item = lo; item < hi; ++item) {
+#define STRATA_DG_ST(P, I)                                                                         \
+    {                                                                                              \
+        const int q_ = tid + DG_THREADS * (I);                                                     \
+        uint32_t *d_ = wl + (q_ / DG_CPR) * DG_RS + 4 * (q_ % DG_CPR);                             \
+        d_[0] = P.x;                                                                               \
+        d_[1] = P.y;                                                                               \
+        d_[2] = P.z;                                                                               \
+        d_[3] = P.w;                                                                               \
+    }
+    int4 rec = erec[1 + item / DG_SEGS];
+    STRATA_DG_FETCH(rec.x, item % DG_SEGS)
+    for (; item < nitems; item += gridDim.x) {
+        const int seg = item % DG_SEGS;
+        const int n = rec.z;
+        int slot = rec.w;
+        const int nxt = item + gridDim.x;
+        // token 0's operands and the next record are in flight with the weights
+        XOps xo = load_xops(xq, slot >= 0 && slot < nslot ? slot / K : 0, s, l);
+        const int4 rec_n = erec[1 + min(nxt, nitems - 1) / DG_SEGS];
         __syncthreads();   // the previous item's LDS readers are done
-        uint4 *dst = reinterpret_cast<uint4 *>(wlds);
-        dst[tid] = p0;
-        dst[tid + DG_THREADS] = p1;
-        dst[tid + 2 * DG_THREADS] = p2;
-        dst[tid + 3 * DG_THREADS] = p3;
+        STRATA_DG_ST(p0, 0)
+        STRATA_DG_ST(p1, 1)
+        STRATA_DG_ST(p2, 2)
+        STRATA_DG_ST(p3, 3)
         if (has4)
-            dst[tid + 4 * DG_THREADS] = p4;
+            STRATA_DG_ST(p4, 4)
         __syncthreads();
-        if (item + 1 < hi)
-            STRATA_DG_FETCH(item + 1)   // in flight while this item is computed
-
-        const int a = item / DG_SLICES, s = item % DG_SLICES;
-        if (a != cache_a) {   // a new expert: its slot range (kept while it lasts)
-            er = expert_of(a, offsets, active, nslot);
-            cache_a = a;
-            slot0 = er.ok && er.ntok > 0 ? slots[er.beg] : -1;
-        }
-        for (int ti = 0; er.ok && ti < er.ntok; ++ti) {
-            const int slot = ti == 0 ? slot0 : slots[er.beg + ti];
+        if (nxt < nitems)
+            STRATA_DG_FETCH(rec_n.x, nxt % DG_SEGS)   // in flight while this item is computed
+        for (int ti = 0; ti < n; ++ti) {
+            if (ti > 0) {
+                slot = slots[rec.y + ti];
+                if (slot >= 0 && slot < nslot)
+                    xo = load_xops(xq, slot / K, s, l);
+            }
             if (slot < 0 || slot >= nslot)
-                continue;   // only a corrupt grouping gets here; uniform per block
-            const int t = slot / K;
-            if (t != d_tok) {   // the token's activation block c, kept across items
-                const uint4 *dsrc = reinterpret_cast<const uint4 *>(
-                    xq.dig + ((size_t)t * XBLK + c) * BLK_DWORDS);
-#pragma unroll
-                for (int i = 0; i < BLK_DWORDS / 4; ++i) {
-                    const uint4 v = dsrc[i];
-                    D[4 * i] = v.x;
-                    D[4 * i + 1] = v.y;
-                    D[4 * i + 2] = v.z;
-                    D[4 * i + 3] = v.w;
-                }
-                sx = xq.scale[(size_t)t * XBLK + c] * xq.inv_rms[t];
-                qs = xq.sum[(size_t)t * XBLK + c];
-                d_tok = t;
-            }
-#pragma unroll
-            for (int pass = 0; pass < DG_ROWS / 8; ++pass) {
-                const int R = pass * 8 + r;
-                uint32_t w[4];
-                float d;
-                lds_block(wlds + R * ROW_G, bc, w, d);
-                const float part = (d * sx) * (float)block_dot64(w, D, qs);
-                const float rs = sum8(part);
-                if ((lane & 7) == 0)
-                    red[wave][R] = rs;
-            }
-            __syncthreads();
-            if (tid < DG_ROWS)
-                gu[tid] = (((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid]) + red[4][tid];
+                continue;   // only a corrupt grouping gets here; uniform per workgroup
+            float acc = block_dot<0>(myrow, xo.d0, xo.sc.x, xo.qs.x);
+            acc += block_dot<1>(myrow + 4, xo.d1, xo.sc.y, xo.qs.y);
+            acc += block_dot<0>(myrow + 9, xo.d2, xo.sc.z, xo.qs.z);
+            acc += block_dot<1>(myrow + 13, xo.d3, xo.sc.w, xo.qs.w);
+            acc += __shfl_xor(acc, 32, 64);   // the wave's two column streams
+            if (lane < DG_ROWS)
+                part[wave][lane] = acc;
             __syncthreads();
             if (wave == 0) {
-                // lanes 0..15: h_j = silu(g_j) * u_j for j = 16 s + lane
-                const int j = lane & 15;
-                const float g = gu[j], u = gu[DG_SLICE + j];
-                const float h = lane < 16 ? g / (1.f + expf(-g)) * u : 0.f;
+                const int j = lane & 31;
+                const float v = (((part[0][j] + part[1][j]) + part[2][j]) + part[3][j]) + part[4][j];
+                const float u = __shfl(v, (lane & 15) + DG_SEG, 64);
+                const float h = lane < DG_SEG ? v / (1.f + expf(-v)) * u : 0.f;
                 const QuantOut qo = quant_lanes<false>(h);
-                const size_t seg = (size_t)slot * HSEG16 + s;
-                if (lane == 12 || lane == 13) {
-                    uint32_t *o = hq.dig + seg * SEG16_DWORDS + (lane - 12) * 4;
-                    o[0] = qo.pk[0];
-                    o[1] = qo.pk[1];
-                    o[2] = qo.pk[2];
-                    o[3] = qo.pk[3];
-                }
+                if (lane == 12 || lane == 13)
+                    store_quarter(hq.dig + ((size_t)slot * HBLK + (seg >> 2)) * BLK_DWORDS, seg & 3,
+                                  lane - 12, qo.pk);
                 if (lane == 0) {
-                    hq.scale[seg] = qo.scale;
-                    hq.sum[seg] = qo.sum;
+                    hq.scale[(size_t)slot * HSEG16 + seg] = qo.scale;
+                    hq.sum[(size_t)slot * HSEG16 + seg] = qo.sum;
                 }
             }
+            __syncthreads();
         }
+        rec = rec_n;
     }
+#undef STRATA_DG_ST
 #undef STRATA_DG_FETCH
 #undef STRATA_DG_LD
 }
 
-constexpr int DD_THREADS = 320;
-constexpr int DD_ROWS = 32;
-constexpr int DD_CHUNKS_PER_E = H / DD_ROWS;       // 80
-constexpr int DD_BYTES = DD_ROWS * ROW_D;          // 5,760
-constexpr int DD_CH16 = DD_BYTES / 16;             // 360
-constexpr int DD_LOADS = 2;
+// ----------------------------------------------------------------------- down
+constexpr int DD_WAVES = 4;                         // items per workgroup
+constexpr int DD_ROWS = 32;                         // output rows per item
+constexpr int DD_ITEMS_PER_E = H / DD_ROWS;         // 80
+constexpr int DD_CHUNKS = DD_ROWS * ROW_D / 16;     // 360 16-byte chunks per item
+constexpr int DD_RS = ROW_D / 4;                    // 45 dwords per row (odd: no bank conflicts)
+static_assert(DD_CHUNKS > 5 * 64 && DD_CHUNKS <= 6 * 64, "six loads per lane");
 
-__global__ __launch_bounds__(DD_THREADS) void dec_down(
-    const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ slots, const int32_t *__restrict__ active, HQ hq,
-    float *__restrict__ out, int T)
+// Operands of one slot's h for lane column set c0 = r / 2 (block columns
+// 2 j + c0): per column the digit pair, and in lane l of each row the scale
+// and sum of segment 4 (2 j + c0) + k for index 4 j + k = 16 m + l (m = 0, 1).
+struct HOps {
+    uint2 d[5];
+    float sh0, sh1;
+    int qs0, qs1;
+};
+
+__device__ inline HOps load_hops(const HQ &hq, int slot, int c0, int l)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t wlds[DD_BYTES];
-    __shared__ float red[DD_ROWS][NB_D + 1];
-
-    const int nslot = T * K;
-    const int na = min(max(active[0], 0), min(nslot, E));
-    int lo, hi;
-    item_range(na * DD_CHUNKS_PER_E, blockIdx.x, gridDim.x, lo, hi);
-    if (lo >= hi)
-        return;
-    const int tid = threadIdx.x;
-    const int r = tid / NB_D, c = tid % NB_D;
-    const BlockCol bc = block_col(c);
-
-    static_assert(DD_LOADS == 2 && DD_CH16 > DD_THREADS, "two loads per thread");
-    uint4 p0, p1 = make_uint4(0, 0, 0, 0);
-    const bool has1 = tid + DD_THREADS < DD_CH16;
-#define STRATA_DD_FETCH(ITEM)                                                                      \
-    {                                                                                              \
-        const int a_ = (ITEM) / DD_CHUNKS_PER_E, ch_ = (ITEM) % DD_CHUNKS_PER_E;                   \
-        int e_ = active[1 + a_];                                                                   \
-        e_ = (e_ < 0 || e_ >= E) ? 0 : e_;                                                         \
-        const uint4 *src_ = reinterpret_cast<const uint4 *>(                                       \
-            blobs + (size_t)e_ * BLOB + 2 * MAT + (size_t)ch_ * DD_ROWS * ROW_D);                 \
-        p0 = src_[tid];                                                                            \
-        if (has1)                                                                                  \
-            p1 = src_[tid + DD_THREADS];                                                           \
-    }
-    int cache_a = -1, slot0 = -1, d_slot = -1;
-    ExpertRange er{0, 0, 0, 0};
-    uint32_t D[BLK_DWORDS];
-    float sh[4] = {0.f, 0.f, 0.f, 0.f};
-    int qs[4] = {0, 0, 0, 0};
-    STRATA_DD_FETCH(lo)
-    for (int item = lo; item < hi; ++item) {
-        __syncthreads();
-        uint4 *dst = reinterpret_cast<uint4 *>(wlds);
-        dst[tid] = p0;
-        if (has1)
-            dst[tid + DD_THREADS] = p1;
-        __syncthreads();
-        if (item + 1 < hi)
-            STRATA_DD_FETCH(item + 1)
-
-        const int a = item / DD_CHUNKS_PER_E, ch = item % DD_CHUNKS_PER_E;
-        if (a != cache_a) {
-            er = expert_of(a, offsets, active, nslot);
-            cache_a = a;
-            slot0 = er.ok && er.ntok > 0 ? slots[er.beg] : -1;
-        }
-        for (int ti = 0; er.ok && ti < er.ntok; ++ti) {
-            const int slot = ti == 0 ? slot0 : slots[er.beg + ti];
-            if (slot < 0 || slot >= nslot)
-                continue;
-            if (slot != d_slot) {   // the slot's h block c, kept across items
-                const size_t seg0 = (size_t)slot * HSEG16 + 4 * c;
-                const uint4 *dsrc = reinterpret_cast<const uint4 *>(hq.dig + seg0 * SEG16_DWORDS);
+    HOps o;
+    const uint2 *dp =
+        reinterpret_cast<const uint2 *>(hq.dig + (size_t)slot * HBLK * BLK_DWORDS) + l;
 #pragma unroll
-                for (int i = 0; i < BLK_DWORDS / 4; ++i) {
-                    const uint4 v = dsrc[i];
-                    D[4 * i] = v.x;
-                    D[4 * i + 1] = v.y;
-                    D[4 * i + 2] = v.z;
-                    D[4 * i + 3] = v.w;
-                }
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    sh[k] = hq.scale[seg0 + k];
-                    qs[k] = hq.sum[seg0 + k];
-                }
-                d_slot = slot;
-            }
-            uint32_t w[4];
-            float d;
-            lds_block(wlds + r * ROW_D, bc, w, d);
-            red[r][c] = d * block_dot16x4(w, D, sh, qs);
-            __syncthreads();
-            if (tid < DD_ROWS) {
-                float acc = 0.f;
-#pragma unroll
-                for (int cc = 0; cc < NB_D; ++cc)
-                    acc += red[tid][cc];
-                out[(size_t)slot * H + ch * DD_ROWS + tid] = acc;
-            }
-            __syncthreads();
-        }
-    }
-#undef STRATA_DD_FETCH
+    for (int j = 0; j < 5; ++j)
+        o.d[j] = dp[16 * (2 * j + c0)];
+    const int seg0 = 4 * (2 * (l >> 2) + c0) + (l & 3);   // index l: j = l / 4, k = l % 4
+    const int seg1 = 4 * (2 * 4 + c0) + (l & 3);          // index 16 + l (l < 4): j = 4
+    const size_t sb = (size_t)slot * HSEG16;
+    o.sh0 = hq.scale[sb + seg0];
+    o.qs0 = hq.sum[sb + seg0];
+    o.sh1 = l < 4 ? hq.scale[sb + seg1] : 0.f;
+    o.qs1 = l < 4 ? hq.sum[sb + seg1] : 0;
+    return o;
 }
 
-hipError_t launch_decode_experts(const uint8_t *blobs, const int32_t *offsets,
-                                 const int32_t *slots, const int32_t *active, XQ xq, HQ hq,
-                                 float *out, int T, int n_cu, hipStream_t st)
+// ACC += (SH of lane N of the row) * V
+#define STRATA_FMA_BCAST(ACC, SH, V, N)                                                            \
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"                    \
+        : "+v"(ACC)                                                                                \
+        : "v"(SH), "v"(V), "i"(N))
+
+// One 16-value segment of a down block: code dword W against digit register D
+// (quarter parity KH), scaled by the segment's scale at broadcast index N.
+#define STRATA_DOWN_SEG(W, D, KH, SHR, QSR, N)                                                     \
+    {                                                                                              \
+        int a0_ = -__builtin_amdgcn_update_dpp(0, QSR, 0x150 + (N), 0xf, 0xf, false);             \
+        int a1_ = 0, a2_ = 0, a3_ = 0;                                                             \
+        if (KH)                                                                                    \
+            STRATA_QUARTER_ODD(W, D, a0_, a1_, a2_, a3_)                                           \
+        else                                                                                       \
+            STRATA_QUARTER_EVEN(W, D, a0_, a1_, a2_, a3_)                                          \
+        const float f_ = (float)digits_combine(a0_, a1_, a2_, a3_);                                \
+        STRATA_FMA_BCAST(bacc, SHR, f_, N);                                                        \
+    }
+
+// One down block from the 5 dwords at p: sel and sh place the codes and the
+// scale (they depend on the block column parity, which is fixed per lane).
+template <int N0, int N1, int N2, int N3>
+__device__ inline float down_block(const uint32_t *p, uint32_t sel, uint32_t sh, uint2 D, float shr,
+                                   int qsr)
+{
+    const uint32_t v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3], v4 = p[4];
+    const uint32_t w0 = __builtin_amdgcn_perm(v1, v0, sel);
+    const uint32_t w1 = __builtin_amdgcn_perm(v2, v1, sel);
+    const uint32_t w2 = __builtin_amdgcn_perm(v3, v2, sel);
+    const uint32_t w3 = __builtin_amdgcn_perm(v4, v3, sel);
+    const float d = half_bits_to_float(v0 >> sh);
+    float bacc = 0.f;
+    STRATA_DOWN_SEG(w0, D.x, 0, shr, qsr, N0)
+    STRATA_DOWN_SEG(w1, D.x, 1, shr, qsr, N1)
+    STRATA_DOWN_SEG(w2, D.y, 0, shr, qsr, N2)
+    STRATA_DOWN_SEG(w3, D.y, 1, shr, qsr, N3)
+    return d * bacc;
+}
+
+// The five blocks 2 j + c0 of a row; their windows start at dwords 9 j (an
+// odd column's window starts 2 bytes before its scale).
+__device__ inline float down_row(const uint32_t *row, int c0, const HOps &ho)
+{
+    const uint32_t sel = c0 ? 0x07060504u : 0x05040302u;
+    const uint32_t sh = c0 ? 16u : 0u;
+    float acc = down_block<0, 1, 2, 3>(row, sel, sh, ho.d[0], ho.sh0, ho.qs0);
+    acc += down_block<4, 5, 6, 7>(row + 9, sel, sh, ho.d[1], ho.sh0, ho.qs0);
+    acc += down_block<8, 9, 10, 11>(row + 18, sel, sh, ho.d[2], ho.sh0, ho.qs0);
+    acc += down_block<12, 13, 14, 15>(row + 27, sel, sh, ho.d[3], ho.sh0, ho.qs0);
+    acc += down_block<0, 1, 2, 3>(row + 36, sel, sh, ho.d[4], ho.sh1, ho.qs1);
+    return acc;
+}
+
+__global__ __launch_bounds__(64 * DD_WAVES) void dec_down(const uint8_t *__restrict__ blobs,
+                                                         const int4 *__restrict__ erec,
+                                                         const int32_t *__restrict__ slots, HQ hq,
+                                                         float *__restrict__ out, int T)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t wl[DD_WAVES][DD_ROWS * DD_RS];
+
+    const int nslot = T * K;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int item = blockIdx.x * DD_WAVES + wave;
+    if (item >= active_count(erec, T) * DD_ITEMS_PER_E)
+        return;
+    const int r = lane >> 4, l = lane & 15;
+    const int c0 = r >> 1;
+    const int4 rec = erec[1 + item / DD_ITEMS_PER_E];
+    const int ch = item % DD_ITEMS_PER_E;
+    int slot = rec.w;
+    HOps ho = load_hops(hq, slot >= 0 && slot < nslot ? slot : 0, c0, l);
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(blobs + (size_t)rec.x * BLOB + 2 * MAT +
+                                                           (size_t)ch * DD_ROWS * ROW_D);
+        uint4 *dst = reinterpret_cast<uint4 *>(wl[wave]);
+        const bool has5 = lane + 320 < DD_CHUNKS;
+        const uint4 v0 = src[lane], v1 = src[lane + 64], v2 = src[lane + 128];
+        const uint4 v3 = src[lane + 192], v4 = src[lane + 256];
+        const uint4 v5 = has5 ? src[lane + 320] : make_uint4(0, 0, 0, 0);
+        dst[lane] = v0;
+        dst[lane + 64] = v1;
+        dst[lane + 128] = v2;
+        dst[lane + 192] = v3;
+        dst[lane + 256] = v4;
+        if (has5)
+            dst[lane + 320] = v5;
+    }
+    // the wave reads back what its own lanes wrote: LDS keeps a wave's order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t *row = wl[wave] + ((r & 1) * 16 + l) * DD_RS + 4 * c0;
+    for (int ti = 0; ti < rec.z; ++ti) {
+        if (ti > 0) {
+            slot = slots[rec.y + ti];
+            if (slot >= 0 && slot < nslot)
+                ho = load_hops(hq, slot, c0, l);
+        }
+        if (slot < 0 || slot >= nslot)
+            continue;   // only a corrupt grouping gets here; uniform per wave
+        float acc = down_row(row, c0, ho);
+        acc += __shfl_xor(acc, 32, 64);
+        if (lane < DD_ROWS)
+            out[(size_t)slot * H + ch * DD_ROWS + lane] = acc;
+    }
+}
+
+hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
+                                 XQ xq, HQ hq, float *out, int T, int n_cu, hipStream_t st)
 {
     const int amax = T * K < E ? T * K : E;
-    const int g1 = min(amax * DG_SLICES, 3 * n_cu);
-    const int g2 = min(amax * DD_CHUNKS_PER_E, 4 * n_cu);
-    hipLaunchKernelGGL(dec_gateup, dim3(g1), dim3(DG_THREADS), 0, st, blobs, offsets, slots,
-                       active, xq, hq, T);
-    hipLaunchKernelGGL(dec_down, dim3(g2), dim3(DD_THREADS), 0, st, blobs, offsets, slots, active,
-                       hq, out, T);
+    const int g1 = min(amax * DG_SEGS, 5 * n_cu);
+    const int g2 = (amax * DD_ITEMS_PER_E + DD_WAVES - 1) / DD_WAVES;
+    hipLaunchKernelGGL(dec_gateup, dim3(g1), dim3(DG_THREADS), 0, st, blobs, erec, slots, xq, hq,
+                       T);
+    hipLaunchKernelGGL(dec_down, dim3(g2), dim3(64 * DD_WAVES), 0, st, blobs, erec, slots, hq, out,
+                       T);
     return hipGetLastError();
 }
 

@@ -13,7 +13,12 @@
 // of (code - 1) * q = that - sum q removes the code offset of the Q2_0 table
 // {0,1,2,3} -> {-1,0,1,2} ("Strata in the source...", section "The CPU kernels").
 //
-// Layout of one quantised block of 64 values: 32 dwords [quarter k][par][i].
+// Layout of one quantised block of 64 values (32 dwords).  Logical dword
+// j = 8k + 4 par + i (quarter k, parity par, digit i) is stored at position
+// 2 (j mod 16) + j / 16: lane l of a 16-lane row loads the pair (j = l,
+// j = 16 + l) with one 8-byte load, and the decode kernels hand dword j to all
+// 16 lanes of the row with a DPP row broadcast (row_newbcast) folded into the
+// v_dot8 itself, so the activations never pass through scalar registers or LDS.
 #pragma once
 #include "common.hpp"
 
@@ -23,7 +28,10 @@ constexpr int QMAX = 30000;
 constexpr int XBLK = H / QK;          // 40 activation blocks per token
 constexpr int BLK_DWORDS = 32;        // 64 values x 4 digits x 4 bits
 constexpr int HSEG16 = FF / 16;       // 40 h segments of 16 per slot
-constexpr int SEG16_DWORDS = 8;
+constexpr int HBLK = FF / QK;         // 10 h blocks of 64 per slot
+
+// Storage position of logical dword j of a quantised block.
+__host__ __device__ constexpr int dig_pos(int j) { return 2 * (j & 15) + (j >> 4); }
 
 // Quantised activations of the decode path.
 struct XQ {
@@ -32,8 +40,10 @@ struct XQ {
     int32_t *sum;      // [T][XBLK]
     float *inv_rms;    // [T]            1 / sqrt(mean(x^2) + 1e-6), or 1 without RMSNorm
 };
+// h per 16 values; the digits of four consecutive segments form one 64-value
+// block in the layout above, so dig is [T*K][HBLK][32].
 struct HQ {
-    uint32_t *dig;     // [T*K][HSEG16][8]
+    uint32_t *dig;     // [T*K][HBLK][32]
     float *scale;      // [T*K][HSEG16]
     int32_t *sum;      // [T*K][HSEG16]
 };
@@ -84,20 +94,13 @@ template <bool WHOLE_WAVE> __device__ inline QuantOut quant_lanes(float v)
     return o;
 }
 
-// sum over one quarter (16 codes in w) of code * q, digits D[par][i].
-__device__ inline void quarter_dot(uint32_t w, const uint32_t *D, int &a0, int &a1, int &a2,
-                                   int &a3)
+// Store the packed digits of quarter k (0..3) of a block at blk (32 dwords):
+// called by lanes 12 (par 0) and 13 (par 1) of a row.
+__device__ inline void store_quarter(uint32_t *blk, int k, int par, const uint32_t pk[4])
 {
-    const int e0 = (int)(w & 0x33333333u);
-    const int e1 = (int)((w >> 2) & 0x33333333u);
-    a0 = __builtin_amdgcn_sdot8(e0, (int)D[0], a0, false);
-    a1 = __builtin_amdgcn_sdot8(e0, (int)D[1], a1, false);
-    a2 = __builtin_amdgcn_sdot8(e0, (int)D[2], a2, false);
-    a3 = __builtin_amdgcn_sdot8(e0, (int)D[3], a3, false);
-    a0 = __builtin_amdgcn_sdot8(e1, (int)D[4], a0, false);
-    a1 = __builtin_amdgcn_sdot8(e1, (int)D[5], a1, false);
-    a2 = __builtin_amdgcn_sdot8(e1, (int)D[6], a2, false);
-    a3 = __builtin_amdgcn_sdot8(e1, (int)D[7], a3, false);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        blk[dig_pos(8 * k + 4 * par + i)] = pk[i];
 }
 
 __device__ inline int digits_combine(int a0, int a1, int a2, int a3)
@@ -105,61 +108,31 @@ __device__ inline int digits_combine(int a0, int a1, int a2, int a3)
     return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
 }
 
-// sum over a whole 64-block of (code - 1) * q with one scale for the block.
-__device__ inline int block_dot64(const uint32_t w[4], const uint32_t D[32], int qsum)
-{
-    int a0 = -qsum, a1 = 0, a2 = 0, a3 = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        quarter_dot(w[k], D + 8 * k, a0, a1, a2, a3);
-    return digits_combine(a0, a1, a2, a3);
-}
+// acc += dot8(dword N of the row's broadcast register D, E): v_dot8c with the
+// activation operand taken by row_newbcast:N from lane N of each 16-lane row.
+#define STRATA_DOT8_BCAST(ACC, D, E, N)                                                            \
+    asm("v_dot8c_i32_i4_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"                 \
+        : "+v"(ACC)                                                                                \
+        : "v"(D), "v"(E), "i"(N))
 
-// The same block against four 16-value segments with their own scales:
-// returns sum_k s_k * sum_quarter_k (code - 1) * q in fp32.
-__device__ inline float block_dot16x4(const uint32_t w[4], const uint32_t D[32], const float s[4],
-                                      const int qsum[4])
-{
-    float acc = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        int a0 = -qsum[k], a1 = 0, a2 = 0, a3 = 0;
-        quarter_dot(w[k], D + 8 * k, a0, a1, a2, a3);
-        acc = fmaf(s[k], (float)digits_combine(a0, a1, a2, a3), acc);
+// Sum over quarter k of a block of code * q, for the code dword W and the
+// row-broadcast digit register D that holds logical dwords 16 (k / 2) ..
+// 16 (k / 2) + 15: quarters with k even use broadcast lanes 0..7, k odd 8..15.
+#define STRATA_QUARTER_BODY(W, D, A0, A1, A2, A3, N0, N1, N2, N3, N4, N5, N6, N7)                 \
+    {                                                                                              \
+        const int e0_ = (int)((W) & 0x33333333u), e1_ = (int)(((W) >> 2) & 0x33333333u);          \
+        STRATA_DOT8_BCAST(A0, D, e0_, N0);                                                         \
+        STRATA_DOT8_BCAST(A1, D, e0_, N1);                                                         \
+        STRATA_DOT8_BCAST(A2, D, e0_, N2);                                                         \
+        STRATA_DOT8_BCAST(A3, D, e0_, N3);                                                         \
+        STRATA_DOT8_BCAST(A0, D, e1_, N4);                                                         \
+        STRATA_DOT8_BCAST(A1, D, e1_, N5);                                                         \
+        STRATA_DOT8_BCAST(A2, D, e1_, N6);                                                         \
+        STRATA_DOT8_BCAST(A3, D, e1_, N7);                                                         \
     }
-    return acc;
-}
-
-// Per-lane constants to read block column c of a row staged in LDS: the 5
-// dwords at byte offset st = 18c - 2(c & 1) (4-aligned) hold the whole block;
-// for even c the scale is their bytes 0-1 and the codes bytes 2..17, for odd c
-// the scale is bytes 2-3 and the codes bytes 4..19.
-struct BlockCol {
-    int st;         // byte offset of the 5-dword window within the row
-    uint32_t sel;   // v_perm selector assembling a code dword from 2 window dwords
-    uint32_t sh;    // bit offset of the scale inside window dword 0
-};
-
-__device__ inline BlockCol block_col(int c)
-{
-    BlockCol b;
-    const int odd = c & 1;
-    b.st = 18 * c - 2 * odd;
-    b.sel = odd ? 0x07060504u : 0x05040302u;
-    b.sh = odd ? 16u : 0u;
-    return b;
-}
-
-// Read one block from an LDS row: the four code dwords and the fp32 scale.
-__device__ inline void lds_block(const uint8_t *row, const BlockCol &bc, uint32_t w[4], float &d)
-{
-    const uint32_t *p = reinterpret_cast<const uint32_t *>(row + bc.st);
-    const uint32_t v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3], v4 = p[4];
-    w[0] = __builtin_amdgcn_perm(v1, v0, bc.sel);
-    w[1] = __builtin_amdgcn_perm(v2, v1, bc.sel);
-    w[2] = __builtin_amdgcn_perm(v3, v2, bc.sel);
-    w[3] = __builtin_amdgcn_perm(v4, v3, bc.sel);
-    d = half_bits_to_float(__builtin_amdgcn_ubfe(v0, bc.sh, 16));
-}
+#define STRATA_QUARTER_EVEN(W, D, A0, A1, A2, A3)                                                  \
+    STRATA_QUARTER_BODY(W, D, A0, A1, A2, A3, 0, 1, 2, 3, 4, 5, 6, 7)
+#define STRATA_QUARTER_ODD(W, D, A0, A1, A2, A3)                                                   \
+    STRATA_QUARTER_BODY(W, D, A0, A1, A2, A3, 8, 9, 10, 11, 12, 13, 14, 15)
 
 } // namespace strata

@@ -25,14 +25,48 @@ constexpr int RG_THREADS = 128;
 constexpr int RG_WAVES = RG_THREADS / 64;
 constexpr int RG_BLOCKS = E / RG_WAVES;   // 256
 
+// Work records of the decode expert kernels from a grouping (offsets, slots,
+// active) that the caller supplies: erec[0] = {na, 0, 0, 0} and, for active
+// expert a, erec[1 + a] = {e, beg, n, first slot}, every field clamped into
+// range (an expert id outside 0..E-1 or a first slot outside 0..T*K-1 gives an
+// empty record).
+struct GroupIn {
+    const int32_t *offsets, *slots, *active;
+    int4 *erec;
+};
+
+__device__ inline void build_records(const GroupIn &gi, int T, int tid0, int nthreads)
+{
+    const int nslot = T * K;
+    const int na = min(max(gi.active[0], 0), min(nslot, E));
+    for (int i = tid0; i <= na; i += nthreads) {
+        if (i == 0) {
+            gi.erec[0] = make_int4(na, 0, 0, 0);
+            continue;
+        }
+        const int e = gi.active[i];
+        int4 r = make_int4(0, 0, 0, -1);
+        if (e >= 0 && e < E) {
+            const int beg = min(max(gi.offsets[e], 0), nslot);
+            const int n = min(max(gi.offsets[e + 1], beg), nslot) - beg;
+            const int s0 = n > 0 ? gi.slots[beg] : -1;
+            if (s0 >= 0 && s0 < nslot)
+                r = make_int4(e, beg, n, s0);
+        }
+        gi.erec[i] = r;
+    }
+}
+
 template <bool GEMV, bool PREP>
 __global__ __launch_bounds__(RG_THREADS) void rdec_gemv(const float *__restrict__ x, int T,
                                                         const uint16_t *__restrict__ R,
                                                         float *__restrict__ lraw, XQ xq,
-                                                        int rmsnorm)
+                                                        int rmsnorm, GroupIn gi)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int g = blockIdx.x * RG_WAVES + wave;   // global wave id 0..511
+    if (gi.erec)
+        build_records(gi, T, g * 64 + lane, gridDim.x * RG_THREADS);
     if (GEMV) {
         const int e = g;
         const uint4 *row = reinterpret_cast<const uint4 *>(R + (size_t)e * H);
@@ -98,13 +132,8 @@ __global__ __launch_bounds__(RG_THREADS) void rdec_gemv(const float *__restrict_
             const float v = x[(size_t)t * H + b * QK + lane];
             const QuantOut qo = quant_lanes<true>(v);
             const int l16 = lane & 15;
-            if (l16 == 12 || l16 == 13) {
-                uint32_t *o = xq.dig + (size_t)p * BLK_DWORDS + (lane >> 4) * 8 + (l16 - 12) * 4;
-                o[0] = qo.pk[0];
-                o[1] = qo.pk[1];
-                o[2] = qo.pk[2];
-                o[3] = qo.pk[3];
-            }
+            if (l16 == 12 || l16 == 13)
+                store_quarter(xq.dig + (size_t)p * BLK_DWORDS, lane >> 4, l16 - 12, qo.pk);
             if (lane == 0) {
                 xq.scale[p] = qo.scale;
                 xq.sum[p] = qo.sum;
@@ -124,12 +153,14 @@ __device__ inline bool ranks_before(float p, int e, float q, int f)
 __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
     const float *__restrict__ lraw, const float *__restrict__ inv_rms, const float *__restrict__ bias,
     int T, int32_t *__restrict__ ids, float *__restrict__ wout, int group,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ slots, int32_t *__restrict__ active)
+    int32_t *__restrict__ offsets, int32_t *__restrict__ slots, int32_t *__restrict__ active,
+    int4 *__restrict__ erec)
 {
     constexpr int NW_SLOT = (DECODE_T_MAX * K + 63) / 64;   // waves holding slots (3)
     __shared__ int sid[NW_SLOT * 64];
     __shared__ int cntw[NW_SLOT][E];
     __shared__ int offl[E];
+    __shared__ int first[E];
     __shared__ int wsum[8];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = T * K;
@@ -274,14 +305,19 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
             wsum[wave] = finc;
     }
     __syncthreads();
+    int my_a = -1;
     if (tid < E) {
         int base = 0;
         for (int w = 0; w < wave; ++w)
             base += wsum[w];
-        if (f)
-            active[1 + base + finc - 1] = tid;
-        if (tid == E - 1)
+        if (f) {
+            my_a = base + finc - 1;
+            active[1 + my_a] = tid;
+        }
+        if (tid == E - 1) {
             active[0] = base + finc;
+            erec[0] = make_int4(base + finc, 0, 0, 0);
+        }
     }
     if (wave < NW_SLOT) {
         unsigned long long same = __ballot(my_e >= 0);
@@ -295,31 +331,41 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
             for (int w = 0; w < wave; ++w)
                 rank += cntw[w][my_e];
             slots[offl[my_e] + rank] = tid;
+            if (rank == 0)
+                first[my_e] = tid;
         }
     }
+    __syncthreads();
+    // work record of each active expert: {e, first grouped slot, count, first slot}
+    if (my_a >= 0)
+        erec[1 + my_a] = make_int4(tid, off, c, first[tid]);
 }
 
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
                                int rmsnorm, float *lraw, XQ xq, bool prep, int32_t *ids,
                                float *w, int group, int32_t *offsets, int32_t *slots,
-                               int32_t *active, hipStream_t st)
+                               int32_t *active, int4 *erec, hipStream_t st)
 {
+    const GroupIn none{nullptr, nullptr, nullptr, nullptr};
     if (prep)
         hipLaunchKernelGGL((rdec_gemv<true, true>), dim3(RG_BLOCKS), dim3(RG_THREADS), 0, st, x,
-                           T, R, lraw, xq, rmsnorm);
+                           T, R, lraw, xq, rmsnorm, none);
     else
         hipLaunchKernelGGL((rdec_gemv<true, false>), dim3(RG_BLOCKS), dim3(RG_THREADS), 0, st, x,
-                           T, R, lraw, xq, rmsnorm);
+                           T, R, lraw, xq, rmsnorm, none);
     hipLaunchKernelGGL(rdec_topk, dim3(1), dim3(RT_THREADS), 0, st, lraw, xq.inv_rms, bias, T, ids,
-                       w, group, offsets, slots, active);
+                       w, group, offsets, slots, active, erec);
     return hipGetLastError();
 }
 
-hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, hipStream_t st)
+hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const int32_t *offsets,
+                              const int32_t *slots, const int32_t *active, int4 *erec,
+                              hipStream_t st)
 {
     const int blocks = min(RG_BLOCKS, (T * XBLK + RG_WAVES - 1) / RG_WAVES);
+    const GroupIn gi{offsets, slots, active, erec};
     hipLaunchKernelGGL((rdec_gemv<false, true>), dim3(blocks), dim3(RG_THREADS), 0, st, x, T,
-                       (const uint16_t *)nullptr, (float *)nullptr, xq, rmsnorm);
+                       (const uint16_t *)nullptr, (float *)nullptr, xq, rmsnorm, gi);
     return hipGetLastError();
 }
 
