@@ -118,24 +118,6 @@ __device__ inline float bf16_bits_to_float(uint32_t bits)
     return __uint_as_float((bits & 0xffff) << 16);
 }
 
-// Sum over the 64 lanes of a wave with a fixed butterfly (same tree for every
-// wave, so equal inputs give equal bits).
-__device__ inline float wave_sum(float v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m, 64);
-    return v;
-}
-
-__device__ inline float wave_max(float v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
-
 // ---------------------------------------------------------------- DPP lane exchange
 // dpp_ctrl encodings (GCN/CDNA): quad_perm 0x00-0xFF, row_shr:n 0x110+n,
 // row_mirror 0x140, row_half_mirror 0x141.  Lanes without a source get `old`.
@@ -177,58 +159,65 @@ __device__ inline int isum16(int v)
     v += dpp_i<DPP_HMIRROR>(v);
     return v + dpp_i<DPP_MIRROR>(v);
 }
-// Whole-wave results, uniform in every lane: rows of 16 reduced by DPP, then
-// the four row results combined in a fixed order from lanes 0, 16, 32, 48.
-__device__ inline float wave_sum_dpp(float v)
+// Whole-wave reductions in six DPP steps (quad xor 1, xor 2, half mirror,
+// mirror, then the gfx9 row broadcasts of lanes 15 and 31 into the next rows):
+// lane 63 ends with the result, which v_readlane hands to every lane.  The
+// order of the operations is fixed, so equal inputs give equal bits.
+template <int CTRL, int ROWS> __device__ inline float dppf_rows(float v, float old)
 {
-    v = sum16(v);
-    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (a + b) + (c + d);
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWS, 0xF, false));
 }
-__device__ inline float wave_max_dpp(float v)
+template <int CTRL, int ROWS> __device__ inline int dppi_rows(int v, int old)
 {
-    v = max16(v);
-    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
 }
+constexpr int DPP_BCAST15 = 0x142;
+constexpr int DPP_BCAST31 = 0x143;
 
-// Wave-wide argmax of (p desc, id asc); every lane returns the winner.
-__device__ inline void wave_argmax(float &bp, int &be)
+__device__ inline float wave_sum63(float v)
 {
-    // within rows of 16 (all lanes of a row end with the row's winner)
-#define STRATA_ARGMAX_STEP(CTRL)                                                                   \
-    {                                                                                              \
-        const float op = dpp_f<CTRL>(bp);                                                          \
-        const int oe = dpp_i<CTRL>(be);                                                            \
-        if (op > bp || (op == bp && oe < be)) {                                                    \
-            bp = op;                                                                               \
-            be = oe;                                                                               \
-        }                                                                                          \
-    }
-    STRATA_ARGMAX_STEP(DPP_XOR1)
-    STRATA_ARGMAX_STEP(DPP_XOR2)
-    STRATA_ARGMAX_STEP(DPP_HMIRROR)
-    STRATA_ARGMAX_STEP(DPP_MIRROR)
-#undef STRATA_ARGMAX_STEP
-    float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bp), 0));
-    int id = __builtin_amdgcn_readlane(be, 0);
-#pragma unroll
-    for (int rl = 16; rl < 64; rl += 16) {
-        const float op = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bp), rl));
-        const int oe = __builtin_amdgcn_readlane(be, rl);
-        if (op > p || (op == p && oe < id)) {
-            p = op;
-            id = oe;
-        }
-    }
-    bp = p;
-    be = id;
+    v += dppf_rows<DPP_XOR1, 0xF>(v, 0.f);
+    v += dppf_rows<DPP_XOR2, 0xF>(v, 0.f);
+    v += dppf_rows<DPP_HMIRROR, 0xF>(v, 0.f);
+    v += dppf_rows<DPP_MIRROR, 0xF>(v, 0.f);
+    v += dppf_rows<DPP_BCAST15, 0xA>(v, 0.f);
+    v += dppf_rows<DPP_BCAST31, 0xC>(v, 0.f);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ inline float wave_max63(float v)
+{
+    v = fmaxf(v, dppf_rows<DPP_XOR1, 0xF>(v, v));
+    v = fmaxf(v, dppf_rows<DPP_XOR2, 0xF>(v, v));
+    v = fmaxf(v, dppf_rows<DPP_HMIRROR, 0xF>(v, v));
+    v = fmaxf(v, dppf_rows<DPP_MIRROR, 0xF>(v, v));
+    v = fmaxf(v, dppf_rows<DPP_BCAST15, 0xA>(v, v));
+    v = fmaxf(v, dppf_rows<DPP_BCAST31, 0xC>(v, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ inline int wave_min63(int v)
+{
+    v = min(v, dppi_rows<DPP_XOR1, 0xF>(v, v));
+    v = min(v, dppi_rows<DPP_XOR2, 0xF>(v, v));
+    v = min(v, dppi_rows<DPP_HMIRROR, 0xF>(v, v));
+    v = min(v, dppi_rows<DPP_MIRROR, 0xF>(v, v));
+    v = min(v, dppi_rows<DPP_BCAST15, 0xA>(v, v));
+    v = min(v, dppi_rows<DPP_BCAST31, 0xC>(v, v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+// Inclusive prefix sum over the 64 lanes (row shifts 1, 2, 3, 4, 8, then the
+// row broadcasts), and the exclusive one.
+__device__ inline int wave_incl_scan(int v)
+{
+    const int v0 = v;
+    v += __builtin_amdgcn_update_dpp(0, v0, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v0, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v0, 0x113, 0xF, 0xF, true);   // row_shr:3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xE, false);   // row_shr:4, banks 1-3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xC, false);   // row_shr:8, banks 2-3
+    v += __builtin_amdgcn_update_dpp(0, v, DPP_BCAST15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, DPP_BCAST31, 0xC, 0xF, false);
+    return v;
 }
 
 } // namespace strata

@@ -13,7 +13,8 @@
 //                 k = 0..2559 FMA chain, so identical router rows give
 //                 identical logits.
 //  topk_kernel    one wave per token: softmax in fp32, ten rounds of a
-//                 wave-wide argmax on (p desc, id asc), clamped renorm.
+//                 wave-wide max of p and min of the id among the maxima
+//                 (the order p desc, id asc), clamped renorm.
 #include "common.hpp"
 
 namespace strata {
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     }
     float inv = 1.f;
     if (rmsnorm) {
-        ss = wave_sum(ss);
+        ss = wave_sum63(ss);
         if ((tid & 63) == 0)
             wsum[tid >> 6] = ss;
         __syncthreads();
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 #pragma unroll
     for (int i = 1; i < 8; ++i)
         m = fmaxf(m, l[i]);
-    m = wave_max_dpp(m);
+    m = wave_max63(m);
     float p[8];
     float s = 0.f;
 #pragma unroll
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
         p[i] = expf(l[i] - m);
         s += p[i];
     }
-    s = wave_sum_dpp(s);
+    s = wave_sum63(s);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         p[i] = p[i] / s;
@@ -183,7 +184,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
                 be = e;
             }
         }
-        wave_argmax(bp, be);
+        // the best candidate: the largest p, and among equal p the lowest id
+        const float pm = wave_max63(bp);
+        be = wave_min63(bp == pm ? be : 0x7fffffff);
+        bp = pm;
         if ((be & 63) == lane)
             taken |= 1u << ((be >> 6) & 7);
         if (lane == k) {

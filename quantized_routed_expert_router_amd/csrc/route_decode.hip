@@ -6,24 +6,32 @@
 // descending argsort, the gather of the top 10 and the renormalisation with a
 // lower clamp.
 //
-//  rdec_gemv   256 workgroups x 2 waves, one router row per wave: raw logits
-//              R . x for every token (the RMSNorm factor is a per-token scalar
-//              applied in rdec_topk), plus -- when asked -- the per-token
-//              inverse RMS and the 16-bit quantisation of each 64-value block
-//              of x for the experts (the RMSNorm factor stays out of the
-//              quantisation: it scales the block scale).
+//  rdec_gemv   one workgroup of 5 waves per router row: wave w holds the row's
+//              elements 512 w .. 512 w + 511 (8 per lane), reads x for up to
+//              8 tokens at once and reduces each token's partial dot product
+//              with DPP; the 5 partials meet in LDS in a fixed order.  These
+//              are the raw logits R . x (the RMSNorm factor is a per-token
+//              scalar applied in rdec_topk).  The same launch computes the
+//              per-token inverse RMS and, when asked, the 16-bit quantisation
+//              of each 64-value block of x for the experts (the RMSNorm factor
+//              stays out of the quantisation: it scales the block scale).
 //  rdec_topk   one workgroup: wave t takes token t (softmax with DPP
-//              reductions, ten rounds of a wave-wide argmax on (p desc, id
-//              asc), clamped renorm); then the workgroup groups the T*10 slots
-//              by expert (counts, scan, active list, stable ranks).
+//              reductions, a sorting network on each lane's 8 candidates, then
+//              ten rounds of a wave-wide max of p and min of the id among the
+//              maxima -- the order (p desc, id asc) -- and the clamped renorm).
+//              Wave 0 then groups the T*10 slots by expert: counts, offsets,
+//              the active list, stable slot order and one work record per
+//              active expert for the expert kernels.
 #include "common.hpp"
 #include "quant.hpp"
 
 namespace strata {
 
-constexpr int RG_THREADS = 128;
-constexpr int RG_WAVES = RG_THREADS / 64;
-constexpr int RG_BLOCKS = E / RG_WAVES;   // 256
+constexpr int RG_WAVES = 5;                       // waves per router row
+constexpr int RG_THREADS = 64 * RG_WAVES;
+constexpr int RG_SPAN = H / RG_WAVES;             // 512 elements per wave
+constexpr int RG_TOK = 8;                         // tokens whose x is in flight at once
+static_assert(RG_SPAN == 64 * 8, "8 elements per lane");
 
 // Work records of the decode expert kernels from a grouping (offsets, slots,
 // active) that the caller supplies: erec[0] = {na, 0, 0, 0} and, for active
@@ -63,67 +71,69 @@ __global__ __launch_bounds__(RG_THREADS) void rdec_gemv(const float *__restrict_
                                                         float *__restrict__ lraw, XQ xq,
                                                         int rmsnorm, GroupIn gi)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int g = blockIdx.x * RG_WAVES + wave;   // global wave id 0..511
-    if (gi.erec)
-        build_records(gi, T, g * 64 + lane, gridDim.x * RG_THREADS);
-    if (GEMV) {
-        const int e = g;
-        const uint4 *row = reinterpret_cast<const uint4 *>(R + (size_t)e * H);
-        float rv[40];
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const uint4 q = row[lane + 64 * i];
-            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                rv[8 * i + 2 * j] = bf16_bits_to_float(u[j]);
-                rv[8 * i + 2 * j + 1] = bf16_bits_to_float(u[j] >> 16);
-            }
-        }
-        for (int t = 0; t < T; ++t) {
-            const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)t * H);
-            float4 xa[10];
-#pragma unroll
-            for (int i = 0; i < 5; ++i) {
-                xa[2 * i] = xr[2 * (lane + 64 * i)];
-                xa[2 * i + 1] = xr[2 * (lane + 64 * i) + 1];
-            }
-            float acc = 0.f;
-#pragma unroll
-            for (int i = 0; i < 5; ++i) {
-                acc = fmaf(rv[8 * i + 0], xa[2 * i].x, acc);
-                acc = fmaf(rv[8 * i + 1], xa[2 * i].y, acc);
-                acc = fmaf(rv[8 * i + 2], xa[2 * i].z, acc);
-                acc = fmaf(rv[8 * i + 3], xa[2 * i].w, acc);
-                acc = fmaf(rv[8 * i + 4], xa[2 * i + 1].x, acc);
-                acc = fmaf(rv[8 * i + 5], xa[2 * i + 1].y, acc);
-                acc = fmaf(rv[8 * i + 6], xa[2 * i + 1].z, acc);
-                acc = fmaf(rv[8 * i + 7], xa[2 * i + 1].w, acc);
-            }
-            acc = wave_sum_dpp(acc);
-            if (lane == 0)
-                lraw[(size_t)t * E + e] = acc;
-        }
-    }
+    __shared__ float part[RG_WAVES][DECODE_T_MAX];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int g = blockIdx.x * RG_WAVES + wave;   // global wave id
     const int nw = gridDim.x * RG_WAVES;
-    // inverse RMS of token g (needed by the router and the experts)
-    {
-        for (int t = g; t < T; t += nw) {
-            const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)t * H);
-            float ss = 0.f;
+    if (gi.erec)
+        build_records(gi, T, g * 64 + lane, nw * 64);
+    if (GEMV) {
+        const int e = blockIdx.x;
+        const int k0 = wave * RG_SPAN + 8 * lane;
+        const uint4 q = *reinterpret_cast<const uint4 *>(R + (size_t)e * H + k0);
+        const float r0 = bf16_bits_to_float(q.x), r1 = bf16_bits_to_float(q.x >> 16);
+        const float r2 = bf16_bits_to_float(q.y), r3 = bf16_bits_to_float(q.y >> 16);
+        const float r4 = bf16_bits_to_float(q.z), r5 = bf16_bits_to_float(q.z >> 16);
+        const float r6 = bf16_bits_to_float(q.w), r7 = bf16_bits_to_float(q.w >> 16);
+        for (int t0 = 0; t0 < T; t0 += RG_TOK) {
+            float4 xa[RG_TOK], xb[RG_TOK];
 #pragma unroll
-            for (int i = 0; i < 10; ++i) {
-                const float4 a = xr[lane + 64 * i];
-                ss = fmaf(a.x, a.x, ss);
-                ss = fmaf(a.y, a.y, ss);
-                ss = fmaf(a.z, a.z, ss);
-                ss = fmaf(a.w, a.w, ss);
+            for (int i = 0; i < RG_TOK; ++i) {
+                if (t0 + i < T) {
+                    const float4 *xr =
+                        reinterpret_cast<const float4 *>(x + (size_t)(t0 + i) * H + k0);
+                    xa[i] = xr[0];
+                    xb[i] = xr[1];
+                }
             }
-            ss = wave_sum_dpp(ss);
-            if (lane == 0)
-                xq.inv_rms[t] = rmsnorm ? 1.f / sqrtf(ss / (float)H + 1e-6f) : 1.f;
+#pragma unroll
+            for (int i = 0; i < RG_TOK; ++i) {
+                if (t0 + i < T) {
+                    float acc = r0 * xa[i].x;
+                    acc = fmaf(r1, xa[i].y, acc);
+                    acc = fmaf(r2, xa[i].z, acc);
+                    acc = fmaf(r3, xa[i].w, acc);
+                    acc = fmaf(r4, xb[i].x, acc);
+                    acc = fmaf(r5, xb[i].y, acc);
+                    acc = fmaf(r6, xb[i].z, acc);
+                    acc = fmaf(r7, xb[i].w, acc);
+                    acc = wave_sum63(acc);
+                    if (lane == 0)
+                        part[wave][t0 + i] = acc;
+                }
+            }
         }
+        __syncthreads();
+        if (tid < T)
+            lraw[(size_t)tid * E + e] =
+                (((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid]) + part[4][tid];
+    }
+    // inverse RMS of token g (needed by the router and the experts)
+    for (int t = g; t < T; t += nw) {
+        const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)t * H);
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 10; ++i) {
+            const float4 a = xr[lane + 64 * i];
+            ss = fmaf(a.x, a.x, ss);
+            ss = fmaf(a.y, a.y, ss);
+            ss = fmaf(a.z, a.z, ss);
+            ss = fmaf(a.w, a.w, ss);
+        }
+        ss = wave_sum63(ss);
+        if (lane == 0)
+            xq.inv_rms[t] = rmsnorm ? 1.f / sqrtf(ss / (float)H + 1e-6f) : 1.f;
     }
     if (PREP) {
         // 16-bit quantisation of the 64-value blocks (token, block) = p
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(RG_THREADS) void rdec_gemv(const float *__restrict_
     }
 }
 
-constexpr int RT_THREADS = 1024;
+constexpr int RT_THREADS = 64 * DECODE_T_MAX;     // one wave per token
 
 // (p, e) ranks before (q, f): larger probability, or equal and lower id.
 __device__ inline bool ranks_before(float p, int e, float q, int f)
@@ -156,19 +166,19 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
     int32_t *__restrict__ offsets, int32_t *__restrict__ slots, int32_t *__restrict__ active,
     int4 *__restrict__ erec)
 {
-    constexpr int NW_SLOT = (DECODE_T_MAX * K + 63) / 64;   // waves holding slots (3)
-    __shared__ int sid[NW_SLOT * 64];
-    __shared__ int cntw[NW_SLOT][E];
-    __shared__ int offl[E];
-    __shared__ int first[E];
-    __shared__ int wsum[8];
+    __shared__ int sid[DECODE_T_MAX * K];   // expert of each slot
+    __shared__ int cnt[E];                  // slots per expert
+    __shared__ int cur[E];                  // slots placed so far, per expert
+    __shared__ int first[E];                // first slot of each expert
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = T * K;
-    for (int i = tid; i < NW_SLOT * E; i += RT_THREADS)
-        (&cntw[0][0])[i] = 0;
-    for (int i = tid; i < NW_SLOT * 64; i += RT_THREADS)
-        sid[i] = -1;
-    __syncthreads();
+    if (group) {
+        for (int i = tid; i < E; i += RT_THREADS) {
+            cnt[i] = 0;
+            cur[i] = 0;
+        }
+        __syncthreads();
+    }
     if (wave < T) {
         const int t = wave;
         const float sc = inv_rms[t];
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
 #pragma unroll
         for (int i = 1; i < 8; ++i)
             m = fmaxf(m, l[i]);
-        m = wave_max_dpp(m);
+        m = wave_max63(m);
         float p[8], s = 0.f;
         int e[8];
 #pragma unroll
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
             s += p[i];
             e[i] = lane + 64 * i;
         }
-        s = wave_sum_dpp(s);
+        s = wave_sum63(s);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             p[i] = p[i] / s;
@@ -224,9 +234,9 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
         float my_p = 0.f, sel = 0.f;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            float bp = p[0];
-            int be = e[0];
-            wave_argmax(bp, be);
+            // the best head: the largest p, and among equal p the lowest id
+            const float bp = wave_max63(p[0]);
+            const int be = wave_min63(p[0] == bp ? e[0] : 0x7fffffff);
             const bool pop = e[0] == be;
 #pragma unroll
             for (int i = 0; i < 7; ++i) {
@@ -245,81 +255,48 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
         if (lane < K) {
             ids[(size_t)t * K + lane] = my_id;
             wout[(size_t)t * K + lane] = my_p / den;
-            sid[t * K + lane] = my_id;
+            if (group) {
+                sid[t * K + lane] = my_id;
+                atomicAdd(&cnt[my_id], 1);
+            }
         }
     }
     if (!group)
         return;
     __syncthreads();
-    // Grouping of the N = T*K slots: per-wave counts, scan, active list, and
-    // stable ranks from ballots (equal ids inside a 64-slot wave) plus the
-    // counts of the earlier waves.
-    int my_e = -1;
-    if (wave < NW_SLOT) {
-        my_e = sid[tid];
-        if (my_e >= 0 && my_e < E && tid < N)
-            atomicAdd(&cntw[wave][my_e], 1);
-        else
-            my_e = -1;
-    }
-    __syncthreads();
-    int c = 0, inc = 0;
-    if (tid < E) {
+    if (wave != 0)
+        return;
+    // Wave 0: lane l owns experts 8 l .. 8 l + 7.
+    int c[8], incl = 0, fl = 0;
 #pragma unroll
-        for (int w = 0; w < NW_SLOT; ++w)
-            c += cntw[w][tid];
-        inc = c;
+    for (int j = 0; j < 8; ++j) {
+        c[j] = cnt[8 * lane + j];
+        incl += c[j];
+        fl += c[j] > 0;
+    }
+    const int cbase = wave_incl_scan(incl) - incl;   // slots of the lower experts
+    const int abase = wave_incl_scan(fl) - fl;       // active experts below
+    {
+        int o = cbase, a = abase;
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int o = __shfl_up(inc, d, 64);
-            if (lane >= d)
-                inc += o;
+        for (int j = 0; j < 8; ++j) {
+            const int ex = 8 * lane + j;
+            offsets[ex] = o;
+            cnt[ex] = o;   // from here on: the expert's first grouped slot
+            if (c[j] > 0)
+                active[1 + a++] = ex;
+            o += c[j];
         }
-        if (lane == 63)
-            wsum[wave] = inc;
-    }
-    __syncthreads();
-    int off = 0;
-    if (tid < E) {
-        int base = 0;
-        for (int w = 0; w < wave; ++w)
-            base += wsum[w];
-        off = base + inc - c;
-        offsets[tid] = off;
-        offl[tid] = off;
-        if (tid == E - 1)
-            offsets[E] = base + inc;
-    }
-    __syncthreads();
-    int f = 0, finc = 0;
-    if (tid < E) {
-        f = c > 0;
-        finc = f;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int o = __shfl_up(finc, d, 64);
-            if (lane >= d)
-                finc += o;
-        }
-        if (lane == 63)
-            wsum[wave] = finc;
-    }
-    __syncthreads();
-    int my_a = -1;
-    if (tid < E) {
-        int base = 0;
-        for (int w = 0; w < wave; ++w)
-            base += wsum[w];
-        if (f) {
-            my_a = base + finc - 1;
-            active[1 + my_a] = tid;
-        }
-        if (tid == E - 1) {
-            active[0] = base + finc;
-            erec[0] = make_int4(base + finc, 0, 0, 0);
+        if (lane == 63) {
+            offsets[E] = o;
+            active[0] = a;
+            erec[0] = make_int4(a, 0, 0, 0);
         }
     }
-    if (wave < NW_SLOT) {
+    // Stable placement: slot s goes after the earlier slots of its expert.
+    for (int s0 = 0; s0 < N; s0 += 64) {
+        const int s = s0 + lane;
+        const int my_e = s < N ? sid[s] : -1;
         unsigned long long same = __ballot(my_e >= 0);
 #pragma unroll
         for (int bit = 0; bit < 9; ++bit) {
@@ -327,18 +304,25 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
             same &= ((my_e >> bit) & 1) ? bits : ~bits;
         }
         if (my_e >= 0) {
-            int rank = __popcll(same & ((1ull << lane) - 1ull));
-            for (int w = 0; w < wave; ++w)
-                rank += cntw[w][my_e];
-            slots[offl[my_e] + rank] = tid;
+            const int before = __popcll(same & ((1ull << lane) - 1ull));
+            const int rank = cur[my_e] + before;
+            slots[cnt[my_e] + rank] = s;
             if (rank == 0)
-                first[my_e] = tid;
+                first[my_e] = s;
+            if (before == 0)   // the lowest lane of the group advances the count
+                cur[my_e] += __popcll(same);
         }
     }
-    __syncthreads();
-    // work record of each active expert: {e, first grouped slot, count, first slot}
-    if (my_a >= 0)
-        erec[1 + my_a] = make_int4(tid, off, c, first[tid]);
+    // one work record per active expert: {e, first grouped slot, count, first slot}
+    {
+        int a = abase;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int ex = 8 * lane + j;
+            if (c[j] > 0)
+                erec[1 + a++] = make_int4(ex, cnt[ex], c[j], first[ex]);
+        }
+    }
 }
 
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
@@ -348,11 +332,11 @@ hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const f
 {
     const GroupIn none{nullptr, nullptr, nullptr, nullptr};
     if (prep)
-        hipLaunchKernelGGL((rdec_gemv<true, true>), dim3(RG_BLOCKS), dim3(RG_THREADS), 0, st, x,
-                           T, R, lraw, xq, rmsnorm, none);
+        hipLaunchKernelGGL((rdec_gemv<true, true>), dim3(E), dim3(RG_THREADS), 0, st, x, T, R,
+                           lraw, xq, rmsnorm, none);
     else
-        hipLaunchKernelGGL((rdec_gemv<true, false>), dim3(RG_BLOCKS), dim3(RG_THREADS), 0, st, x,
-                           T, R, lraw, xq, rmsnorm, none);
+        hipLaunchKernelGGL((rdec_gemv<true, false>), dim3(E), dim3(RG_THREADS), 0, st, x, T, R,
+                           lraw, xq, rmsnorm, none);
     hipLaunchKernelGGL(rdec_topk, dim3(1), dim3(RT_THREADS), 0, st, lraw, xq.inv_rms, bias, T, ids,
                        w, group, offsets, slots, active, erec);
     return hipGetLastError();
@@ -362,7 +346,7 @@ hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const i
                               const int32_t *slots, const int32_t *active, int4 *erec,
                               hipStream_t st)
 {
-    const int blocks = min(RG_BLOCKS, (T * XBLK + RG_WAVES - 1) / RG_WAVES);
+    const int blocks = (T * XBLK + RG_WAVES - 1) / RG_WAVES;
     const GroupIn gi{offsets, slots, active, erec};
     hipLaunchKernelGGL((rdec_gemv<false, true>), dim3(blocks), dim3(RG_THREADS), 0, st, x, T,
                        (const uint16_t *)nullptr, (float *)nullptr, xq, rmsnorm, gi);
