@@ -20,8 +20,9 @@
 //              row l of gate (r even) or up (r odd) and block columns
 //              4 s .. 4 s + 3 with s = 2 w + r / 2.  Partial sums meet in a
 //              fixed order; wave 0 forms h = silu(g) * u for the 16 rows and
-//              quantises them as one 16-value segment.  The next item's bytes
-//              are loaded into registers while the current one is computed.
+//              quantises them as one 16-value segment.  Five workgroups per
+//              CU loop over the items; each loads its next item into
+//              registers while the current one is computed.
 //  dec_down    item = (active expert, 32 output rows), one wave: lane (r, l)
 //              takes row 16 (r % 2) + l and block columns 2 j + r / 2; the two
 //              halves of each row are added and the row's value written per
@@ -44,6 +45,7 @@ constexpr int DG_RS = ROW_G / 4 + 1;                // LDS row stride in dwords 
 constexpr int DG_LOADS = (DG_CHUNKS + DG_THREADS - 1) / DG_THREADS;   // 5
 static_assert(DG_LOADS == 5 && DG_CHUNKS > 4 * DG_THREADS, "five loads per thread");
 static_assert(5 * 2 * 4 == NB_G, "5 waves x 2 column streams x 4 block columns");
+constexpr int DG_PER_CU = 5;                        // resident workgroups per CU (23 KB of LDS each)
 
 // Records of the grouping for the decode kernels: erec[0].x = number of active
 // experts, erec[1 + a] = {expert, first grouped slot, token count, first slot}.
@@ -52,13 +54,14 @@ __device__ inline int active_count(const int4 *erec, int T)
     return min(max(erec[0].x, 0), min(T * K, E));
 }
 
-// Activation operands of one token for lane column stream s: per block column
-// 4 s + j the pair (dword l, dword 16 + l), the block scale times the inverse
-// RMS, and the sum of q.
+// Activation operands of one token for lane column stream s (block columns
+// 4 s + j): the digit pairs (dword l, dword 16 + l) of each column, and in
+// lane j < 4 of each 16-lane row the column's scale times the inverse RMS
+// and its -sum q (handed to the row by DPP broadcast).
 struct XOps {
     uint2 d0, d1, d2, d3;
-    float4 sc;
-    int4 qs;
+    float sc;
+    int nq;
 };
 
 __device__ inline XOps load_xops(const XQ &xq, int t, int s, int l)
@@ -70,31 +73,25 @@ __device__ inline XOps load_xops(const XQ &xq, int t, int s, int l)
     o.d1 = dp[16];
     o.d2 = dp[32];
     o.d3 = dp[48];
-    const float r = xq.inv_rms[t];
-    const float4 sc = *reinterpret_cast<const float4 *>(xq.scale + xb);
-    o.sc = make_float4(sc.x * r, sc.y * r, sc.z * r, sc.w * r);
-    o.qs = *reinterpret_cast<const int4 *>(xq.sum + xb);
+    const int j = l & 3;
+    o.sc = xq.scale[xb + j] * xq.inv_rms[t];
+    o.nq = xq.nsum[xb + j];
     return o;
 }
 
 // One block of a row held in LDS: the 5 dwords from p hold it; ODD (block
-// column parity) says where the scale and the codes sit in them.
-template <int ODD>
-__device__ inline float block_dot(const uint32_t *p, uint2 D, float sx, int qs)
+// column parity) says where the scale and the codes sit in them; J is the
+// block's index among the lane's four columns.
+template <int ODD, int J>
+__device__ inline float block_dot(const uint32_t *p, uint2 D, const XOps &xo)
 {
     const uint32_t v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3], v4 = p[4];
     constexpr uint32_t sel = ODD ? 0x07060504u : 0x05040302u;
-    const uint32_t w0 = __builtin_amdgcn_perm(v1, v0, sel);
-    const uint32_t w1 = __builtin_amdgcn_perm(v2, v1, sel);
-    const uint32_t w2 = __builtin_amdgcn_perm(v3, v2, sel);
-    const uint32_t w3 = __builtin_amdgcn_perm(v4, v3, sel);
+    const Codes c = split_codes(__builtin_amdgcn_perm(v1, v0, sel), __builtin_amdgcn_perm(v2, v1, sel),
+                                __builtin_amdgcn_perm(v3, v2, sel), __builtin_amdgcn_perm(v4, v3, sel));
     const float d = half_bits_to_float(ODD ? (v0 >> 16) : v0);
-    int a0 = -qs, a1 = 0, a2 = 0, a3 = 0;
-    STRATA_QUARTER_EVEN(w0, D.x, a0, a1, a2, a3)
-    STRATA_QUARTER_ODD(w1, D.x, a0, a1, a2, a3)
-    STRATA_QUARTER_EVEN(w2, D.y, a0, a1, a2, a3)
-    STRATA_QUARTER_ODD(w3, D.y, a0, a1, a2, a3)
-    return (d * sx) * (float)digits_combine(a0, a1, a2, a3);
+    const int a = block_codes_dot(c, D.x, D.y, row_bcast_i<J>(xo.nq));
+    return (d * row_bcast_f<J>(xo.sc)) * (float)a;
 }
 
 __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restrict__ blobs,
@@ -117,7 +114,7 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restri
     const uint32_t *myrow = wl + ((r & 1) * DG_SEG + l) * DG_RS + 18 * s;
 
     // Chunk q of an item (q < 720: gate rows, else up rows) goes to LDS row
-    // q / 45 at dword 4 (q % 45).
+    // q / 45 at dword 4 (q % 45).  The next item's chunks wait in p0..p4.
     uint4 p0, p1, p2, p3, p4 = make_uint4(0, 0, 0, 0);
     const bool has4 = tid + 4 * DG_THREADS < DG_CHUNKS;
 #define STRATA_DG_LD(P, I)                                                                         \
@@ -148,7 +145,6 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restri
     STRATA_DG_FETCH(rec.x, item % DG_SEGS)
     for (; item < nitems; item += gridDim.x) {
         const int seg = item % DG_SEGS;
-        const int n = rec.z;
         int slot = rec.w;
         const int nxt = item + gridDim.x;
         // token 0's operands and the next record are in flight with the weights
@@ -164,7 +160,7 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restri
         __syncthreads();
         if (nxt < nitems)
             STRATA_DG_FETCH(rec_n.x, nxt % DG_SEGS)   // in flight while this item is computed
-        for (int ti = 0; ti < n; ++ti) {
+        for (int ti = 0; ti < rec.z; ++ti) {
             if (ti > 0) {
                 slot = slots[rec.y + ti];
                 if (slot >= 0 && slot < nslot)
@@ -172,11 +168,13 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restri
             }
             if (slot < 0 || slot >= nslot)
                 continue;   // only a corrupt grouping gets here; uniform per workgroup
-            float acc = block_dot<0>(myrow, xo.d0, xo.sc.x, xo.qs.x);
-            acc += block_dot<1>(myrow + 4, xo.d1, xo.sc.y, xo.qs.y);
-            acc += block_dot<0>(myrow + 9, xo.d2, xo.sc.z, xo.qs.z);
-            acc += block_dot<1>(myrow + 13, xo.d3, xo.sc.w, xo.qs.w);
+            float acc = block_dot<0, 0>(myrow, xo.d0, xo);
+            acc += block_dot<1, 1>(myrow + 4, xo.d1, xo);
+            acc += block_dot<0, 2>(myrow + 9, xo.d2, xo);
+            acc += block_dot<1, 3>(myrow + 13, xo.d3, xo);
             acc += __shfl_xor(acc, 32, 64);   // the wave's two column streams
+            if (ti > 0)
+                __syncthreads();   // wave 0 is done with the previous token's partials
             if (lane < DG_ROWS)
                 part[wave][lane] = acc;
             __syncthreads();
@@ -191,10 +189,9 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restri
                                   lane - 12, qo.pk);
                 if (lane == 0) {
                     hq.scale[(size_t)slot * HSEG16 + seg] = qo.scale;
-                    hq.sum[(size_t)slot * HSEG16 + seg] = qo.sum;
+                    hq.nsum[(size_t)slot * HSEG16 + seg] = -qo.sum;
                 }
             }
-            __syncthreads();
         }
         rec = rec_n;
     }
@@ -213,11 +210,11 @@ static_assert(DD_CHUNKS > 5 * 64 && DD_CHUNKS <= 6 * 64, "six loads per lane");
 
 // Operands of one slot's h for lane column set c0 = r / 2 (block columns
 // 2 j + c0): per column the digit pair, and in lane l of each row the scale
-// and sum of segment 4 (2 j + c0) + k for index 4 j + k = 16 m + l (m = 0, 1).
+// and -sum q of segment 4 (2 j + c0) + k for index 4 j + k = 16 m + l (m = 0, 1).
 struct HOps {
     uint2 d[5];
     float sh0, sh1;
-    int qs0, qs1;
+    int nq0, nq1;
 };
 
 __device__ inline HOps load_hops(const HQ &hq, int slot, int c0, int l)
@@ -232,49 +229,39 @@ __device__ inline HOps load_hops(const HQ &hq, int slot, int c0, int l)
     const int seg1 = 4 * (2 * 4 + c0) + (l & 3);          // index 16 + l (l < 4): j = 4
     const size_t sb = (size_t)slot * HSEG16;
     o.sh0 = hq.scale[sb + seg0];
-    o.qs0 = hq.sum[sb + seg0];
+    o.nq0 = hq.nsum[sb + seg0];
     o.sh1 = l < 4 ? hq.scale[sb + seg1] : 0.f;
-    o.qs1 = l < 4 ? hq.sum[sb + seg1] : 0;
+    o.nq1 = l < 4 ? hq.nsum[sb + seg1] : 0;
     return o;
 }
 
-// ACC += (SH of lane N of the row) * V
+// ACC += (scale of lane N of the row) * V
 #define STRATA_FMA_BCAST(ACC, SH, V, N)                                                            \
     asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"                    \
         : "+v"(ACC)                                                                                \
         : "v"(SH), "v"(V), "i"(N))
 
-// One 16-value segment of a down block: code dword W against digit register D
-// (quarter parity KH), scaled by the segment's scale at broadcast index N.
-#define STRATA_DOWN_SEG(W, D, KH, SHR, QSR, N)                                                     \
-    {                                                                                              \
-        int a0_ = -__builtin_amdgcn_update_dpp(0, QSR, 0x150 + (N), 0xf, 0xf, false);             \
-        int a1_ = 0, a2_ = 0, a3_ = 0;                                                             \
-        if (KH)                                                                                    \
-            STRATA_QUARTER_ODD(W, D, a0_, a1_, a2_, a3_)                                           \
-        else                                                                                       \
-            STRATA_QUARTER_EVEN(W, D, a0_, a1_, a2_, a3_)                                          \
-        const float f_ = (float)digits_combine(a0_, a1_, a2_, a3_);                                \
-        STRATA_FMA_BCAST(bacc, SHR, f_, N);                                                        \
-    }
-
 // One down block from the 5 dwords at p: sel and sh place the codes and the
 // scale (they depend on the block column parity, which is fixed per lane).
-template <int N0, int N1, int N2, int N3>
+// Its four 16-value segments have their scales at broadcast indices N..N+3.
+template <int N>
 __device__ inline float down_block(const uint32_t *p, uint32_t sel, uint32_t sh, uint2 D, float shr,
-                                   int qsr)
+                                   int nqr)
 {
     const uint32_t v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3], v4 = p[4];
-    const uint32_t w0 = __builtin_amdgcn_perm(v1, v0, sel);
-    const uint32_t w1 = __builtin_amdgcn_perm(v2, v1, sel);
-    const uint32_t w2 = __builtin_amdgcn_perm(v3, v2, sel);
-    const uint32_t w3 = __builtin_amdgcn_perm(v4, v3, sel);
+    const Codes c = split_codes(__builtin_amdgcn_perm(v1, v0, sel), __builtin_amdgcn_perm(v2, v1, sel),
+                                __builtin_amdgcn_perm(v3, v2, sel), __builtin_amdgcn_perm(v4, v3, sel));
     const float d = half_bits_to_float(v0 >> sh);
+    const Quad qd = quarters_codes_dot(c, D.x, D.y);
     float bacc = 0.f;
-    STRATA_DOWN_SEG(w0, D.x, 0, shr, qsr, N0)
-    STRATA_DOWN_SEG(w1, D.x, 1, shr, qsr, N1)
-    STRATA_DOWN_SEG(w2, D.y, 0, shr, qsr, N2)
-    STRATA_DOWN_SEG(w3, D.y, 1, shr, qsr, N3)
+    const float f0 = (float)(qd.q[0] + row_bcast_i<N>(nqr));
+    STRATA_FMA_BCAST(bacc, shr, f0, N);
+    const float f1 = (float)(qd.q[1] + row_bcast_i<N + 1>(nqr));
+    STRATA_FMA_BCAST(bacc, shr, f1, N + 1);
+    const float f2 = (float)(qd.q[2] + row_bcast_i<N + 2>(nqr));
+    STRATA_FMA_BCAST(bacc, shr, f2, N + 2);
+    const float f3 = (float)(qd.q[3] + row_bcast_i<N + 3>(nqr));
+    STRATA_FMA_BCAST(bacc, shr, f3, N + 3);
     return d * bacc;
 }
 
@@ -284,11 +271,11 @@ __device__ inline float down_row(const uint32_t *row, int c0, const HOps &ho)
 {
     const uint32_t sel = c0 ? 0x07060504u : 0x05040302u;
     const uint32_t sh = c0 ? 16u : 0u;
-    float acc = down_block<0, 1, 2, 3>(row, sel, sh, ho.d[0], ho.sh0, ho.qs0);
-    acc += down_block<4, 5, 6, 7>(row + 9, sel, sh, ho.d[1], ho.sh0, ho.qs0);
-    acc += down_block<8, 9, 10, 11>(row + 18, sel, sh, ho.d[2], ho.sh0, ho.qs0);
-    acc += down_block<12, 13, 14, 15>(row + 27, sel, sh, ho.d[3], ho.sh0, ho.qs0);
-    acc += down_block<0, 1, 2, 3>(row + 36, sel, sh, ho.d[4], ho.sh1, ho.qs1);
+    float acc = down_block<0>(row, sel, sh, ho.d[0], ho.sh0, ho.nq0);
+    acc += down_block<4>(row + 9, sel, sh, ho.d[1], ho.sh0, ho.nq0);
+    acc += down_block<8>(row + 18, sel, sh, ho.d[2], ho.sh0, ho.nq0);
+    acc += down_block<12>(row + 27, sel, sh, ho.d[3], ho.sh0, ho.nq0);
+    acc += down_block<0>(row + 36, sel, sh, ho.d[4], ho.sh1, ho.nq1);
     return acc;
 }
 
@@ -350,7 +337,7 @@ hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const i
                                  XQ xq, HQ hq, float *out, int T, int n_cu, hipStream_t st)
 {
     const int amax = T * K < E ? T * K : E;
-    const int g1 = min(amax * DG_SEGS, 5 * n_cu);
+    const int g1 = min(amax * DG_SEGS, DG_PER_CU * n_cu);
     const int g2 = (amax * DD_ITEMS_PER_E + DD_WAVES - 1) / DD_WAVES;
     hipLaunchKernelGGL(dec_gateup, dim3(g1), dim3(DG_THREADS), 0, st, blobs, erec, slots, xq, hq,
                        T);

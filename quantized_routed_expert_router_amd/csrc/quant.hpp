@@ -9,9 +9,12 @@
 // of 8 nibbles: dword (par, i) holds in nibble m the digit of value 2m + par.
 // That is how the 2-bit codes fall out of one code dword w: (w & 0x33333333)
 // has code 2m in nibble m, ((w >> 2) & 0x33333333) code 2m + 1.  So the sum of
-// code * q over a quarter is 8 v_dot8 instructions, exact in int32, and the sum
-// of (code - 1) * q = that - sum q removes the code offset of the Q2_0 table
-// {0,1,2,3} -> {-1,0,1,2} ("Strata in the source...", section "The CPU kernels").
+// code * q over a block is 32 v_dot8 instructions, exact in int32 (digit plane
+// i accumulated apart and weighted by 16^i at the end, or -- for a single
+// quarter -- planes 3, 2, 1, 0 in turn with a shift by 4 between them),
+// and the sum of (code - 1) * q = that - sum q removes the code offset of the
+// Q2_0 table {0,1,2,3} -> {-1,0,1,2} ("Strata in the source...", section "The
+// CPU kernels"); the segment stores -sum q for that last add.
 //
 // Layout of one quantised block of 64 values (32 dwords).  Logical dword
 // j = 8k + 4 par + i (quarter k, parity par, digit i) is stored at position
@@ -37,7 +40,7 @@ __host__ __device__ constexpr int dig_pos(int j) { return 2 * (j & 15) + (j >> 4
 struct XQ {
     uint32_t *dig;     // [T][XBLK][32]  one 64-value block per Q2_0 block column
     float *scale;      // [T][XBLK]      scale of raw x; the RMSNorm factor is apart
-    int32_t *sum;      // [T][XBLK]
+    int32_t *nsum;     // [T][XBLK]      -(sum of q over the block)
     float *inv_rms;    // [T]            1 / sqrt(mean(x^2) + 1e-6), or 1 without RMSNorm
 };
 // h per 16 values; the digits of four consecutive segments form one 64-value
@@ -45,7 +48,7 @@ struct XQ {
 struct HQ {
     uint32_t *dig;     // [T*K][HBLK][32]
     float *scale;      // [T*K][HSEG16]
-    int32_t *sum;      // [T*K][HSEG16]
+    int32_t *nsum;     // [T*K][HSEG16]  -(sum of q over the segment)
 };
 
 // Quantise the value v of each lane, with the scale taken over each 16-lane
@@ -103,11 +106,6 @@ __device__ inline void store_quarter(uint32_t *blk, int k, int par, const uint32
         blk[dig_pos(8 * k + 4 * par + i)] = pk[i];
 }
 
-__device__ inline int digits_combine(int a0, int a1, int a2, int a3)
-{
-    return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
-}
-
 // acc += dot8(dword N of the row's broadcast register D, E): v_dot8c with the
 // activation operand taken by row_newbcast:N from lane N of each 16-lane row.
 #define STRATA_DOT8_BCAST(ACC, D, E, N)                                                            \
@@ -115,24 +113,93 @@ __device__ inline int digits_combine(int a0, int a1, int a2, int a3)
         : "+v"(ACC)                                                                                \
         : "v"(D), "v"(E), "i"(N))
 
-// Sum over quarter k of a block of code * q, for the code dword W and the
-// row-broadcast digit register D that holds logical dwords 16 (k / 2) ..
-// 16 (k / 2) + 15: quarters with k even use broadcast lanes 0..7, k odd 8..15.
-#define STRATA_QUARTER_BODY(W, D, A0, A1, A2, A3, N0, N1, N2, N3, N4, N5, N6, N7)                 \
-    {                                                                                              \
-        const int e0_ = (int)((W) & 0x33333333u), e1_ = (int)(((W) >> 2) & 0x33333333u);          \
-        STRATA_DOT8_BCAST(A0, D, e0_, N0);                                                         \
-        STRATA_DOT8_BCAST(A1, D, e0_, N1);                                                         \
-        STRATA_DOT8_BCAST(A2, D, e0_, N2);                                                         \
-        STRATA_DOT8_BCAST(A3, D, e0_, N3);                                                         \
-        STRATA_DOT8_BCAST(A0, D, e1_, N4);                                                         \
-        STRATA_DOT8_BCAST(A1, D, e1_, N5);                                                         \
-        STRATA_DOT8_BCAST(A2, D, e1_, N6);                                                         \
-        STRATA_DOT8_BCAST(A3, D, e1_, N7);                                                         \
+// Digit plane I (0..3) of one 16-value quarter against its two code
+// registers E0 (even codes) and E1 (odd codes): quarter k takes logical dwords
+// 8k + I (par 0) and 8k + 4 + I (par 1), from register DX (k < 2) or DY.
+#define STRATA_QPLANE(A, DR, E0, E1, KH, I)                                                        \
+    STRATA_DOT8_BCAST(A, DR, E0, 8 * (KH) + (I));                                                  \
+    STRATA_DOT8_BCAST(A, DR, E1, 8 * (KH) + 4 + (I))
+
+// The 16 code dwords of a block (W0..W3) split into even/odd code registers.
+struct Codes {
+    int e0[4], e1[4];
+};
+__device__ inline Codes split_codes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3)
+{
+    Codes c;
+    const uint32_t w[4] = {w0, w1, w2, w3};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        c.e0[k] = (int)(w[k] & 0x33333333u);
+        c.e1[k] = (int)((w[k] >> 2) & 0x33333333u);
     }
-#define STRATA_QUARTER_EVEN(W, D, A0, A1, A2, A3)                                                  \
-    STRATA_QUARTER_BODY(W, D, A0, A1, A2, A3, 0, 1, 2, 3, 4, 5, 6, 7)
-#define STRATA_QUARTER_ODD(W, D, A0, A1, A2, A3)                                                   \
-    STRATA_QUARTER_BODY(W, D, A0, A1, A2, A3, 8, 9, 10, 11, 12, 13, 14, 15)
+    return c;
+}
+
+// Sum over a 64-value block of code * q plus A0: one accumulator per digit
+// plane, so that consecutive v_dot8 never wait on each other's result.
+__device__ inline int block_codes_dot(const Codes &c, uint32_t DX, uint32_t DY, int A0)
+{
+    int a0 = A0, a1 = 0, a2 = 0, a3 = 0;
+#define STRATA_BQUARTER(DR, K, KH)                                                                 \
+    STRATA_DOT8_BCAST(a0, DR, c.e0[K], 8 * (KH) + 0);                                              \
+    STRATA_DOT8_BCAST(a1, DR, c.e0[K], 8 * (KH) + 1);                                              \
+    STRATA_DOT8_BCAST(a2, DR, c.e0[K], 8 * (KH) + 2);                                              \
+    STRATA_DOT8_BCAST(a3, DR, c.e0[K], 8 * (KH) + 3);                                              \
+    STRATA_DOT8_BCAST(a0, DR, c.e1[K], 8 * (KH) + 4);                                              \
+    STRATA_DOT8_BCAST(a1, DR, c.e1[K], 8 * (KH) + 5);                                              \
+    STRATA_DOT8_BCAST(a2, DR, c.e1[K], 8 * (KH) + 6);                                              \
+    STRATA_DOT8_BCAST(a3, DR, c.e1[K], 8 * (KH) + 7)
+    STRATA_BQUARTER(DX, 0, 0);
+    STRATA_BQUARTER(DX, 1, 1);
+    STRATA_BQUARTER(DY, 2, 0);
+    STRATA_BQUARTER(DY, 3, 1);
+#undef STRATA_BQUARTER
+    return a0 + (a1 << 4) + (a2 << 8) + (a3 << 12);
+}
+
+// The four 16-value quarters of a block, each summed apart (code * q), the
+// four chains interleaved so that consecutive v_dot8 do not depend on each
+// other; each chain takes digit planes 3, 2, 1, 0 with a shift by 4 between.
+struct Quad {
+    int q[4];
+};
+__device__ inline Quad quarters_codes_dot(const Codes &c, uint32_t DX, uint32_t DY)
+{
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+#define STRATA_QPLANES(I)                                                                          \
+    STRATA_DOT8_BCAST(a0, DX, c.e0[0], 0 + (I));                                                   \
+    STRATA_DOT8_BCAST(a1, DX, c.e0[1], 8 + (I));                                                   \
+    STRATA_DOT8_BCAST(a2, DY, c.e0[2], 0 + (I));                                                   \
+    STRATA_DOT8_BCAST(a3, DY, c.e0[3], 8 + (I));                                                   \
+    STRATA_DOT8_BCAST(a0, DX, c.e1[0], 4 + (I));                                                   \
+    STRATA_DOT8_BCAST(a1, DX, c.e1[1], 12 + (I));                                                  \
+    STRATA_DOT8_BCAST(a2, DY, c.e1[2], 4 + (I));                                                   \
+    STRATA_DOT8_BCAST(a3, DY, c.e1[3], 12 + (I))
+    STRATA_QPLANES(3);
+    a0 <<= 4; a1 <<= 4; a2 <<= 4; a3 <<= 4;
+    STRATA_QPLANES(2);
+    a0 <<= 4; a1 <<= 4; a2 <<= 4; a3 <<= 4;
+    STRATA_QPLANES(1);
+    a0 <<= 4; a1 <<= 4; a2 <<= 4; a3 <<= 4;
+    STRATA_QPLANES(0);
+#undef STRATA_QPLANES
+    Quad r;
+    r.q[0] = a0;
+    r.q[1] = a1;
+    r.q[2] = a2;
+    r.q[3] = a3;
+    return r;
+}
+
+// Lane N of the caller's 16-lane row, as seen by every lane of the row.
+template <int N> __device__ inline int row_bcast_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0x150 + N, 0xF, 0xF, false);
+}
+template <int N> __device__ inline float row_bcast_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+}
 
 } // namespace strata

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(RG_THREADS) void rdec_gemv(const float *__restrict_
                 store_quarter(xq.dig + (size_t)p * BLK_DWORDS, lane >> 4, l16 - 12, qo.pk);
             if (lane == 0) {
                 xq.scale[p] = qo.scale;
-                xq.sum[p] = qo.sum;
+                xq.nsum[p] = -qo.sum;
             }
         }
     }
