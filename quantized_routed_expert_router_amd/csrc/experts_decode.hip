@@ -16,13 +16,12 @@
 // registers carry a whole 64-value block.
 //
 //  dec_gateup  item = (active expert, 16 FF rows): the 16 gate and 16 up rows
-//              (23 KB).  320 threads = 5 waves; lane (r = lane / 16, l) takes
+//              (23 KB).  256 threads = 4 waves; lane (r = lane / 16, l) takes
 //              row l of gate (r even) or up (r odd) and block columns
-//              4 s .. 4 s + 3 with s = 2 w + r / 2.  Partial sums meet in a
+//              5 s .. 5 s + 4 with s = 2 w + r / 2.  Partial sums meet in a
 //              fixed order; wave 0 forms h = silu(g) * u for the 16 rows and
-//              quantises them as one 16-value segment.  Five workgroups per
-//              CU loop over the items; each loads its next item into
-//              registers while the current one is computed.
+//              quantises them as one 16-value segment.  One item per
+//              workgroup; 4-wave workgroups of 23 KB LDS run six to a CU.
 //  dec_down    item = (active expert, 32 output rows), one wave: lane (r, l)
 //              takes row 16 (r % 2) + l and block columns 2 j + r / 2; the two
 //              halves of each row are added and the row's value written per
@@ -35,17 +34,17 @@
 namespace strata {
 
 // ------------------------------------------------------------------ gate / up
-constexpr int DG_THREADS = 320;
+constexpr int DG_WAVES = 4;
+constexpr int DG_THREADS = 64 * DG_WAVES;
 constexpr int DG_SEG = 16;                          // FF rows per item (one h segment)
 constexpr int DG_SEGS = FF / DG_SEG;                // 40
 constexpr int DG_ROWS = 2 * DG_SEG;                 // 16 gate + 16 up rows
 constexpr int DG_CPR = ROW_G / 16;                  // 45 16-byte chunks per row
 constexpr int DG_CHUNKS = DG_ROWS * DG_CPR;         // 1,440
 constexpr int DG_RS = ROW_G / 4 + 1;                // LDS row stride in dwords (181, odd)
-constexpr int DG_LOADS = (DG_CHUNKS + DG_THREADS - 1) / DG_THREADS;   // 5
-static_assert(DG_LOADS == 5 && DG_CHUNKS > 4 * DG_THREADS, "five loads per thread");
-static_assert(5 * 2 * 4 == NB_G, "5 waves x 2 column streams x 4 block columns");
-constexpr int DG_PER_CU = 5;                        // resident workgroups per CU (23 KB of LDS each)
+constexpr int DG_COLS = 5;                          // block columns per lane
+static_assert(DG_WAVES * 2 * DG_COLS == NB_G, "4 waves x 2 column streams x 5 block columns");
+static_assert(DG_CHUNKS > 5 * DG_THREADS && DG_CHUNKS <= 6 * DG_THREADS, "six loads per thread");
 
 // Records of the grouping for the decode kernels: erec[0].x = number of active
 // experts, erec[1 + a] = {expert, first grouped slot, token count, first slot}.
@@ -55,11 +54,11 @@ __device__ inline int active_count(const int4 *erec, int T)
 }
 
 // Activation operands of one token for lane column stream s (block columns
-// 4 s + j): the digit pairs (dword l, dword 16 + l) of each column, and in
-// lane j < 4 of each 16-lane row the column's scale times the inverse RMS
-// and its -sum q (handed to the row by DPP broadcast).
+// 5 s + j): the digit pairs (dword l, dword 16 + l) of each column, and in
+// lane j < 5 of each 16-lane row the column's scale times the inverse RMS and
+// its -sum q (handed to the row by DPP broadcast).
 struct XOps {
-    uint2 d0, d1, d2, d3;
+    uint2 d[DG_COLS];
     float sc;
     int nq;
 };
@@ -67,29 +66,28 @@ struct XOps {
 __device__ inline XOps load_xops(const XQ &xq, int t, int s, int l)
 {
     XOps o;
-    const size_t xb = (size_t)t * XBLK + 4 * s;
+    const size_t xb = (size_t)t * XBLK + DG_COLS * s;
     const uint2 *dp = reinterpret_cast<const uint2 *>(xq.dig + xb * BLK_DWORDS) + l;
-    o.d0 = dp[0];
-    o.d1 = dp[16];
-    o.d2 = dp[32];
-    o.d3 = dp[48];
-    const int j = l & 3;
+#pragma unroll
+    for (int j = 0; j < DG_COLS; ++j)
+        o.d[j] = dp[16 * j];
+    const int j = l < DG_COLS ? l : 0;
     o.sc = xq.scale[xb + j] * xq.inv_rms[t];
     o.nq = xq.nsum[xb + j];
     return o;
 }
 
-// One block of a row held in LDS: the 5 dwords from p hold it; ODD (block
-// column parity) says where the scale and the codes sit in them; J is the
-// block's index among the lane's four columns.
-template <int ODD, int J>
-__device__ inline float block_dot(const uint32_t *p, uint2 D, const XOps &xo)
+// One block of a row held in LDS: the 5 dwords from p hold it; sel and sh
+// place the codes and the scale (they depend on the column parity); J is the
+// block's index among the lane's columns.
+template <int J>
+__device__ inline float block_dot(const uint32_t *p, uint32_t sel, uint32_t sh, uint2 D,
+                                  const XOps &xo)
 {
     const uint32_t v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3], v4 = p[4];
-    constexpr uint32_t sel = ODD ? 0x07060504u : 0x05040302u;
     const Codes c = split_codes(__builtin_amdgcn_perm(v1, v0, sel), __builtin_amdgcn_perm(v2, v1, sel),
                                 __builtin_amdgcn_perm(v3, v2, sel), __builtin_amdgcn_perm(v4, v3, sel));
-    const float d = half_bits_to_float(ODD ? (v0 >> 16) : v0);
+    const float d = half_bits_to_float(v0 >> sh);
     const int a = block_codes_dot(c, D.x, D.y, row_bcast_i<J>(xo.nq));
     return (d * row_bcast_f<J>(xo.sc)) * (float)a;
 }
@@ -100,38 +98,31 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restri
                                                          HQ hq, int T)
 {
     __shared__ uint32_t wl[DG_ROWS * DG_RS];
-    __shared__ float part[5][DG_ROWS];
+    __shared__ float part[DG_WAVES][DG_ROWS];
 
     const int nslot = T * K;
-    const int nitems = active_count(erec, T) * DG_SEGS;
-    int item = blockIdx.x;
-    if (item >= nitems)
+    const int item = blockIdx.x;
+    if (item >= active_count(erec, T) * DG_SEGS)
         return;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane >> 4, l = lane & 15;
-    const int s = 2 * wave + (r >> 1);                       // column stream: columns 4s..4s+3
-    const uint32_t *myrow = wl + ((r & 1) * DG_SEG + l) * DG_RS + 18 * s;
-
-    // Chunk q of an item (q < 720: gate rows, else up rows) goes to LDS row
-    // q / 45 at dword 4 (q % 45).  The next item's chunks wait in p0..p4.
-    uint4 p0, p1, p2, p3, p4 = make_uint4(0, 0, 0, 0);
-    const bool has4 = tid + 4 * DG_THREADS < DG_CHUNKS;
+    const int s = 2 * wave + (r >> 1);                 // column stream: columns 5s .. 5s+4
+    const int4 rec = erec[1 + item / DG_SEGS];
+    const int seg = item % DG_SEGS;
+    int slot = rec.w;
+    // token 0's operands are in flight with the weights
+    XOps xo = load_xops(xq, slot >= 0 && slot < nslot ? slot / K : 0, s, l);
+    {
+        // chunk q (q < 720: gate rows, else up rows) goes to LDS row q / 45 at
+        // dword 4 (q % 45)
+        const uint8_t *blob = blobs + (size_t)rec.x * BLOB + (size_t)seg * DG_SEG * ROW_G;
+        const uint4 *g = reinterpret_cast<const uint4 *>(blob);
+        const uint4 *u = reinterpret_cast<const uint4 *>(blob + MAT);
+        const bool has5 = tid + 5 * DG_THREADS < DG_CHUNKS;
 #define STRATA_DG_LD(P, I)                                                                         \
-    P = (tid + DG_THREADS * (I)) < DG_CHUNKS / 2 ? g_[tid + DG_THREADS * (I)]                      \
-                                                 : u_[tid + DG_THREADS * (I) - DG_CHUNKS / 2];
-#define STRATA_DG_FETCH(E_, SEG_)                                                                  \
-    {                                                                                              \
-        const uint8_t *blob_ = blobs + (size_t)(E_) * BLOB + (size_t)(SEG_) * DG_SEG * ROW_G;      \
-        const uint4 *g_ = reinterpret_cast<const uint4 *>(blob_);                                  \
-        const uint4 *u_ = reinterpret_cast<const uint4 *>(blob_ + MAT);                            \
-        STRATA_DG_LD(p0, 0)                                                                        \
-        STRATA_DG_LD(p1, 1)                                                                        \
-        STRATA_DG_LD(p2, 2)                                                                        \
-        STRATA_DG_LD(p3, 3)                                                                        \
-        if (has4)                                                                                  \
-            STRATA_DG_LD(p4, 4)                                                                    \
-    }
+    const uint4 P = (tid + DG_THREADS * (I)) < DG_CHUNKS / 2 ? g[tid + DG_THREADS * (I)]           \
+                                                             : u[tid + DG_THREADS * (I) - DG_CHUNKS / 2];
 #define STRATA_DG_ST(P, I)                                                                         \
     {                                                                                              \
         const int q_ = tid + DG_THREADS * (I);                                                     \
@@ -141,63 +132,69 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restri
         d_[2] = P.z;                                                                               \
         d_[3] = P.w;                                                                               \
     }
-    int4 rec = erec[1 + item / DG_SEGS];
-    STRATA_DG_FETCH(rec.x, item % DG_SEGS)
-    for (; item < nitems; item += gridDim.x) {
-        const int seg = item % DG_SEGS;
-        int slot = rec.w;
-        const int nxt = item + gridDim.x;
-        // token 0's operands and the next record are in flight with the weights
-        XOps xo = load_xops(xq, slot >= 0 && slot < nslot ? slot / K : 0, s, l);
-        const int4 rec_n = erec[1 + min(nxt, nitems - 1) / DG_SEGS];
-        __syncthreads();   // the previous item's LDS readers are done
+        STRATA_DG_LD(p0, 0)
+        STRATA_DG_LD(p1, 1)
+        STRATA_DG_LD(p2, 2)
+        STRATA_DG_LD(p3, 3)
+        STRATA_DG_LD(p4, 4)
+        const uint4 p5 = has5 ? u[tid + 5 * DG_THREADS - DG_CHUNKS / 2] : make_uint4(0, 0, 0, 0);
         STRATA_DG_ST(p0, 0)
         STRATA_DG_ST(p1, 1)
         STRATA_DG_ST(p2, 2)
         STRATA_DG_ST(p3, 3)
-        if (has4)
-            STRATA_DG_ST(p4, 4)
+        STRATA_DG_ST(p4, 4)
+        if (has5)
+            STRATA_DG_ST(p5, 5)
+#undef STRATA_DG_ST
+#undef STRATA_DG_LD
+    }
+    // Block column 5 s + j starts at byte 90 s + 18 j of the row; its 5-dword
+    // window starts 2 bytes earlier when the column is odd.
+    const uint32_t *row = wl + ((r & 1) * DG_SEG + l) * DG_RS;
+    const int odd_s = s & 1;
+    const uint32_t sel_e = odd_s ? 0x07060504u : 0x05040302u;   // columns with j even
+    const uint32_t sel_o = odd_s ? 0x05040302u : 0x07060504u;   // columns with j odd
+    const uint32_t sh_e = odd_s ? 16u : 0u, sh_o = odd_s ? 0u : 16u;
+    const uint32_t *w0 = row + (90 * s - 2 * odd_s) / 4;         // j = 0
+    const uint32_t *w1 = row + (90 * s + 18 - 2 * (1 - odd_s)) / 4;
+    const uint32_t *w2 = row + (90 * s + 36 - 2 * odd_s) / 4;
+    const uint32_t *w3 = row + (90 * s + 54 - 2 * (1 - odd_s)) / 4;
+    const uint32_t *w4 = row + (90 * s + 72 - 2 * odd_s) / 4;
+    __syncthreads();
+    for (int ti = 0; ti < rec.z; ++ti) {
+        if (ti > 0) {
+            slot = slots[rec.y + ti];
+            if (slot >= 0 && slot < nslot)
+                xo = load_xops(xq, slot / K, s, l);
+        }
+        if (slot < 0 || slot >= nslot)
+            continue;   // only a corrupt grouping gets here; uniform per workgroup
+        float acc = block_dot<0>(w0, sel_e, sh_e, xo.d[0], xo);
+        acc += block_dot<1>(w1, sel_o, sh_o, xo.d[1], xo);
+        acc += block_dot<2>(w2, sel_e, sh_e, xo.d[2], xo);
+        acc += block_dot<3>(w3, sel_o, sh_o, xo.d[3], xo);
+        acc += block_dot<4>(w4, sel_e, sh_e, xo.d[4], xo);
+        acc += __shfl_xor(acc, 32, 64);   // the wave's two column streams
+        if (ti > 0)
+            __syncthreads();   // wave 0 is done with the previous token's partials
+        if (lane < DG_ROWS)
+            part[wave][lane] = acc;
         __syncthreads();
-        if (nxt < nitems)
-            STRATA_DG_FETCH(rec_n.x, nxt % DG_SEGS)   // in flight while this item is computed
-        for (int ti = 0; ti < rec.z; ++ti) {
-            if (ti > 0) {
-                slot = slots[rec.y + ti];
-                if (slot >= 0 && slot < nslot)
-                    xo = load_xops(xq, slot / K, s, l);
-            }
-            if (slot < 0 || slot >= nslot)
-                continue;   // only a corrupt grouping gets here; uniform per workgroup
-            float acc = block_dot<0, 0>(myrow, xo.d0, xo);
-            acc += block_dot<1, 1>(myrow + 4, xo.d1, xo);
-            acc += block_dot<0, 2>(myrow + 9, xo.d2, xo);
-            acc += block_dot<1, 3>(myrow + 13, xo.d3, xo);
-            acc += __shfl_xor(acc, 32, 64);   // the wave's two column streams
-            if (ti > 0)
-                __syncthreads();   // wave 0 is done with the previous token's partials
-            if (lane < DG_ROWS)
-                part[wave][lane] = acc;
-            __syncthreads();
-            if (wave == 0) {
-                const int j = lane & 31;
-                const float v = (((part[0][j] + part[1][j]) + part[2][j]) + part[3][j]) + part[4][j];
-                const float u = __shfl(v, (lane & 15) + DG_SEG, 64);
-                const float h = lane < DG_SEG ? v / (1.f + expf(-v)) * u : 0.f;
-                const QuantOut qo = quant_lanes<false>(h);
-                if (lane == 12 || lane == 13)
-                    store_quarter(hq.dig + ((size_t)slot * HBLK + (seg >> 2)) * BLK_DWORDS, seg & 3,
-                                  lane - 12, qo.pk);
-                if (lane == 0) {
-                    hq.scale[(size_t)slot * HSEG16 + seg] = qo.scale;
-                    hq.nsum[(size_t)slot * HSEG16 + seg] = -qo.sum;
-                }
+        if (wave == 0) {
+            const int j = lane & 31;
+            const float v = ((part[0][j] + part[1][j]) + part[2][j]) + part[3][j];
+            const float u = __shfl(v, (lane & 15) + DG_SEG, 64);
+            const float h = lane < DG_SEG ? v / (1.f + expf(-v)) * u : 0.f;
+            const QuantOut qo = quant_lanes<false>(h);
+            if (lane == 12 || lane == 13)
+                store_quarter(hq.dig + ((size_t)slot * HBLK + (seg >> 2)) * BLK_DWORDS, seg & 3,
+                              lane - 12, qo.pk);
+            if (lane == 0) {
+                hq.scale[(size_t)slot * HSEG16 + seg] = qo.scale;
+                hq.nsum[(size_t)slot * HSEG16 + seg] = -qo.sum;
             }
         }
-        rec = rec_n;
     }
-#undef STRATA_DG_ST
-#undef STRATA_DG_FETCH
-#undef STRATA_DG_LD
 }
 
 // ----------------------------------------------------------------------- down
@@ -337,7 +334,8 @@ hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const i
                                  XQ xq, HQ hq, float *out, int T, int n_cu, hipStream_t st)
 {
     const int amax = T * K < E ? T * K : E;
-    const int g1 = min(amax * DG_SEGS, DG_PER_CU * n_cu);
+    const int g1 = amax * DG_SEGS;
+    (void)n_cu;
     const int g2 = (amax * DD_ITEMS_PER_E + DD_WAVES - 1) / DD_WAVES;
     hipLaunchKernelGGL(dec_gateup, dim3(g1), dim3(DG_THREADS), 0, st, blobs, erec, slots, xq, hq,
                        T);
