@@ -207,8 +207,8 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = "experts stage (prep_kernel + dec_gateup + dec_down)" if not prefill else \
-        "experts stage (prep_kernel + plan_kernel + pf_gateup + pf_down)"
+    roof["kernel"] = ("experts stage (rdec_gemv<false,true> + dec_gateup + dec_down)" if not prefill else
+                      "experts stage (prep_kernel + plan_kernel + pf_gateup + pf_down)")
     roof["ms_per_launch"] = ex_ms
 
     if stack:
