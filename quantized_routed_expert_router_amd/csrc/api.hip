@@ -17,12 +17,14 @@ hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_it
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
                                int rmsnorm, float *lraw, XQ xq, bool prep, int32_t *ids,
                                float *w, int group, int32_t *offsets, int32_t *slots,
-                               int32_t *active, int4 *erec, hipStream_t st);
+                               int32_t *active, int4 *erec, int32_t *cdone, int32_t *esync,
+                               hipStream_t st);
 hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const int32_t *offsets,
                               const int32_t *slots, const int32_t *active, int4 *erec,
-                              hipStream_t st);
+                              int32_t *esync, hipStream_t st);
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
-                                 XQ xq, HQ hq, float *out, int T, int n_cu, hipStream_t st);
+                                 XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
+                                 const float *w, float *y, float *res, hipStream_t st);
 hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
@@ -56,6 +58,7 @@ struct Carve {
     HQ hq;
     int32_t *offsets, *slots, *active, *ids, *mlist, *nitems;
     int4 *erec;
+    int32_t *cdone, *esync;
 };
 
 Carve carve(void *ws, int T)
@@ -74,29 +77,14 @@ Carve carve(void *ws, int T)
     c.slots = at<int32_t>(ws, L.slots);
     c.active = at<int32_t>(ws, L.active);
     c.erec = at<int4>(ws, L.erec);
+    c.cdone = at<int32_t>(ws, L.cdone);
+    c.esync = at<int32_t>(ws, L.esync);
     c.ids = at<int32_t>(ws, L.ids);
     c.w = at<float>(ws, L.w);
     c.mlist = at<int32_t>(ws, L.mlist);
     c.nitems = at<int32_t>(ws, L.nitems);
     c.out = at<float>(ws, L.out);
     return c;
-}
-
-// Compute units of the current device (cached per device).
-int n_cu()
-{
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    if (!cache[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
 }
 
 #define STRATA_TRY(expr)                                                                           \
@@ -111,7 +99,8 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
                 const int32_t *slots, const int32_t *active, float *out, int T, hipStream_t st)
 {
     if (is_decode(T)) {
-        STRATA_TRY(launch_decode_experts(blobs, c.erec, slots, c.xq, c.hq, out, T, n_cu(), st));
+        STRATA_TRY(launch_decode_experts(blobs, c.erec, slots, c.xq, c.hq, out, T, c.esync, nullptr,
+                                         nullptr, nullptr, nullptr, st));
     } else {
         STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
         STRATA_TRY(launch_prefill_experts(blobs, offsets, slots, active, c.mlist, c.nitems,
@@ -127,7 +116,7 @@ int run_prep(const Carve &c, const float *x, int T, int rms, const int32_t *offs
              const int32_t *slots, const int32_t *active, hipStream_t st)
 {
     if (is_decode(T))
-        STRATA_TRY(launch_prep_decode(x, T, rms, c.xq, offsets, slots, active, c.erec, st));
+        STRATA_TRY(launch_prep_decode(x, T, rms, c.xq, offsets, slots, active, c.erec, c.esync, st));
     else
         STRATA_TRY(launch_prep(x, T, rms, c.xhat, c.xperm, st));
     return STRATA_OK;
@@ -167,7 +156,7 @@ int strata_moe_route(const float *x, int T, const uint16_t *router, const float 
     const int rms = flags & STRATA_RMSNORM;
     if (is_decode(T)) {
         STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, false, ids, w, 0,
-                                       nullptr, nullptr, nullptr, nullptr, st));
+                                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st));
     } else {
         STRATA_TRY(launch_prep(x, T, rms, c.xhat, nullptr, st));
         STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
@@ -252,16 +241,22 @@ int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
     const int rms = flags & STRATA_RMSNORM;
     if (is_decode(T)) {
         STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, true, ids_o, w_o, 1,
-                                       c.offsets, c.slots, c.active, c.erec, st));
+                                       c.offsets, c.slots, c.active, c.erec, c.cdone, c.esync,
+                                       st));
     } else {
         STRATA_TRY(launch_prep(x, T, rms, c.xhat, c.xperm, st));
         STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
         STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
         STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, st));
     }
+    const bool res = flags & STRATA_RESIDUAL;
+    if (is_decode(T)) {   // the down kernel finishes the combine
+        STRATA_TRY(launch_decode_experts(blobs, c.erec, c.slots, c.xq, c.hq, c.out, T, c.esync,
+                                         c.cdone, w_o, y, res ? x : nullptr, st));
+        return STRATA_OK;
+    }
     if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st)))
         return rc;
-    const bool res = flags & STRATA_RESIDUAL;
     STRATA_TRY(launch_combine(c.out, w_o, T, y, res ? x : nullptr, 0, st));
     return STRATA_OK;
 }

@@ -60,6 +60,8 @@ struct Ws {
     size_t hq_sum;     // i32 [Td*K][40]
     size_t hperm;      // f16 [Tp*K][FF]     (grouped order)
     size_t out;        // f32 [T*K][H]
+    size_t cdone;      // i32 [Td][H/32]      decode layer: finished slots per (token, 32 rows)
+    size_t esync;      // i32 [1+32E]        decode experts: finished gate/up items per expert (128-B apart)
     size_t total;
     int max_items;
 };
@@ -103,6 +105,8 @@ inline Ws ws_layout(int T)
     L.hq_sum = take(Td * K * ns * 4);
     L.hperm = take(Tp * K * FF * 2);
     L.out = take((size_t)T * K * H * 4);
+    L.cdone = take(Td * (H / 32) * 4);
+    L.esync = take(Td ? (size_t)(1 + 32 * E) * 4 : 0);
     L.total = o;
     return L;
 }

@@ -25,7 +25,9 @@
 //  dec_down    item = (active expert, 32 output rows), one wave: lane (r, l)
 //              takes row 16 (r % 2) + l and block columns 2 j + r / 2; the two
 //              halves of each row are added and the row's value written per
-//              slot.  Four items per workgroup.
+//              slot.  Four items per workgroup.  In a layer call it also
+//              finishes the combine (the last slot of a token's rows to be
+//              done sums the token's K slots).
 // Every sum has a fixed order, so results are bitwise reproducible and do not
 // depend on the other tokens of the call.
 #include "common.hpp"
@@ -92,18 +94,25 @@ __device__ inline float block_dot(const uint32_t *p, uint32_t sel, uint32_t sh, 
     return (d * row_bcast_f<J>(xo.sc)) * (float)a;
 }
 
-__global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restrict__ blobs,
-                                                         const int4 *__restrict__ erec,
-                                                         const int32_t *__restrict__ slots, XQ xq,
-                                                         HQ hq, int T)
-{
-    __shared__ uint32_t wl[DG_ROWS * DG_RS];
-    __shared__ float part[DG_WAVES][DG_ROWS];
+// Per-call counters of the fused kernel (zeroed by the router / prep kernel):
+// sync[1 + a] counts the finished gate/up items of active expert a.
+constexpr int EX_WAIT_LIMIT = 1 << 18;   // bounded wait (~0.2 s), never reached in a correct call
+constexpr int EX_GD_STRIDE = 32;         // one 128-byte line per expert counter
 
+// h values are stored and read at agent scope (coherent across the XCDs'
+// L2 caches): the down part of the same launch reads them.
+__device__ inline void store_h(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One gate/up item: LDS wl [DG_ROWS][DG_RS] dwords and part [DG_WAVES][DG_ROWS].
+__device__ void gateup_item(int item, const uint8_t *__restrict__ blobs,
+                            const int4 *__restrict__ erec, const int32_t *__restrict__ slots,
+                            const XQ &xq, const HQ &hq, int T, uint32_t *wl,
+                            float (*part)[DG_ROWS], int32_t *gdone)
+{
     const int nslot = T * K;
-    const int item = blockIdx.x;
-    if (item >= active_count(erec, T) * DG_SEGS)
-        return;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane >> 4, l = lane & 15;
@@ -186,14 +195,26 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restri
             const float u = __shfl(v, (lane & 15) + DG_SEG, 64);
             const float h = lane < DG_SEG ? v / (1.f + expf(-v)) * u : 0.f;
             const QuantOut qo = quant_lanes<false>(h);
-            if (lane == 12 || lane == 13)
-                store_quarter(hq.dig + ((size_t)slot * HBLK + (seg >> 2)) * BLK_DWORDS, seg & 3,
-                              lane - 12, qo.pk);
+            if (lane == 12 || lane == 13) {
+                uint32_t *blk = hq.dig + ((size_t)slot * HBLK + (seg >> 2)) * BLK_DWORDS;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    store_h(blk + dig_pos(8 * (seg & 3) + 4 * (lane - 12) + i), qo.pk[i]);
+            }
             if (lane == 0) {
-                hq.scale[(size_t)slot * HSEG16 + seg] = qo.scale;
-                hq.nsum[(size_t)slot * HSEG16 + seg] = -qo.sum;
+                store_h(reinterpret_cast<uint32_t *>(hq.scale) + (size_t)slot * HSEG16 + seg,
+                        __float_as_uint(qo.scale));
+                store_h(reinterpret_cast<uint32_t *>(hq.nsum) + (size_t)slot * HSEG16 + seg,
+                        (uint32_t)(-qo.sum));
             }
         }
+    }
+    if (wave == 0) {   // every h value of the item is in memory: count the item
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0)
+            __hip_atomic_fetch_add(gdone + EX_GD_STRIDE * (item / DG_SEGS), 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -214,21 +235,28 @@ struct HOps {
     int nq0, nq1;
 };
 
+template <class V> __device__ inline V load_h(const V *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ inline HOps load_hops(const HQ &hq, int slot, int c0, int l)
 {
     HOps o;
-    const uint2 *dp =
-        reinterpret_cast<const uint2 *>(hq.dig + (size_t)slot * HBLK * BLK_DWORDS) + l;
+    const unsigned long long *dp =
+        reinterpret_cast<const unsigned long long *>(hq.dig + (size_t)slot * HBLK * BLK_DWORDS) + l;
 #pragma unroll
-    for (int j = 0; j < 5; ++j)
-        o.d[j] = dp[16 * (2 * j + c0)];
+    for (int j = 0; j < 5; ++j) {
+        const unsigned long long v = load_h(dp + 16 * (2 * j + c0));
+        o.d[j] = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+    }
     const int seg0 = 4 * (2 * (l >> 2) + c0) + (l & 3);   // index l: j = l / 4, k = l % 4
     const int seg1 = 4 * (2 * 4 + c0) + (l & 3);          // index 16 + l (l < 4): j = 4
     const size_t sb = (size_t)slot * HSEG16;
-    o.sh0 = hq.scale[sb + seg0];
-    o.nq0 = hq.nsum[sb + seg0];
-    o.sh1 = l < 4 ? hq.scale[sb + seg1] : 0.f;
-    o.nq1 = l < 4 ? hq.nsum[sb + seg1] : 0;
+    o.sh0 = load_h(hq.scale + sb + seg0);
+    o.nq0 = load_h(hq.nsum + sb + seg0);
+    o.sh1 = l < 4 ? load_h(hq.scale + sb + seg1) : 0.f;
+    o.nq1 = l < 4 ? load_h(hq.nsum + sb + seg1) : 0;
     return o;
 }
 
@@ -276,28 +304,40 @@ __device__ inline float down_row(const uint32_t *row, int c0, const HOps &ho)
     return acc;
 }
 
-__global__ __launch_bounds__(64 * DD_WAVES) void dec_down(const uint8_t *__restrict__ blobs,
-                                                         const int4 *__restrict__ erec,
-                                                         const int32_t *__restrict__ slots, HQ hq,
-                                                         float *__restrict__ out, int T)
-{
-    __shared__ __attribute__((aligned(16))) uint32_t wl[DD_WAVES][DD_ROWS * DD_RS];
+// The layer's combine, fused: when the counters cdone are given, the wave
+// that finishes the last of token t's K slots for a 32-row chunk sums them in
+// routing order, y_t = sum_k w[t][k] * out[t*K + k] (the fma order of
+// combine_kernel), stores y and/or adds it to the residual x.  The per-slot
+// rows are written and read with agent-scope (XCD-coherent) accesses, and a
+// wave's rows are complete in memory before it counts its slot.
+struct Combine {
+    int32_t *cdone;     // [T][H/32] zeroed by the router, or NULL (no combine)
+    const float *w;     // [T][K]
+    float *y;           // [T][H] or NULL
+    float *res;         // [T][H] or NULL: res += y
+};
 
+// One down group: DD_WAVES items (32-row chunks) of one expert, one per wave,
+// each in its own LDS slice wl [DD_ROWS * DD_RS] dwords.  The weights are
+// requested first; the expert's h is read once its gate/up items are counted.
+__device__ void down_group(int grp, const uint8_t *__restrict__ blobs,
+                           const int4 *__restrict__ erec, const int32_t *__restrict__ slots,
+                           const HQ &hq, float *__restrict__ out, int T, const Combine &cb,
+                           uint32_t *wl, const int32_t *gdone)
+{
     const int nslot = T * K;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int item = blockIdx.x * DD_WAVES + wave;
-    if (item >= active_count(erec, T) * DD_ITEMS_PER_E)
-        return;
+    const int item = grp * DD_WAVES + wave;
     const int r = lane >> 4, l = lane & 15;
     const int c0 = r >> 1;
-    const int4 rec = erec[1 + item / DD_ITEMS_PER_E];
+    const int a = item / DD_ITEMS_PER_E;
+    const int4 rec = erec[1 + a];
     const int ch = item % DD_ITEMS_PER_E;
     int slot = rec.w;
-    HOps ho = load_hops(hq, slot >= 0 && slot < nslot ? slot : 0, c0, l);
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(blobs + (size_t)rec.x * BLOB + 2 * MAT +
                                                            (size_t)ch * DD_ROWS * ROW_D);
-        uint4 *dst = reinterpret_cast<uint4 *>(wl[wave]);
+        uint4 *dst = reinterpret_cast<uint4 *>(wl);
         const bool has5 = lane + 320 < DD_CHUNKS;
         const uint4 v0 = src[lane], v1 = src[lane + 64], v2 = src[lane + 128];
         const uint4 v3 = src[lane + 192], v4 = src[lane + 256];
@@ -310,11 +350,24 @@ __global__ __launch_bounds__(64 * DD_WAVES) void dec_down(const uint8_t *__restr
         if (has5)
             dst[lane + 320] = v5;
     }
+    // wait (bounded) until the expert's DG_SEGS gate/up items have stored h;
+    // h itself is read with agent-scope loads, so the poll needs no cache
+    // invalidation, only to stay ahead of those loads in program order.  One
+    // lane of the workgroup polls, sparsely.
+    if (threadIdx.x == 0) {
+        int n = 0;
+        while (__hip_atomic_load(gdone + EX_GD_STRIDE * a, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) < DG_SEGS &&
+               ++n < EX_WAIT_LIMIT)
+            __builtin_amdgcn_s_sleep(32);
+    }
+    __syncthreads();
+    HOps ho = load_hops(hq, slot >= 0 && slot < nslot ? slot : 0, c0, l);
     // the wave reads back what its own lanes wrote: LDS keeps a wave's order
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint32_t *row = wl[wave] + ((r & 1) * 16 + l) * DD_RS + 4 * c0;
+    const uint32_t *row = wl + ((r & 1) * 16 + l) * DD_RS + 4 * c0;
     for (int ti = 0; ti < rec.z; ++ti) {
         if (ti > 0) {
             slot = slots[rec.y + ti];
@@ -325,22 +378,93 @@ __global__ __launch_bounds__(64 * DD_WAVES) void dec_down(const uint8_t *__restr
             continue;   // only a corrupt grouping gets here; uniform per wave
         float acc = down_row(row, c0, ho);
         acc += __shfl_xor(acc, 32, 64);
+        float *orow = out + (size_t)slot * H + ch * DD_ROWS;
+        if (!cb.cdone) {
+            if (lane < DD_ROWS)
+                orow[lane] = acc;
+            continue;
+        }
         if (lane < DD_ROWS)
-            out[(size_t)slot * H + ch * DD_ROWS + lane] = acc;
+            __hip_atomic_store(orow + lane, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the rows are in memory
+        const int t = slot / K;
+        int done = 0;
+        if (lane == 0)
+            done = __hip_atomic_fetch_add(cb.cdone + (size_t)t * (H / DD_ROWS) + ch, 1,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        done = __shfl(done, 0, 64);
+        if (done != K - 1)
+            continue;
+        // the last of the token's slots for these rows: combine them
+        if (lane < DD_ROWS) {
+            const int r0 = ch * DD_ROWS + lane;
+            float sum = 0.f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const float o = __hip_atomic_load(out + ((size_t)t * K + k) * H + r0, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                sum = fmaf(cb.w[(size_t)t * K + k], o, sum);
+            }
+            if (cb.y)
+                cb.y[(size_t)t * H + r0] = sum;
+            if (cb.res)
+                cb.res[(size_t)t * H + r0] += sum;
+        }
+    }
+}
+
+constexpr int EX_THREADS = 64 * DG_WAVES;
+static_assert(DD_WAVES == DG_WAVES, "gate/up and down workgroups have one shape");
+static_assert(DD_ITEMS_PER_E % DD_WAVES == 0, "a down group stays within one expert");
+constexpr int EX_DN_PER_E = DD_ITEMS_PER_E / DD_WAVES;   // 20 down groups per expert
+constexpr size_t EX_LDS_GU = (size_t)DG_ROWS * DG_RS * 4 + (size_t)DG_WAVES * DG_ROWS * 4;
+constexpr size_t EX_LDS_DN = (size_t)DD_WAVES * DD_ROWS * DD_RS * 4;
+constexpr size_t EX_LDS = EX_LDS_GU > EX_LDS_DN ? EX_LDS_GU : EX_LDS_DN;
+
+// The experts of a decode call in one launch.  Workgroup b < 40 amax runs
+// gate/up item b; workgroup 40 amax + g runs down group g (items beyond the
+// call's na active experts exit at once).  A down group waits only for its
+// expert's gate/up items.  Workgroups go to the XCDs round-robin and each XCD
+// dispatches its workgroups in index order, so every gate/up workgroup of an
+// XCD holds a slot before any down workgroup of that XCD can take one: gate/up
+// workgroups never wait behind the down ones, and the waits end.  The wait is
+// bounded all the same.
+__global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restrict__ blobs,
+                                                          const int4 *__restrict__ erec,
+                                                          const int32_t *__restrict__ slots, XQ xq,
+                                                          HQ hq, float *__restrict__ out, int T,
+                                                          Combine cb, int32_t *__restrict__ gdone)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[EX_LDS];
+    const int na = active_count(erec, T);
+    const int amax = T * K < E ? T * K : E;
+    const int b = blockIdx.x;
+    if (b < amax * DG_SEGS) {
+        if (b >= na * DG_SEGS)
+            return;
+        uint32_t *wl = reinterpret_cast<uint32_t *>(lds);
+        float(*part)[DG_ROWS] =
+            reinterpret_cast<float(*)[DG_ROWS]>(lds + (size_t)DG_ROWS * DG_RS * 4);
+        gateup_item(b, blobs, erec, slots, xq, hq, T, wl, part, gdone);
+    } else {
+        const int g = b - amax * DG_SEGS;
+        if (g >= na * EX_DN_PER_E)
+            return;
+        uint32_t *wl = reinterpret_cast<uint32_t *>(lds) +
+                       (size_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DD_ROWS * DD_RS;
+        down_group(g, blobs, erec, slots, hq, out, T, cb, wl, gdone);
     }
 }
 
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
-                                 XQ xq, HQ hq, float *out, int T, int n_cu, hipStream_t st)
+                                 XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
+                                 const float *w, float *y, float *res, hipStream_t st)
 {
+    const Combine cb{cdone, w, y, res};
     const int amax = T * K < E ? T * K : E;
-    const int g1 = amax * DG_SEGS;
-    (void)n_cu;
-    const int g2 = (amax * DD_ITEMS_PER_E + DD_WAVES - 1) / DD_WAVES;
-    hipLaunchKernelGGL(dec_gateup, dim3(g1), dim3(DG_THREADS), 0, st, blobs, erec, slots, xq, hq,
-                       T);
-    hipLaunchKernelGGL(dec_down, dim3(g2), dim3(64 * DD_WAVES), 0, st, blobs, erec, slots, hq, out,
-                       T);
+    hipLaunchKernelGGL(dec_experts, dim3(amax * (DG_SEGS + EX_DN_PER_E)), dim3(EX_THREADS), 0, st,
+                       blobs, erec, slots, xq, hq, out, T, cb, sync + 1);
     return hipGetLastError();
 }
 

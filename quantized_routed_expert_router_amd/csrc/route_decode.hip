@@ -21,7 +21,8 @@
 //              maxima -- the order (p desc, id asc) -- and the clamped renorm).
 //              Wave 0 then groups the T*10 slots by expert: counts, offsets,
 //              the active list, stable slot order and one work record per
-//              active expert for the expert kernels.
+//              active expert for the expert kernels (and, for the layer, the
+//              zeroed slot counters with which dec_down finishes the combine).
 #include "common.hpp"
 #include "quant.hpp"
 
@@ -41,12 +42,15 @@ static_assert(RG_SPAN == 64 * 8, "8 elements per lane");
 struct GroupIn {
     const int32_t *offsets, *slots, *active;
     int4 *erec;
+    int32_t *esync;   // [1+E] counters of the experts kernel, zeroed here
 };
 
 __device__ inline void build_records(const GroupIn &gi, int T, int tid0, int nthreads)
 {
     const int nslot = T * K;
     const int na = min(max(gi.active[0], 0), min(nslot, E));
+    for (int i = tid0; i <= 32 * na; i += nthreads)
+        gi.esync[i] = 0;
     for (int i = tid0; i <= na; i += nthreads) {
         if (i == 0) {
             gi.erec[0] = make_int4(na, 0, 0, 0);
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
     const float *__restrict__ lraw, const float *__restrict__ inv_rms, const float *__restrict__ bias,
     int T, int32_t *__restrict__ ids, float *__restrict__ wout, int group,
     int32_t *__restrict__ offsets, int32_t *__restrict__ slots, int32_t *__restrict__ active,
-    int4 *__restrict__ erec)
+    int4 *__restrict__ erec, int32_t *__restrict__ cdone, int32_t *__restrict__ esync)
 {
     __shared__ int sid[DECODE_T_MAX * K];   // expert of each slot
     __shared__ int cnt[E];                  // slots per expert
@@ -172,6 +176,12 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
     __shared__ int first[E];                // first slot of each expert
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = T * K;
+    if (cdone)   // the down kernel's per-(token, 32 rows) slot counters start at zero
+        for (int i = tid; i < T * (H / 32); i += RT_THREADS)
+            cdone[i] = 0;
+    if (esync)   // so do the experts kernel's per-expert counters
+        for (int i = tid; i <= 32 * E; i += RT_THREADS)
+            esync[i] = 0;
     if (group) {
         for (int i = tid; i < E; i += RT_THREADS) {
             cnt[i] = 0;
@@ -328,9 +338,10 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
                                int rmsnorm, float *lraw, XQ xq, bool prep, int32_t *ids,
                                float *w, int group, int32_t *offsets, int32_t *slots,
-                               int32_t *active, int4 *erec, hipStream_t st)
+                               int32_t *active, int4 *erec, int32_t *cdone, int32_t *esync,
+                               hipStream_t st)
 {
-    const GroupIn none{nullptr, nullptr, nullptr, nullptr};
+    const GroupIn none{nullptr, nullptr, nullptr, nullptr, nullptr};
     if (prep)
         hipLaunchKernelGGL((rdec_gemv<true, true>), dim3(E), dim3(RG_THREADS), 0, st, x, T, R,
                            lraw, xq, rmsnorm, none);
@@ -338,16 +349,16 @@ hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const f
         hipLaunchKernelGGL((rdec_gemv<true, false>), dim3(E), dim3(RG_THREADS), 0, st, x, T, R,
                            lraw, xq, rmsnorm, none);
     hipLaunchKernelGGL(rdec_topk, dim3(1), dim3(RT_THREADS), 0, st, lraw, xq.inv_rms, bias, T, ids,
-                       w, group, offsets, slots, active, erec);
+                       w, group, offsets, slots, active, erec, cdone, esync);
     return hipGetLastError();
 }
 
 hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const int32_t *offsets,
                               const int32_t *slots, const int32_t *active, int4 *erec,
-                              hipStream_t st)
+                              int32_t *esync, hipStream_t st)
 {
     const int blocks = (T * XBLK + RG_WAVES - 1) / RG_WAVES;
-    const GroupIn gi{offsets, slots, active, erec};
+    const GroupIn gi{offsets, slots, active, erec, esync};
     hipLaunchKernelGGL((rdec_gemv<false, true>), dim3(blocks), dim3(RG_THREADS), 0, st, x, T,
                        (const uint16_t *)nullptr, (float *)nullptr, xq, rmsnorm, gi);
     return hipGetLastError();
