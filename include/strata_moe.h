@@ -113,9 +113,11 @@ STRATA_API int strata_moe_group(const int32_t *ids, int T, int32_t *offsets, int
  *   blobs   [E][BLOB] bytes, one layer's store (256-byte aligned).
  *   offsets, slots, active: as written by strata_moe_group for the same T.
  *   out     [T*K][H] fp32 out, unweighted expert outputs by flat slot id.
- * Decode-sized T uses a bandwidth-bound dot-product kernel with 16-bit
- * activations per 32-value segment; larger T uses fp16 MFMA grouped GEMMs
- * with exactly dequantised weights; both accumulate in fp32. */
+ * Decode-sized T (T <= 16) uses one bandwidth-bound kernel of integer dot
+ * products: x as 16-bit integers per 64-value block and h per 16-value
+ * segment, against the exact 2-bit codes, with exact int32 block sums and
+ * fp32 across blocks; larger T uses fp16 MFMA grouped GEMMs with exactly
+ * dequantised weights and fp32 accumulation. */
 STRATA_API int strata_moe_experts(const float *x, int T, const uint8_t *blobs, const int32_t *offsets,
                        const int32_t *slots, const int32_t *active, int flags, float *out,
                        void *ws, size_t ws_bytes, void *stream);
@@ -136,6 +138,18 @@ STRATA_API int strata_moe_combine(const float *out, const float *w, int T, int f
 STRATA_API int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
                      const uint8_t *blobs, int flags, float *y, int32_t *ids, float *w,
                      void *ws, size_t ws_bytes, void *stream);
+
+/* Measurement hook (not part of the layer's math): arms the next
+ * strata_moe_experts or strata_moe_layer call made by this host thread to
+ * launch its dominant kernel with the HIP events `start` and `stop`
+ * (hipEvent_t) attached to the dispatch itself (hipExtLaunchKernel), so that
+ * hipEventElapsedTime(start, stop) is that kernel's own duration.  The kernel
+ * is, for decode-sized T, the fused experts kernel (gate/up, down and, in the
+ * layer call, the combine), and for larger T the gate/up GEMM.  The hook is
+ * used by one call and disarmed.  Events are the caller's; pass both NULL to
+ * disarm.  Returns STRATA_E_ARG if only one is NULL.  Not for use under graph
+ * capture. */
+STRATA_API int strata_moe_time_next_kernel(void *start, void *stop);
 
 /* Human-readable text of a status code (static storage). */
 STRATA_API const char *strata_moe_status_string(int status);

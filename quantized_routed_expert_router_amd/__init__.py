@@ -21,7 +21,7 @@ OK, E_ARG, E_SHAPE, E_WORKSPACE, E_HIP, E_ALIGN = 0, -1, -2, -3, -4, -5
 
 EXPORTS = ("strata_moe_blob_bytes", "strata_moe_workspace_bytes", "strata_moe_route",
            "strata_moe_group", "strata_moe_experts", "strata_moe_combine", "strata_moe_layer",
-           "strata_moe_status_string")
+           "strata_moe_time_next_kernel", "strata_moe_status_string")
 
 _lib = None
 
@@ -55,6 +55,8 @@ def lib():
         L.strata_moe_combine.argtypes = [vp, vp, i32, i32, vp, vp]
         L.strata_moe_layer.restype = i32
         L.strata_moe_layer.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.strata_moe_time_next_kernel.restype = i32
+        L.strata_moe_time_next_kernel.argtypes = [vp, vp]
         L.strata_moe_status_string.restype = ctypes.c_char_p
         L.strata_moe_status_string.argtypes = [i32]
         _lib = L
@@ -156,6 +158,19 @@ def strata_moe_combine(out, w, y, flags=0, stream=None):
     rc = lib().strata_moe_combine(_p(out, torch.float32), _p(w, torch.float32), T, flags,
                                   _p(y, torch.float32), _s(stream))
     _check("strata_moe_combine", rc)
+
+
+def strata_moe_time_next_kernel(start=None, stop=None):
+    """Arm the next experts/layer call to record two torch.cuda.Event objects
+    (enable_timing=True) around its dominant kernel; None, None disarms."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if not ev.cuda_event:
+            raise ValueError("record the event once before passing it (its HIP event is lazy)")
+        return int(ev.cuda_event)
+    rc = lib().strata_moe_time_next_kernel(handle(start), handle(stop))
+    _check("strata_moe_time_next_kernel", rc)
 
 
 def strata_moe_layer(x, router, blobs, ws, bias=None, flags=0, y=None, ids=None, w=None,

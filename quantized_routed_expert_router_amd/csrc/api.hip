@@ -24,16 +24,28 @@ hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const i
                               int32_t *esync, hipStream_t st);
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
                                  XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
-                                 const float *w, float *y, float *res, hipStream_t st);
+                                 const float *w, float *y, float *res, hipEvent_t ev0,
+                                 hipEvent_t ev1, hipStream_t st);
 hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
                                   const __half *xperm, __half *hperm, float *out, int T,
-                                  hipStream_t st);
+                                  hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
 hipError_t launch_combine(const float *out, const float *w, int T, float *y, float *res,
                           int accumulate_y, hipStream_t st);
 
 namespace {
+
+// The measurement hook's events (per host thread, used by one call).
+thread_local hipEvent_t t_ev0 = nullptr, t_ev1 = nullptr;
+
+// Take the armed hook events (or two NULLs) and disarm the hook.
+void take_events(hipEvent_t &e0, hipEvent_t &e1)
+{
+    e0 = t_ev0;
+    e1 = t_ev1;
+    t_ev0 = t_ev1 = nullptr;
+}
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -98,13 +110,15 @@ Carve carve(void *ws, int T)
 int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
                 const int32_t *slots, const int32_t *active, float *out, int T, hipStream_t st)
 {
+    hipEvent_t e0, e1;
+    take_events(e0, e1);
     if (is_decode(T)) {
         STRATA_TRY(launch_decode_experts(blobs, c.erec, slots, c.xq, c.hq, out, T, c.esync, nullptr,
-                                         nullptr, nullptr, nullptr, st));
+                                         nullptr, nullptr, nullptr, e0, e1, st));
     } else {
         STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
         STRATA_TRY(launch_prefill_experts(blobs, offsets, slots, active, c.mlist, c.nitems,
-                                          c.L.max_items, c.xperm, c.hperm, out, T, st));
+                                          c.L.max_items, c.xperm, c.hperm, out, T, e0, e1, st));
     }
     return STRATA_OK;
 }
@@ -250,14 +264,25 @@ int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
         STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, st));
     }
     const bool res = flags & STRATA_RESIDUAL;
-    if (is_decode(T)) {   // the down kernel finishes the combine
+    if (is_decode(T)) {   // the experts kernel finishes the combine
+        hipEvent_t e0, e1;
+        take_events(e0, e1);
         STRATA_TRY(launch_decode_experts(blobs, c.erec, c.slots, c.xq, c.hq, c.out, T, c.esync,
-                                         c.cdone, w_o, y, res ? x : nullptr, st));
+                                         c.cdone, w_o, y, res ? x : nullptr, e0, e1, st));
         return STRATA_OK;
     }
     if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st)))
         return rc;
     STRATA_TRY(launch_combine(c.out, w_o, T, y, res ? x : nullptr, 0, st));
+    return STRATA_OK;
+}
+
+int strata_moe_time_next_kernel(void *start, void *stop)
+{
+    if ((start == nullptr) != (stop == nullptr))
+        return STRATA_E_ARG;
+    t_ev0 = (hipEvent_t)start;
+    t_ev1 = (hipEvent_t)stop;
     return STRATA_OK;
 }
 

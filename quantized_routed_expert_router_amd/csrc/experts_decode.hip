@@ -32,6 +32,7 @@
 // depend on the other tokens of the call.
 #include "common.hpp"
 #include "quant.hpp"
+#include <hip/hip_ext.h>
 
 namespace strata {
 
@@ -459,12 +460,20 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
 
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
                                  XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
-                                 const float *w, float *y, float *res, hipStream_t st)
+                                 const float *w, float *y, float *res, hipEvent_t ev0,
+                                 hipEvent_t ev1, hipStream_t st)
 {
-    const Combine cb{cdone, w, y, res};
+    Combine cb{cdone, w, y, res};
     const int amax = T * K < E ? T * K : E;
-    hipLaunchKernelGGL(dec_experts, dim3(amax * (DG_SEGS + EX_DN_PER_E)), dim3(EX_THREADS), 0, st,
-                       blobs, erec, slots, xq, hq, out, T, cb, sync + 1);
+    int32_t *gdone = sync + 1;
+    const dim3 grid(amax * (DG_SEGS + EX_DN_PER_E)), block(EX_THREADS);
+    if (ev0) {   // timed launch: the events carry the dispatch's own start and end
+        void *args[] = {&blobs, &erec, &slots, &xq, &hq, &out, &T, &cb, &gdone};
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_experts), grid, block, args,
+                                  0, st, ev0, ev1, 0);
+    }
+    hipLaunchKernelGGL(dec_experts, grid, block, 0, st, blobs, erec, slots, xq, hq, out, T, cb,
+                       gdone);
     return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@
 // registers; down tiles hold 256 output rows.  The N-tiles of one item are
 // placed on one XCD (blockIdx % 8), so its gathered rows stay in that L2.
 #include "common.hpp"
+#include <hip/hip_ext.h>
 
 namespace strata {
 
@@ -268,11 +269,20 @@ hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
                                   const __half *xperm, __half *hperm, float *out, int T,
-                                  hipStream_t st)
+                                  hipEvent_t ev0, hipEvent_t ev1, hipStream_t st)
 {
     const int groups = (max_items + 7) / 8;
-    hipLaunchKernelGGL(pf_gateup, dim3(8 * PF_NTILES_G * groups), dim3(PF_THREADS), 0, st, blobs,
-                       offsets, slots, active, mlist, nitems, xperm, hperm, T);
+    const dim3 grid_g(8 * PF_NTILES_G * groups), block(PF_THREADS);
+    if (ev0) {   // timed launch: the events carry the dispatch's own start and end
+        void *args[] = {&blobs, &offsets, &slots, &active, &mlist, &nitems, &xperm, &hperm, &T};
+        const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&pf_gateup), grid_g,
+                                                block, args, 0, st, ev0, ev1, 0);
+        if (e != hipSuccess)
+            return e;
+    } else {
+        hipLaunchKernelGGL(pf_gateup, grid_g, block, 0, st, blobs, offsets, slots, active, mlist,
+                           nitems, xperm, hperm, T);
+    }
     hipLaunchKernelGGL(pf_down, dim3(8 * PF_NTILES_D * groups), dim3(PF_THREADS), 0, st, blobs,
                        offsets, slots, active, mlist, nitems, hperm, out, T);
     return hipGetLastError();

@@ -31,7 +31,7 @@ def m():
 
 def test_exports_every_declared_symbol(m):
     names = declared()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     assert set(names) == set(m.EXPORTS)
     for n in names:
         assert hasattr(m.lib(), n), n
@@ -70,6 +70,10 @@ def test_host_validation_rejects_before_launch(m):
     # y may be NULL only with STRATA_RESIDUAL
     assert L.strata_moe_layer(fake, 4, fake, None, fake, 0, None, None, None, fake, ws_need, None) == m.E_ARG
     assert L.strata_moe_layer(fake, 4, fake, None, fake, 3, None, None, None, fake, 0, None) == m.E_WORKSPACE
+    # the timing hook takes both events or neither (arming touches no device)
+    assert L.strata_moe_time_next_kernel(fake, None) == m.E_ARG
+    assert L.strata_moe_time_next_kernel(None, fake) == m.E_ARG
+    assert L.strata_moe_time_next_kernel(None, None) == m.OK
     for rc in (0, -1, -2, -3, -4, -5):
         assert m.strata_moe_status_string(rc) != "unknown status"
     assert m.strata_moe_status_string(-99) == "unknown status"

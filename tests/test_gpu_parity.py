@@ -144,6 +144,36 @@ def test_decode_batch_invariance():
         assert np.array_equal(y1[0], y[t]), t
 
 
+@pytest.mark.parametrize("T", [4, 64])
+def test_timing_hook_records_and_leaves_results_alone(T):
+    """strata_moe_time_next_kernel: the armed call records both events around
+    one kernel (positive elapsed time), gives bitwise the unarmed results, and
+    the hook is used up by that call."""
+    import torch
+    m = hz.qm()
+    seed = 4200 + T
+    _say(f"case: timing hook T={T}")
+    x, R, _ = hz.single_layer_case(seed, T)
+    st = hz.store(seed)
+    ids, w, y, _ = hz.gpu_layer(x, R, st)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    stale = e0.elapsed_time(e1)
+    m.strata_moe_time_next_kernel(e0, e1)
+    ids2, w2, y2, _ = hz.gpu_layer(x, R, st)
+    ms = e0.elapsed_time(e1)
+    assert ms > 0.0 and ms != stale and ms < 100.0, ms
+    assert np.array_equal(ids, ids2) and np.array_equal(w, w2) and np.array_equal(y, y2)
+    ids3, w3, y3, _ = hz.gpu_layer(x, R, st)   # disarmed: events stay where they were
+    assert e0.elapsed_time(e1) == ms
+    assert np.array_equal(y, y3)
+    with pytest.raises(ValueError):
+        m.strata_moe_time_next_kernel(torch.cuda.Event(enable_timing=True), e1)
+
+
 def test_group_matches_cpu_counting_sort():
     import torch
     m = hz.qm()
