@@ -70,64 +70,234 @@ __device__ inline int pf_pos_of_col(int c)
     return 32 * (p >> 2) + 8 * q + 2 * (p & 3) + hb;
 }
 
-// One (item, N-tile) of a grouped GEMM: acc[ns][mi] += A(64 x K) W(K x 64)
-// for the wave's four 16-column subtiles.  rowp[ns] points at this lane's
-// weight row for subtile ns; NBLK blocks of ROWB-byte rows along K.
-template <int NBLK>
-__device__ inline void pf_mainloop(const uint8_t *const rowp[4], const __half *arow,
-                                   bool arow_ok, int n_msub, __half *xa, floatx4 acc[4][4])
+// Software pipeline of one (item, N-tile), fed by direct global->LDS loads
+// (global_load_lds: the data never passes through registers).
+//  - Activations: one block (64 rows x 64 halfs, 8 KB) per K-step in a ring of
+//    four LDS buffers, requested three blocks ahead.  Rows are packed at 128
+//    bytes; the 16-byte chunk c of row m sits at position c ^ (m & 7), so the
+//    MFMA fragment reads of 16 rows hit distinct banks without padding.
+//  - Weights: gate/up in stages of 2 blocks (36 bytes of each of the 256
+//    rows, two stage buffers, requested one stage ahead); down rows are
+//    contiguous in memory and all 10 blocks (46,080 bytes) arrive at once.
+// Every LDS read of a block and its wait are one asm statement, and the
+// vector-memory waits are explicit counts that follow from the fixed issue
+// order (derived at each wait below); one barrier per block.
+constexpr int PF_ROWS = 256;                            // weight rows per WG
+constexpr int PF_ABYTES = PF_M * QK * 2;                // 8,192 bytes per activation block
+constexpr int PF_NABUF = 4;                             // activation ring
+constexpr int PF_GSROW = 2 * BB;                        // 36 bytes per gate/up row per stage
+constexpr int PF_GSTAGE = PF_ROWS * PF_GSROW;           // 9,216 bytes per gate/up stage
+constexpr int PF_GNB = PF_GSTAGE / 4 / 64 / 4;          // 9 dword loads per wave per stage
+constexpr int PF_DB = PF_ROWS * ROW_D;                  // 46,080 bytes of down rows
+constexpr int PF_DNB = PF_DB / 4 / 64 / 4;              // 45 dword loads per wave
+constexpr int PF_LDS_G = PF_NABUF * PF_ABYTES + 2 * PF_GSTAGE;   // 51,200
+constexpr int PF_LDS_D = PF_NABUF * PF_ABYTES + PF_DB;           // 78,848
+static_assert(PF_GNB * 64 * 4 * 4 == PF_GSTAGE && PF_DNB * 64 * 4 * 4 == PF_DB, "load split");
+static_assert(PF_THREADS == 256, "four waves");
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ inline uint32_t lds_addr(uint8_t *p)
 {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int q = lane >> 4;
-    const int am = tid >> 2, apart = tid & 3;   // staging: row am, 16 halfs at 16*apart
-    for (int b = 0; b < NBLK; ++b) {
-        // Weights for this block: scale and this lane's code dword per subtile.
-        uint32_t dbits[4], wc[4];
+    return (uint32_t)(uintptr_t)(lds_u8 *)p;
+}
+
+// Activation requests of block b for this wave: two 16-byte chunks per lane
+// (rows 16 w + 8 h + lane / 8, position lane % 8).
+struct PfAct {
+    const __half *row[2];   // this lane's two rows (valid memory for every lane)
+    int chunk;              // global 16-byte chunk for this lane's position
+    __device__ void request(uint8_t *abuf, int b) const
+    {
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-            const uint16_t *p16 = reinterpret_cast<const uint16_t *>(rowp[ns] + BB * b);
-            dbits[ns] = p16[0];
-            wc[ns] = (uint32_t)p16[1 + 2 * q] | ((uint32_t)p16[2 + 2 * q] << 16);
-        }
-        // Activations for this block: 64 rows x 64 halfs.
-        uint4 av0 = make_uint4(0, 0, 0, 0), av1 = av0;
-        if (arow_ok) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(arow + QK * b + 16 * apart);
-            av0 = src[0];
-            av1 = src[1];
-        }
-        __syncthreads();
-        uint4 *dst = reinterpret_cast<uint4 *>(xa + am * XA_STRIDE + 16 * apart);
-        dst[0] = av0;
-        dst[1] = av1;
-        __syncthreads();
-        half8 bf[4][2];
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-            uint32_t pr[8];
-            dequant_dword(wc[ns], dbits[ns], pr);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                uint4 v = make_uint4(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]);
-                bf[ns][j] = __builtin_bit_cast(half8, v);
-            }
-        }
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            if (mi >= n_msub)
-                break;
-            const __half *ap = xa + (16 * mi + (lane & 15)) * XA_STRIDE + 8 * q;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const half8 af = *reinterpret_cast<const half8 *>(ap + 32 * j);
-#pragma unroll
-                for (int ns = 0; ns < 4; ++ns)
-                    acc[ns][mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[ns][j],
-                                                                          acc[ns][mi], 0, 0, 0);
-            }
-        }
+        for (int h = 0; h < 2; ++h)
+            __builtin_amdgcn_global_load_lds(row[h] + QK * b + 8 * chunk,
+                                             abuf + (128 * w + 64 * h) * 16, 16, 0, 0);
     }
+};
+
+// Every LDS read of block b (the 4 activation subtiles x 2 K-halves, and for
+// each of the 4 weight subtiles its scale and this lane's code dword), then
+// the wait for them, in one statement: the compiler sees finished values.
+// AOFF: activation buffer offset; BOFF: this block's offset in the weight
+// rows; NS1..NS3: offsets of weight subtiles 1..3 from subtile 0.
+template <int AOFF, int BOFF, int NS1, int NS2, int NS3>
+__device__ inline void pf_reads(uint32_t a0, uint32_t a1, uint32_t bs, uint32_t bc, half8 af[4][2],
+                                uint32_t dbits[4], uint32_t wc[4])
+{
+    asm volatile("ds_read_b128 %0, %16 offset:%20\n\t"
+                 "ds_read_b128 %1, %17 offset:%20\n\t"
+                 "ds_read_b128 %2, %16 offset:%21\n\t"
+                 "ds_read_b128 %3, %17 offset:%21\n\t"
+                 "ds_read_b128 %4, %16 offset:%22\n\t"
+                 "ds_read_b128 %5, %17 offset:%22\n\t"
+                 "ds_read_b128 %6, %16 offset:%23\n\t"
+                 "ds_read_b128 %7, %17 offset:%23\n\t"
+                 "ds_read_u16 %8, %18 offset:%24\n\t"
+                 "ds_read_b32 %12, %19 offset:%24\n\t"
+                 "ds_read_u16 %9, %18 offset:%25\n\t"
+                 "ds_read_b32 %13, %19 offset:%25\n\t"
+                 "ds_read_u16 %10, %18 offset:%26\n\t"
+                 "ds_read_b32 %14, %19 offset:%26\n\t"
+                 "ds_read_u16 %11, %18 offset:%27\n\t"
+                 "ds_read_b32 %15, %19 offset:%27\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(af[0][0]), "=&v"(af[0][1]), "=&v"(af[1][0]), "=&v"(af[1][1]),
+                   "=&v"(af[2][0]), "=&v"(af[2][1]), "=&v"(af[3][0]), "=&v"(af[3][1]),
+                   "=&v"(dbits[0]), "=&v"(dbits[1]), "=&v"(dbits[2]), "=&v"(dbits[3]),
+                   "=&v"(wc[0]), "=&v"(wc[1]), "=&v"(wc[2]), "=&v"(wc[3])
+                 : "v"(a0), "v"(a1), "v"(bs), "v"(bc), "i"(AOFF), "i"(AOFF + 2048),
+                   "i"(AOFF + 4096), "i"(AOFF + 6144), "i"(BOFF), "i"(BOFF + NS1),
+                   "i"(BOFF + NS2), "i"(BOFF + NS3)
+                 : "memory");
+}
+
+// acc[ns][mi] += A(64 x 64) W(64 x 64) from the values read for one block:
+// the four weight subtiles are dequantised first, then the 32 MFMAs run in
+// an order where one accumulator recurs only every 16 instructions.
+__device__ inline void pf_math(const half8 af[4][2], const uint32_t dbits[4], const uint32_t wc[4],
+                               floatx4 acc[4][4])
+{
+    half8 bf[4][2];
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+        uint32_t pr[8];
+        dequant_dword(wc[ns], dbits[ns], pr);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            bf[ns][j] = __builtin_bit_cast(
+                half8, make_uint4(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                acc[ns][mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mi][j], bf[ns][j], acc[ns][mi],
+                                                                      0, 0, 0);
+#ifdef PF_INTERLEAVE
+    // scheduler hint: one MFMA, then up to three VALU, repeated
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#endif
+}
+
+template <int N> __device__ inline void vm_wait()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// Per-lane LDS read addresses of the activation fragments (K-halves j = 0, 1)
+// of row 16 mi + lane % 16, position (lane / 16 + 4 j) ^ (lane % 8).
+__device__ inline void pf_act_read_addrs(uint32_t abase, uint32_t &a0, uint32_t &a1)
+{
+    const int lane = threadIdx.x & 63, q = lane >> 4;
+    a0 = abase + (lane & 15) * 128 + 16 * (q ^ (lane & 7));
+    a1 = abase + (lane & 15) * 128 + 16 * ((q + 4) ^ (lane & 7));
+}
+
+// Gate/up K loop: 40 blocks, weight stage s = blocks 2 s, 2 s + 1.
+// Issue order: prologue A0, W0, A1, A2; iteration b (after its barrier):
+// W(b/2 + 1) if b is even, then A(b + 3) (past the end: the last block or
+// stage again, never read).  At the top of iteration b, the loads younger
+// than W(s = b/2) are A(b+1), A(b+2) (4 lane-loads) when b is even; when b
+// is odd the oldest needed is A(b) and younger are A(b+1), W(s+1), A(b+2):
+// 2 + 9 + 2 = 13.
+__device__ inline void pf_gateup_loop(const uint8_t *blob, const uint32_t goff[PF_GNB],
+                                      const PfAct &act, uint8_t *lds, uint32_t bs, uint32_t bc,
+                                      floatx4 acc[4][4])
+{
+    uint8_t *const wbuf = lds + PF_NABUF * PF_ABYTES;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // stage src into stage buffer par
+    auto wreq = [&](int src, int par) {
+#pragma unroll
+        for (int h = 0; h < PF_GNB; ++h)
+            __builtin_amdgcn_global_load_lds(blob + goff[h] + PF_GSROW * src,
+                                             wbuf + par * PF_GSTAGE + (PF_GNB * 64 * w + 64 * h) * 4,
+                                             4, 0, 0);
+    };
+    constexpr int NST = NB_G / 2;
+    uint32_t a0, a1;
+    pf_act_read_addrs(lds_addr(lds), a0, a1);
+    act.request(lds, 0);
+    wreq(0, 0);
+    act.request(lds + PF_ABYTES, 1);
+    act.request(lds + 2 * PF_ABYTES, 2);
+    constexpr int NS1 = 16 * PF_GSROW, NS2 = 128 * PF_GSROW, NS3 = 144 * PF_GSROW;
+#define STRATA_PF_STEP(R)                                                                          \
+    {                                                                                              \
+        const int b = b0 + (R);                                                                    \
+        vm_wait<((R) & 1) ? 13 : 4>();                                                             \
+        __builtin_amdgcn_s_barrier();                                                              \
+        if (!((R) & 1)) {                                                                          \
+            const int s1 = b / 2 + 1;                                                              \
+            wreq(s1 < NST ? s1 : NST - 1, (((R) >> 1) + 1) & 1);                                   \
+        }                                                                                          \
+        act.request(lds + (((R) + 3) & 3) * PF_ABYTES, b + 3 < NB_G ? b + 3 : NB_G - 1);           \
+        half8 af[4][2];                                                                            \
+        uint32_t dbits[4], wc[4];                                                                  \
+        pf_reads<(R) * PF_ABYTES, ((R) >> 1) * PF_GSTAGE + BB * ((R) & 1), NS1, NS2, NS3>(          \
+            a0, a1, bs, bc, af, dbits, wc);                                                        \
+        pf_math(af, dbits, wc, acc);                                                               \
+    }
+#pragma unroll 1
+    for (int b0 = 0; b0 < NB_G; b0 += 4) {
+        STRATA_PF_STEP(0)
+        STRATA_PF_STEP(1)
+        STRATA_PF_STEP(2)
+        STRATA_PF_STEP(3)
+    }
+#undef STRATA_PF_STEP
+    vm_wait<0>();   // the trailing requests land before the LDS is released
+}
+
+// Down K loop: 10 blocks; all weights requested first.  Issue order: W, A0,
+// A1, A2; iteration b (after its barrier): A(b + 3) (clamped).  At the top of
+// iteration b the loads younger than A(b) are A(b+1), A(b+2): 4.
+__device__ inline void pf_down_loop(const uint8_t *wsrc, const PfAct &act, uint8_t *lds,
+                                    uint32_t bs, uint32_t bc, floatx4 acc[4][4])
+{
+    uint8_t *const wbuf = lds + PF_NABUF * PF_ABYTES;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int h = 0; h < PF_DNB; ++h)
+        __builtin_amdgcn_global_load_lds(wsrc + 4 * (PF_DNB * 64 * w + 64 * h + lane),
+                                         wbuf + (PF_DNB * 64 * w + 64 * h) * 4, 4, 0, 0);
+    uint32_t a0, a1;
+    pf_act_read_addrs(lds_addr(lds), a0, a1);
+    act.request(lds, 0);
+    act.request(lds + PF_ABYTES, 1);
+    act.request(lds + 2 * PF_ABYTES, 2);
+    constexpr int NS1 = 16 * ROW_D, NS2 = 32 * ROW_D, NS3 = 48 * ROW_D;
+#define STRATA_PF_DSTEP(B)                                                                         \
+    {                                                                                              \
+        vm_wait<4>();                                                                              \
+        __builtin_amdgcn_s_barrier();                                                              \
+        act.request(lds + (((B) + 3) & 3) * PF_ABYTES, (B) + 3 < NB_D ? (B) + 3 : NB_D - 1);       \
+        half8 af[4][2];                                                                            \
+        uint32_t dbits[4], wc[4];                                                                  \
+        pf_reads<((B) & 3) * PF_ABYTES, BB * (B), NS1, NS2, NS3>(a0, a1, bs, bc, af, dbits, wc);   \
+        pf_math(af, dbits, wc, acc);                                                               \
+    }
+    STRATA_PF_DSTEP(0)
+    STRATA_PF_DSTEP(1)
+    STRATA_PF_DSTEP(2)
+    STRATA_PF_DSTEP(3)
+    STRATA_PF_DSTEP(4)
+    STRATA_PF_DSTEP(5)
+    STRATA_PF_DSTEP(6)
+    STRATA_PF_DSTEP(7)
+    STRATA_PF_DSTEP(8)
+    STRATA_PF_DSTEP(9)
+#undef STRATA_PF_DSTEP
+    vm_wait<0>();
 }
 
 struct PfItem {
@@ -159,13 +329,13 @@ __device__ inline PfItem pf_item(int item, const int32_t *mlist, const int32_t *
     return it;
 }
 
-__global__ __launch_bounds__(PF_THREADS) void pf_gateup(
+__global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
     const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ slots, const int32_t *__restrict__ active,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
     const __half *__restrict__ xperm, __half *__restrict__ hperm, int T)
 {
-    __shared__ __attribute__((aligned(16))) __half xa[PF_M * XA_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[PF_LDS_G];
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int item = 8 * (idx / PF_NTILES_G) + xcd;
     const int nt = idx % PF_NTILES_G;
@@ -175,27 +345,35 @@ __global__ __launch_bounds__(PF_THREADS) void pf_gateup(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int jw = nt * PF_NT_G + 32 * wave;   // this wave's first FF row
     const uint8_t *blob = blobs + (size_t)it.e * BLOB;
-    const uint8_t *rowp[4];
+    // Activation rows this lane requests (rows past the item's end read its
+    // first row; their results are never stored).
+    PfAct act;
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns)
-        rowp[ns] = blob + (ns >= 2 ? MAT : 0) + (size_t)(jw + 16 * (ns & 1) + (lane & 15)) * ROW_G;
-    // Staged activation row of this thread.
-    const int am = tid >> 2;
-    const bool aok = am < it.rows;
-    int at = 0;
-    if (aok) {
-        const int s = slots[it.gp0 + am];
-        at = (s >= 0 && s < T * K) ? s / K : 0;
+    for (int h = 0; h < 2; ++h) {
+        const int r = 16 * wave + 8 * h + (lane >> 3);
+        const int sl = slots[it.gp0 + (r < it.rows ? r : 0)];
+        const int t = (sl >= 0 && sl < T * K) ? sl / K : 0;
+        act.row[h] = xperm + (size_t)t * H;
     }
-    const __half *arow = xperm + (size_t)at * H;
-    const int n_msub = (it.rows + 15) >> 4;
+    act.chunk = (lane & 7) ^ (lane >> 3);
+    // Weight requests: lane-load h of a stage is stage dword p = 576 w + 64 h
+    // + lane = row p / 9, dword p % 9 (rows 0..127 gate, 128..255 up).
+    uint32_t goff[PF_GNB];
+#pragma unroll
+    for (int h = 0; h < PF_GNB; ++h) {
+        const int p = PF_GNB * 64 * wave + 64 * h + lane;
+        const int n = p / 9, k = p % 9;
+        goff[h] = (uint32_t)((n >= 128 ? MAT : 0) + (size_t)(nt * PF_NT_G + (n & 127)) * ROW_G + 4 * k);
+    }
+    const uint32_t bs = lds_addr(lds + PF_NABUF * PF_ABYTES) + (32 * wave + (lane & 15)) * PF_GSROW;
+    const uint32_t bc = bs + 2 + 4 * (lane >> 4);
     floatx4 acc[4][4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
             acc[ns][mi] = (floatx4){0.f, 0.f, 0.f, 0.f};
-    pf_mainloop<NB_G>(rowp, arow, aok, n_msub, xa, acc);
+    pf_gateup_loop(blob, goff, act, lds, bs, bc, acc);
     // Epilogue: h = silu(g) * u for FF rows jw + 16 h2 + lane%16.
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -217,13 +395,13 @@ __global__ __launch_bounds__(PF_THREADS) void pf_gateup(
     }
 }
 
-__global__ __launch_bounds__(PF_THREADS) void pf_down(
+__global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
     const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ slots, const int32_t *__restrict__ active,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
     const __half *__restrict__ hperm, float *__restrict__ out, int T)
 {
-    __shared__ __attribute__((aligned(16))) __half xa[PF_M * XA_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[PF_LDS_D];
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int item = 8 * (idx / PF_NTILES_D) + xcd;
     const int nt = idx % PF_NTILES_D;
@@ -232,22 +410,23 @@ __global__ __launch_bounds__(PF_THREADS) void pf_down(
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rw = nt * PF_NT_D + 64 * wave;   // this wave's first output row
-    const uint8_t *dmat = blobs + (size_t)it.e * BLOB + 2 * MAT;
-    const uint8_t *rowp[4];
+    PfAct act;
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns)
-        rowp[ns] = dmat + (size_t)(rw + 16 * ns + (lane & 15)) * ROW_D;
-    const int am = tid >> 2;
-    const bool aok = am < it.rows;
-    const __half *arow = hperm + (size_t)(it.gp0 + (aok ? am : 0)) * FF;
-    const int n_msub = (it.rows + 15) >> 4;
+    for (int h = 0; h < 2; ++h) {
+        const int r = 16 * wave + 8 * h + (lane >> 3);
+        act.row[h] = hperm + (size_t)(it.gp0 + (r < it.rows ? r : 0)) * FF;
+    }
+    act.chunk = (lane & 7) ^ (lane >> 3);
+    const uint8_t *wsrc = blobs + (size_t)it.e * BLOB + 2 * MAT + (size_t)nt * PF_DB;
+    const uint32_t bs = lds_addr(lds + PF_NABUF * PF_ABYTES) + (64 * wave + (lane & 15)) * ROW_D;
+    const uint32_t bc = bs + 2 + 4 * (lane >> 4);
     floatx4 acc[4][4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
             acc[ns][mi] = (floatx4){0.f, 0.f, 0.f, 0.f};
-    pf_mainloop<NB_D>(rowp, arow, aok, n_msub, xa, acc);
+    pf_down_loop(wsrc, act, lds, bs, bc, acc);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
