@@ -5,9 +5,9 @@
 #include "quant.hpp"
 
 namespace strata {
-hipError_t launch_prep(const float *x, int T, int rmsnorm, float *xhat, __half *xperm,
+hipError_t launch_prep(const float *x, int T, int rmsnorm, uint16_t *xsplit, __half *xperm,
                        hipStream_t st);
-hipError_t launch_logits(const float *xhat, int T, const uint16_t *R, const float *bias,
+hipError_t launch_logits(const uint16_t *xsplit, int T, const uint16_t *R, const float *bias,
                          float *logits, hipStream_t st);
 hipError_t launch_topk(const float *logits, int T, int32_t *ids, float *w, hipStream_t st);
 hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
@@ -64,7 +64,8 @@ template <class P> P *at(void *ws, size_t off) { return reinterpret_cast<P *>((u
 
 struct Carve {
     Ws L;
-    float *xhat, *logits, *w, *out;
+    uint16_t *xsplit;
+    float *logits, *w, *out;
     __half *xperm, *hperm;
     XQ xq;
     HQ hq;
@@ -78,7 +79,7 @@ Carve carve(void *ws, int T)
     Carve c;
     c.L = ws_layout(T);
     const Ws &L = c.L;
-    c.xhat = at<float>(ws, L.xhat);
+    c.xsplit = at<uint16_t>(ws, L.xsplit);
     c.xperm = at<__half>(ws, L.xperm);
     c.logits = at<float>(ws, L.logits);
     c.xq = XQ{at<uint32_t>(ws, L.xq_dig), at<float>(ws, L.xq_scale), at<int32_t>(ws, L.xq_sum),
@@ -132,7 +133,7 @@ int run_prep(const Carve &c, const float *x, int T, int rms, const int32_t *offs
     if (is_decode(T))
         STRATA_TRY(launch_prep_decode(x, T, rms, c.xq, offsets, slots, active, c.erec, c.esync, st));
     else
-        STRATA_TRY(launch_prep(x, T, rms, c.xhat, c.xperm, st));
+        STRATA_TRY(launch_prep(x, T, rms, nullptr, c.xperm, st));
     return STRATA_OK;
 }
 
@@ -172,8 +173,8 @@ int strata_moe_route(const float *x, int T, const uint16_t *router, const float 
         STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, false, ids, w, 0,
                                        nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st));
     } else {
-        STRATA_TRY(launch_prep(x, T, rms, c.xhat, nullptr, st));
-        STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
+        STRATA_TRY(launch_prep(x, T, rms, c.xsplit, nullptr, st));
+        STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
         STRATA_TRY(launch_topk(c.logits, T, ids, w, st));
     }
     return STRATA_OK;
@@ -258,8 +259,8 @@ int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
                                        c.offsets, c.slots, c.active, c.erec, c.cdone, c.esync,
                                        st));
     } else {
-        STRATA_TRY(launch_prep(x, T, rms, c.xhat, c.xperm, st));
-        STRATA_TRY(launch_logits(c.xhat, T, router, bias, c.logits, st));
+        STRATA_TRY(launch_prep(x, T, rms, c.xsplit, c.xperm, st));
+        STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
         STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
         STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, st));
     }

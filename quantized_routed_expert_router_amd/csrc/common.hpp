@@ -40,7 +40,7 @@ constexpr int PF_NTILES_D = H / PF_NT_D;       // 10
 // Workspace regions (byte offsets, 256-aligned) for a call with T tokens;
 // Td = T on the decode path (T <= DECODE_T_MAX) else 0, Tp the converse.
 struct Ws {
-    size_t xhat;       // f32 [Tp][H]        router input (prefill)
+    size_t xsplit;     // bf16 [Tp][3][H]    router input (prefill): x = x1 + x2 + x3 exactly
     size_t xperm;      // f16 [Tp][H]        MFMA-ordered activations (prefill)
     size_t logits;     // f32 [T][E]         logits (prefill) / raw logits (decode)
     size_t inv_rms;    // f32 [Td]
@@ -84,7 +84,7 @@ inline Ws ws_layout(int T)
         return at;
     };
     const size_t nb = H / QK, ns = FF / 16;
-    L.xhat = take(Tp * H * 4);
+    L.xsplit = take(Tp * 3 * H * 2);
     L.xperm = take(Tp * H * 2);
     L.logits = take((size_t)T * E * 4);
     L.inv_rms = take(Td * 4);

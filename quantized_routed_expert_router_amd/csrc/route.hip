@@ -6,11 +6,11 @@
 //
 // Kernels:
 //  prep_kernel    one workgroup per token: optional RMSNorm (eps 1e-6, unit
-//                 gain), xhat in fp32 for the router and fp16 xhat in the K
-//                 order the prefill MFMA kernels consume.  (Decode-sized T
+//                 gain), xhat as three bf16 terms for the router and fp16
+//                 xhat in the K order the prefill MFMA kernels consume.  (Decode-sized T
 //                 uses route_decode.hip.)
-//  gemm_kernel    64 x 64 fp32 tiles through LDS; each logit is a sequential
-//                 k = 0..2559 FMA chain, so identical router rows give
+//  gemm_kernel    bf16 MFMA over the exact three-term bf16 split of xhat
+//                 (fp32-accurate logits); identical router rows give
 //                 identical logits.
 //  topk_kernel    one wave per token: softmax in fp32, ten rounds of a
 //                 wave-wide max of p and min of the id among the maxima
@@ -29,8 +29,14 @@ __device__ inline int pf_col_of_pos(int pi)
 
 constexpr int PREP_THREADS = 256;
 
+// bf16 bits of v, round to nearest even (finite inputs)
+__device__ inline uint16_t bf16_rn_bits(float v)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
 __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
-    const float *__restrict__ x, int rmsnorm, float *__restrict__ xhat,
+    const float *__restrict__ x, int rmsnorm, uint16_t *__restrict__ xsplit,
     __half *__restrict__ xperm)
 {
     __shared__ float xs[H];
@@ -57,8 +63,19 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
 #pragma unroll
     for (int i = 0; i < H / PREP_THREADS; ++i) {
         const float h = v[i] * inv;
-        xs[tid + PREP_THREADS * i] = h;
-        xhat[(size_t)t * H + tid + PREP_THREADS * i] = h;
+        const int c = tid + PREP_THREADS * i;
+        xs[c] = h;
+        // the router's exact three-term bf16 split of xhat
+        const uint16_t b1 = bf16_rn_bits(h);
+        const float r1 = h - bf16_bits_to_float(b1);   // exact
+        const uint16_t b2 = bf16_rn_bits(r1);
+        const float r2 = r1 - bf16_bits_to_float(b2);  // exact
+        if (xsplit) {
+            uint16_t *xo = xsplit + (size_t)t * 3 * H + c;
+            xo[0] = b1;
+            xo[H] = b2;
+            xo[2 * H] = bf16_rn_bits(r2);
+        }
     }
     __syncthreads();
     if (xperm) {
@@ -70,70 +87,87 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
 }
 
 // ---------------------------------------------------------------- router GEMM
-constexpr int GM_TILE = 64;
-constexpr int GM_KC = 32;
+// logits = xhat . R^T on the bf16 matrix cores.  R is bf16 already; the prep
+// kernel splits each fp32 xhat value exactly into three bf16 terms
+// x1 + x2 + x3 (x1 = bf16(x), x2 = bf16(x - x1), x3 = bf16(x - x1 - x2):
+// together all 24 bits of the fp32 significand), and bf16 x bf16 products are
+// exact in the fp32 accumulation, so the logits keep fp32 accuracy.  Every
+// logit is the same sequence of MFMAs over K, so identical router rows give
+// identical logits.  Workgroup: 16 tokens x 128 experts, wave w owns experts
+// 32 w .. 32 w + 31 (two 16-expert subtiles); K in steps of 32, the operands
+// of four steps in flight.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+constexpr int GR_M = 16, GR_N = 128, GR_KS = 32, GR_STEPS = H / GR_KS;
+static_assert(GR_STEPS % 4 == 0 && E % GR_N == 0, "router GEMM tiling");
+
+struct GrOps {
+    uint4 a[3];   // x1, x2, x3: 8 bf16 of row lane % 16 at K 8 (lane / 16) ..
+    uint4 b[2];   // 8 bf16 router values per expert subtile
+};
+
+__device__ inline void gr_load(GrOps &o, const uint16_t *xa, const uint16_t *rb0, const uint16_t *rb1,
+                               int step)
+{
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        o.a[j] = *reinterpret_cast<const uint4 *>(xa + (size_t)j * H + GR_KS * step);
+    o.b[0] = *reinterpret_cast<const uint4 *>(rb0 + GR_KS * step);
+    o.b[1] = *reinterpret_cast<const uint4 *>(rb1 + GR_KS * step);
+}
+
+__device__ inline void gr_step(const GrOps &o, floatx4 acc[2])
+{
+    const bf16x8 b0 = __builtin_bit_cast(bf16x8, o.b[0]);
+    const bf16x8 b1 = __builtin_bit_cast(bf16x8, o.b[1]);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const bf16x8 xj = __builtin_bit_cast(bf16x8, o.a[j]);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xj, b0, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xj, b1, acc[1], 0, 0, 0);
+    }
+}
 
 __global__ __launch_bounds__(256) void gemm_kernel(
-    const float *__restrict__ xhat, int T, const uint16_t *__restrict__ R,
+    const uint16_t *__restrict__ xsplit, int T, const uint16_t *__restrict__ R,
     const float *__restrict__ bias, float *__restrict__ logits)
 {
-    __shared__ float xs[GM_KC][GM_TILE + 4];
-    __shared__ float rs[GM_KC][GM_TILE + 4];
-    const int tid = threadIdx.x;
-    const int m0 = blockIdx.x * GM_TILE;
-    const int n0 = blockIdx.y * GM_TILE;
-    const int ty = tid >> 4, tx = tid & 15;
-    const int lrow = tid >> 2, lk = (tid & 3) * 8;
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < H; k0 += GM_KC) {
-        const int m = m0 + lrow;
-        float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-        if (m < T) {
-            const float4 *src = reinterpret_cast<const float4 *>(xhat + (size_t)m * H + k0 + lk);
-            a0 = src[0];
-            a1 = src[1];
-        }
-        const uint4 rq = *reinterpret_cast<const uint4 *>(R + (size_t)(n0 + lrow) * H + k0 + lk);
-        __syncthreads();
-        xs[lk + 0][lrow] = a0.x;
-        xs[lk + 1][lrow] = a0.y;
-        xs[lk + 2][lrow] = a0.z;
-        xs[lk + 3][lrow] = a0.w;
-        xs[lk + 4][lrow] = a1.x;
-        xs[lk + 5][lrow] = a1.y;
-        xs[lk + 6][lrow] = a1.z;
-        xs[lk + 7][lrow] = a1.w;
-        const uint32_t u[4] = {rq.x, rq.y, rq.z, rq.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            rs[lk + 2 * j][lrow] = bf16_bits_to_float(u[j]);
-            rs[lk + 2 * j + 1][lrow] = bf16_bits_to_float(u[j] >> 16);
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int kk = 0; kk < GM_KC; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = xs[kk][ty + 16 * i];
-                b[i] = rs[kk][tx + 16 * i];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-        }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l = lane & 15, q = lane >> 4;
+    const int m0 = blockIdx.x * GR_M;
+    const int n0 = blockIdx.y * GR_N + 32 * wave;
+    const int m = min(m0 + l, T - 1);   // rows past T compute a copy and are not stored
+    const uint16_t *xa = xsplit + (size_t)m * 3 * H + 8 * q;
+    const uint16_t *rb0 = R + (size_t)(n0 + l) * H + 8 * q;
+    const uint16_t *rb1 = rb0 + (size_t)16 * H;
+    floatx4 acc[2] = {(floatx4){0.f, 0.f, 0.f, 0.f}, (floatx4){0.f, 0.f, 0.f, 0.f}};
+    GrOps p0, p1, p2, p3;
+    gr_load(p0, xa, rb0, rb1, 0);
+    gr_load(p1, xa, rb0, rb1, 1);
+    gr_load(p2, xa, rb0, rb1, 2);
+    gr_load(p3, xa, rb0, rb1, 3);
+    // the last four loads re-read the last step (never used), so every
+    // iteration issues the same loads
+#pragma unroll 1
+    for (int s = 0; s < GR_STEPS; s += 4) {
+        gr_step(p0, acc);
+        gr_load(p0, xa, rb0, rb1, min(s + 4, GR_STEPS - 1));
+        gr_step(p1, acc);
+        gr_load(p1, xa, rb0, rb1, min(s + 5, GR_STEPS - 1));
+        gr_step(p2, acc);
+        gr_load(p2, xa, rb0, rb1, min(s + 6, GR_STEPS - 1));
+        gr_step(p3, acc);
+        gr_load(p3, xa, rb0, rb1, min(s + 7, GR_STEPS - 1));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + ty + 16 * i;
-        if (m >= T)
-            continue;
+    for (int ns = 0; ns < 2; ++ns) {
+        const int n = n0 + 16 * ns + l;
+        const float bn = bias ? bias[n] : 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + tx + 16 * j;
-            logits[(size_t)m * E + n] = acc[i][j] + (bias ? bias[n] : 0.f);
+        for (int r = 0; r < 4; ++r) {
+            const int mr = m0 + 4 * q + r;
+            if (mr < T)
+                logits[(size_t)mr * E + n] = acc[ns][r] + bn;
         }
     }
 }
@@ -203,18 +237,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     }
 }
 
-hipError_t launch_prep(const float *x, int T, int rmsnorm, float *xhat, __half *xperm,
+hipError_t launch_prep(const float *x, int T, int rmsnorm, uint16_t *xsplit, __half *xperm,
                        hipStream_t st)
 {
-    hipLaunchKernelGGL(prep_kernel, dim3(T), dim3(PREP_THREADS), 0, st, x, rmsnorm, xhat, xperm);
+    hipLaunchKernelGGL(prep_kernel, dim3(T), dim3(PREP_THREADS), 0, st, x, rmsnorm, xsplit, xperm);
     return hipGetLastError();
 }
 
-hipError_t launch_logits(const float *xhat, int T, const uint16_t *R, const float *bias,
+hipError_t launch_logits(const uint16_t *xsplit, int T, const uint16_t *R, const float *bias,
                          float *logits, hipStream_t st)
 {
-    hipLaunchKernelGGL(gemm_kernel, dim3((T + GM_TILE - 1) / GM_TILE, E / GM_TILE), dim3(256), 0,
-                       st, xhat, T, R, bias, logits);
+    hipLaunchKernelGGL(gemm_kernel, dim3((T + GR_M - 1) / GR_M, E / GR_N), dim3(256), 0, st,
+                       xsplit, T, R, bias, logits);
     return hipGetLastError();
 }
 
