@@ -17,6 +17,7 @@ namespace strata {
 
 constexpr int GR_THREADS = 1024;
 constexpr int GR_WAVES = GR_THREADS / 64;
+constexpr int GR_BATCH = 8;   // 64-slot steps whose ids are loaded together
 
 __device__ inline int block_exclusive_scan_512(int v, int tid, int *tmp, int *total)
 {
@@ -64,10 +65,19 @@ __global__ __launch_bounds__(GR_THREADS) void group_kernel(const int32_t *__rest
     for (int i = tid; i < GR_WAVES * E; i += GR_THREADS)
         (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int i = beg + lane; i < end; i += 64) {
-        const int e = ids[i];
-        if (e >= 0 && e < E)
-            atomicAdd(&hist[wave][e], 1);
+    // the ids are read eight 64-slot steps at a time, so their loads overlap
+    const int steps = (S + 63) / 64;
+    for (int it0 = 0; it0 < steps; it0 += GR_BATCH) {
+        int ev[GR_BATCH];
+#pragma unroll
+        for (int j = 0; j < GR_BATCH; ++j) {
+            const int i = beg + (it0 + j) * 64 + lane;
+            ev[j] = i < end ? ids[i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < GR_BATCH; ++j)
+            if (ev[j] >= 0 && ev[j] < E)
+                atomicAdd(&hist[wave][ev[j]], 1);
     }
     __syncthreads();
     // Per expert: each wave's start within the expert, and the expert total.
@@ -97,33 +107,36 @@ __global__ __launch_bounds__(GR_THREADS) void group_kernel(const int32_t *__rest
         active[0] = tot;
     __syncthreads();
 
-    // Stable scatter: every wave takes the same number of 64-slot steps.
-    const int steps = (S + 63) / 64;
+    // Stable scatter: each wave walks its slice in order; a wave's cursors
+    // (hist[wave]) are its own, and LDS keeps one wave's accesses in order.
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
-    for (int it = 0; it < steps; ++it) {
-        const int i = beg + it * 64 + lane;
-        int e = -1;
-        if (i < end) {
-            e = ids[i];
-            if (e < 0 || e >= E)
-                e = -1;
-        }
-        unsigned long long same = __ballot(e >= 0);
-        if (e < 0)
-            same = 0;
+    for (int it0 = 0; it0 < steps; it0 += GR_BATCH) {
+        int ev[GR_BATCH];
 #pragma unroll
-        for (int b = 0; b < 9; ++b) {
-            const unsigned long long bits = __ballot(e >= 0 && ((e >> b) & 1));
-            same &= ((e >> b) & 1) ? bits : ~bits;
+        for (int j = 0; j < GR_BATCH; ++j) {
+            const int i = beg + (it0 + j) * 64 + lane;
+            ev[j] = i < end ? ids[i] : -1;
         }
-        if (e >= 0) {
-            const int rank = __popcll(same & lt_mask);
-            const int cur = hist[wave][e];
-            slots[cur + rank] = i;
-            if ((same >> lane) == 1ull)   // highest lane of its group
-                hist[wave][e] = cur + __popcll(same);
+#pragma unroll
+        for (int j = 0; j < GR_BATCH; ++j) {
+            const int i = beg + (it0 + j) * 64 + lane;
+            const int e = (ev[j] >= 0 && ev[j] < E) ? ev[j] : -1;
+            unsigned long long same = __ballot(e >= 0);
+            if (e < 0)
+                same = 0;
+#pragma unroll
+            for (int b = 0; b < 9; ++b) {
+                const unsigned long long bits = __ballot(e >= 0 && ((e >> b) & 1));
+                same &= ((e >> b) & 1) ? bits : ~bits;
+            }
+            if (e >= 0) {
+                const int rank = __popcll(same & lt_mask);
+                const int cur = hist[wave][e];
+                slots[cur + rank] = i;
+                if ((same >> lane) == 1ull)   // highest lane of its group
+                    hist[wave][e] = cur + __popcll(same);
+            }
         }
-        __syncthreads();
     }
 }
 
