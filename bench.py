@@ -40,6 +40,38 @@ WORKLOADS = {
 }
 
 
+# HBM traffic of the dominant kernel from committed rocprofv3 counter
+# summaries (profiles/<kernel>_traffic_<workload>.txt): used only while the
+# kernel sources still hash to the value recorded there.
+TRAFFIC = {
+    ("dec_experts", "window"): ("T4_window", ["experts_decode.hip", "quant.hpp", "common.hpp"]),
+    ("pf_gateup", "prefill"): ("T2048_prefill", ["experts_prefill.hip", "common.hpp"]),
+}
+
+
+def traffic_from_profile(kernel, workload):
+    import hashlib
+    key = TRAFFIC.get((kernel, workload))
+    if key is None:
+        return None
+    tag, files = key
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic_{tag}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "quantized_routed_expert_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256") != h.hexdigest() or "hbm_bytes_per_launch" not in fields:
+        return None
+    return float(fields["hbm_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,8 +246,12 @@ def main():
         roof = {"bound": "hbm", "achieved": k_work / (k_ms / 1e3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
     roof["kernel"] = "pf_gateup" if prefill else "dec_experts"
+    # HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or null
+    roof["traffic"] = traffic_from_profile(roof["kernel"], a.workload)
+    if roof["traffic"] is not None and not prefill:
+        roof["traffic_per_algorithmic_byte"] = roof["traffic"] / k_work
+    roof["traffic_unit"] = "bytes per launch"
     roof["ms_per_launch"] = k_ms
     roof["launches"] = len(evs)
     roof["work_per_launch"] = (f"{float(np.mean(units)):.1f} slots x {per_unit} flops" if prefill
