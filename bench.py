@@ -10,9 +10,11 @@ and the combine.  The working set of one layer (~54 MB) would sit in the
 the layer's store (and router) at distinct HBM addresses; every step reads
 cold memory and computes the same result.
 
-Other workloads (--workload): token (T = 1 layer), stack-decode (48-layer
-T = 1 stack on the full 34 GB store), prefill (T = 2048 layer), stack-prefill
-(one 2048-token chunk through 48 Zipf-biased layers).
+Other workloads (--workload): token (T = 1 layer), window-corr (a T = 4
+verify window of correlated tokens whose distinct experts average 3.05 times
+one token's), stack-decode (48-layer T = 1 stack on the full 34 GB store),
+prefill (T = 2048 layer), stack-prefill (one 2048-token chunk through 48
+Zipf-biased layers).
 
 Prints one JSON line.  With --gpus > 1 it exits: this build measures one GPU.
 """
@@ -33,6 +35,7 @@ FLOP_PER_SLOT = 3 * 2 * 2560 * 640
 
 WORKLOADS = {
     "window": dict(cfg=1, T=4, layers=1, copies=48),
+    "window-corr": dict(cfg=5, T=4, layers=1, copies=48),
     "token": dict(cfg=0, T=1, layers=1, copies=48),
     "stack-decode": dict(cfg=2, T=1, layers=48, copies=1),
     "prefill": dict(cfg=3, T=2048, layers=1, copies=4),
@@ -111,7 +114,7 @@ def main():
     stack = L > 1
     flags = (m.RMSNORM | m.RESIDUAL) if stack else 0
     st = inputs.Streams(seed)
-    x = inputs.draw_x(st.x, T)
+    x = inputs.draw_window(st.x, T) if cfg.get("window") else inputs.draw_x(st.x, T)
     routers = [inputs.draw_router(st.router) for _ in range(L)]
     biases = [inputs.draw_zipf_bias(st.bias) for _ in range(L)] if cfg["zipf"] else None
     blob = inputs.blob_bytes()

@@ -112,6 +112,23 @@ def draw_x(rng, T, h=H):
     return rng.standard_normal((T, h)).astype(np.float32)
 
 
+# Correlated verify windows: token t of a window of T tokens is
+# x_t = c u + sqrt(1 - c^2) z_t with u, z_t ~ N(0, I) (so every x_t is N(0, I)
+# like the other workloads' tokens).  c per window size was chosen by
+# simulation with the router recipe below and top-10 routing so that a
+# window's distinct experts average 1.75, 2.4 and 3.05 times one token's 10
+# for T = 2, 3, 4 -- the multiples "Strata in the source..." quotes in "The
+# plan: three destinations per expert".
+WINDOW_CORR = {2: 0.79, 3: 0.78, 4: 0.75}
+
+
+def draw_window(rng, T, h=H):
+    c = WINDOW_CORR[T]
+    u = rng.standard_normal(h)
+    z = rng.standard_normal((T, h))
+    return (c * u[None, :] + np.sqrt(1.0 - c * c) * z).astype(np.float32)
+
+
 def draw_router(rng, e=E, h=H):
     """bf16(N(0, 0.02)) router [E][H] as uint16 bit patterns."""
     return f32_to_bf16_bits((rng.standard_normal((e, h)) * 0.02).astype(np.float32))
@@ -132,6 +149,10 @@ CONFIGS = {
             chunk=2048),
     4: dict(name="stack48-T32768-zipf", T=32768, layers=48, seed=4, stack=True, zipf=True,
             chunk=2048),
+    # not one of the five above: a T = 4 verify window of correlated tokens
+    # (draw_window), for the window-dedup workload
+    5: dict(name="layer-T4-correlated-window", T=4, layers=1, seed=5, stack=False, zipf=False,
+            chunk=4, window=True),
 }
 
 

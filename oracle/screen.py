@@ -58,6 +58,22 @@ def screened_x(st, T, R_bits, bias=None, rmsnorm=False, margin=TIE_MARGIN, h=inp
     raise RuntimeError("near-tie screen did not converge")
 
 
+def screened_windows(st, T, n, R_bits, margin=TIE_MARGIN, h=inputs.H):
+    """n correlated windows [n][T][H] drawn from st.x (inputs.draw_window); a
+    window with a near-tie in any token's top 11 logits is replaced by a draw
+    from st.x_redraw.  Returns (windows, number of replaced windows)."""
+    out, redrawn = [], 0
+    for _ in range(n):
+        w = inputs.draw_window(st.x, T, h=h)
+        while not np.all(top11_gap(logits_np(w.astype(np.float64), R_bits, None)) > margin):
+            w = inputs.draw_window(st.x_redraw, T, h=h)
+            redrawn += 1
+            if redrawn > 100 * n:
+                raise RuntimeError("near-tie screen did not converge")
+        out.append(w)
+    return np.stack(out), redrawn
+
+
 class BlobSource:
     """Host blobs of one seed, generated on demand (threaded) and cached."""
 
