@@ -95,6 +95,21 @@ __device__ inline float block_dot(const uint32_t *p, uint32_t sel, uint32_t sh, 
     return (d * row_bcast_f<J>(xo.sc)) * (float)a;
 }
 
+// The same block against two tokens' operands: the codes are split once and
+// each token's result is the expression block_dot computes for it alone.
+template <int J>
+__device__ inline float2 block_dot2(const uint32_t *p, uint32_t sel, uint32_t sh, uint2 DA,
+                                    uint2 DB, const XOps &xa, const XOps &xb)
+{
+    const uint32_t v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3], v4 = p[4];
+    const Codes c = split_codes(__builtin_amdgcn_perm(v1, v0, sel), __builtin_amdgcn_perm(v2, v1, sel),
+                                __builtin_amdgcn_perm(v3, v2, sel), __builtin_amdgcn_perm(v4, v3, sel));
+    const float d = half_bits_to_float(v0 >> sh);
+    const int a = block_codes_dot(c, DA.x, DA.y, row_bcast_i<J>(xa.nq));
+    const int b = block_codes_dot(c, DB.x, DB.y, row_bcast_i<J>(xb.nq));
+    return make_float2((d * row_bcast_f<J>(xa.sc)) * (float)a, (d * row_bcast_f<J>(xb.sc)) * (float)b);
+}
+
 // Per-call counters of the fused kernel (zeroed by the router / prep kernel):
 // sync[1 + a] counts the finished gate/up items of active expert a.
 constexpr int EX_WAIT_LIMIT = 1 << 18;   // bounded wait (~0.2 s), never reached in a correct call
@@ -107,7 +122,31 @@ __device__ inline void store_h(uint32_t *p, uint32_t v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One gate/up item: LDS wl [DG_ROWS][DG_RS] dwords and part [DG_WAVES][DG_ROWS].
+// Wave 0: h = silu(g) * u of one token's 16 FF rows from the partial sums
+// part [DG_WAVES][DG_ROWS], quantised and stored as segment seg of slot.
+__device__ inline void emit_h(const float (*part)[DG_ROWS], int slot, int seg, const HQ &hq)
+{
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 31;
+    const float v = ((part[0][j] + part[1][j]) + part[2][j]) + part[3][j];
+    const float u = __shfl(v, (lane & 15) + DG_SEG, 64);
+    const float h = lane < DG_SEG ? v / (1.f + expf(-v)) * u : 0.f;
+    const QuantOut qo = quant_lanes<false>(h);
+    if (lane == 12 || lane == 13) {
+        uint32_t *blk = hq.dig + ((size_t)slot * HBLK + (seg >> 2)) * BLK_DWORDS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            store_h(blk + dig_pos(8 * (seg & 3) + 4 * (lane - 12) + i), qo.pk[i]);
+    }
+    if (lane == 0) {
+        store_h(reinterpret_cast<uint32_t *>(hq.scale) + (size_t)slot * HSEG16 + seg,
+                __float_as_uint(qo.scale));
+        store_h(reinterpret_cast<uint32_t *>(hq.nsum) + (size_t)slot * HSEG16 + seg,
+                (uint32_t)(-qo.sum));
+    }
+}
+
+// One gate/up item: LDS wl [DG_ROWS][DG_RS] dwords and part [2 DG_WAVES][DG_ROWS].
 __device__ void gateup_item(int item, const uint8_t *__restrict__ blobs,
                             const int4 *__restrict__ erec, const int32_t *__restrict__ slots,
                             const XQ &xq, const HQ &hq, int T, uint32_t *wl,
@@ -171,43 +210,60 @@ __device__ void gateup_item(int item, const uint8_t *__restrict__ blobs,
     const uint32_t *w3 = row + (90 * s + 54 - 2 * (1 - odd_s)) / 4;
     const uint32_t *w4 = row + (90 * s + 72 - 2 * odd_s) / 4;
     __syncthreads();
-    for (int ti = 0; ti < rec.z; ++ti) {
+    // Tokens two at a time: the weights of a block are decoded once for both,
+    // and each token's arithmetic is what it gets alone.  part[w] holds the
+    // first token's partial sums, part[DG_WAVES + w] the second's.
+    for (int ti = 0; ti < rec.z; ti += 2) {
+        const bool two = ti + 1 < rec.z;   // uniform per workgroup
         if (ti > 0) {
             slot = slots[rec.y + ti];
-            if (slot >= 0 && slot < nslot)
-                xo = load_xops(xq, slot / K, s, l);
+            xo = load_xops(xq, slot >= 0 && slot < nslot ? slot / K : 0, s, l);
         }
-        if (slot < 0 || slot >= nslot)
-            continue;   // only a corrupt grouping gets here; uniform per workgroup
-        float acc = block_dot<0>(w0, sel_e, sh_e, xo.d[0], xo);
-        acc += block_dot<1>(w1, sel_o, sh_o, xo.d[1], xo);
-        acc += block_dot<2>(w2, sel_e, sh_e, xo.d[2], xo);
-        acc += block_dot<3>(w3, sel_o, sh_o, xo.d[3], xo);
-        acc += block_dot<4>(w4, sel_e, sh_e, xo.d[4], xo);
+        int slot2 = -1;
+        XOps xo2 = xo;
+        if (two) {
+            slot2 = slots[rec.y + ti + 1];
+            xo2 = load_xops(xq, slot2 >= 0 && slot2 < nslot ? slot2 / K : 0, s, l);
+        }
+        float acc, acc2 = 0.f;
+        if (two) {
+            float2 t = block_dot2<0>(w0, sel_e, sh_e, xo.d[0], xo2.d[0], xo, xo2);
+            acc = t.x;
+            acc2 = t.y;
+            t = block_dot2<1>(w1, sel_o, sh_o, xo.d[1], xo2.d[1], xo, xo2);
+            acc += t.x;
+            acc2 += t.y;
+            t = block_dot2<2>(w2, sel_e, sh_e, xo.d[2], xo2.d[2], xo, xo2);
+            acc += t.x;
+            acc2 += t.y;
+            t = block_dot2<3>(w3, sel_o, sh_o, xo.d[3], xo2.d[3], xo, xo2);
+            acc += t.x;
+            acc2 += t.y;
+            t = block_dot2<4>(w4, sel_e, sh_e, xo.d[4], xo2.d[4], xo, xo2);
+            acc += t.x;
+            acc2 += t.y;
+            acc2 += __shfl_xor(acc2, 32, 64);
+        } else {
+            acc = block_dot<0>(w0, sel_e, sh_e, xo.d[0], xo);
+            acc += block_dot<1>(w1, sel_o, sh_o, xo.d[1], xo);
+            acc += block_dot<2>(w2, sel_e, sh_e, xo.d[2], xo);
+            acc += block_dot<3>(w3, sel_o, sh_o, xo.d[3], xo);
+            acc += block_dot<4>(w4, sel_e, sh_e, xo.d[4], xo);
+        }
         acc += __shfl_xor(acc, 32, 64);   // the wave's two column streams
         if (ti > 0)
-            __syncthreads();   // wave 0 is done with the previous token's partials
-        if (lane < DG_ROWS)
+            __syncthreads();   // wave 0 is done with the previous tokens' partials
+        if (lane < DG_ROWS) {
             part[wave][lane] = acc;
+            if (two)
+                part[DG_WAVES + wave][lane] = acc2;
+        }
         __syncthreads();
         if (wave == 0) {
-            const int j = lane & 31;
-            const float v = ((part[0][j] + part[1][j]) + part[2][j]) + part[3][j];
-            const float u = __shfl(v, (lane & 15) + DG_SEG, 64);
-            const float h = lane < DG_SEG ? v / (1.f + expf(-v)) * u : 0.f;
-            const QuantOut qo = quant_lanes<false>(h);
-            if (lane == 12 || lane == 13) {
-                uint32_t *blk = hq.dig + ((size_t)slot * HBLK + (seg >> 2)) * BLK_DWORDS;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    store_h(blk + dig_pos(8 * (seg & 3) + 4 * (lane - 12) + i), qo.pk[i]);
-            }
-            if (lane == 0) {
-                store_h(reinterpret_cast<uint32_t *>(hq.scale) + (size_t)slot * HSEG16 + seg,
-                        __float_as_uint(qo.scale));
-                store_h(reinterpret_cast<uint32_t *>(hq.nsum) + (size_t)slot * HSEG16 + seg,
-                        (uint32_t)(-qo.sum));
-            }
+            if (slot >= 0 && slot < nslot)   // only a corrupt grouping fails this
+                emit_h(part, slot, seg, hq);
+            if (two && slot2 >= 0 && slot2 < nslot)
+                emit_h(part + DG_WAVES, slot2, seg, hq);
         }
     }
     if (wave == 0) {   // every h value of the item is in memory: count the item
@@ -291,6 +347,38 @@ __device__ inline float down_block(const uint32_t *p, uint32_t sel, uint32_t sh,
     return d * bacc;
 }
 
+// down_block against two slots' h: the codes are split once and each slot's
+// result is the expression down_block computes for it alone.
+template <int N>
+__device__ inline float2 down_block2(const uint32_t *p, uint32_t sel, uint32_t sh, uint2 DA,
+                                     uint2 DB, float shrA, int nqrA, float shrB, int nqrB)
+{
+    const uint32_t v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3], v4 = p[4];
+    const Codes c = split_codes(__builtin_amdgcn_perm(v1, v0, sel), __builtin_amdgcn_perm(v2, v1, sel),
+                                __builtin_amdgcn_perm(v3, v2, sel), __builtin_amdgcn_perm(v4, v3, sel));
+    const float d = half_bits_to_float(v0 >> sh);
+    const Quad qa = quarters_codes_dot(c, DA.x, DA.y);
+    const Quad qb = quarters_codes_dot(c, DB.x, DB.y);
+    float ba = 0.f, bb = 0.f;
+    const float a0 = (float)(qa.q[0] + row_bcast_i<N>(nqrA));
+    STRATA_FMA_BCAST(ba, shrA, a0, N);
+    const float b0 = (float)(qb.q[0] + row_bcast_i<N>(nqrB));
+    STRATA_FMA_BCAST(bb, shrB, b0, N);
+    const float a1 = (float)(qa.q[1] + row_bcast_i<N + 1>(nqrA));
+    STRATA_FMA_BCAST(ba, shrA, a1, N + 1);
+    const float b1 = (float)(qb.q[1] + row_bcast_i<N + 1>(nqrB));
+    STRATA_FMA_BCAST(bb, shrB, b1, N + 1);
+    const float a2 = (float)(qa.q[2] + row_bcast_i<N + 2>(nqrA));
+    STRATA_FMA_BCAST(ba, shrA, a2, N + 2);
+    const float b2 = (float)(qb.q[2] + row_bcast_i<N + 2>(nqrB));
+    STRATA_FMA_BCAST(bb, shrB, b2, N + 2);
+    const float a3 = (float)(qa.q[3] + row_bcast_i<N + 3>(nqrA));
+    STRATA_FMA_BCAST(ba, shrA, a3, N + 3);
+    const float b3 = (float)(qb.q[3] + row_bcast_i<N + 3>(nqrB));
+    STRATA_FMA_BCAST(bb, shrB, b3, N + 3);
+    return make_float2(d * ba, d * bb);
+}
+
 // The five blocks 2 j + c0 of a row; their windows start at dwords 9 j (an
 // odd column's window starts 2 bytes before its scale).
 __device__ inline float down_row(const uint32_t *row, int c0, const HOps &ho)
@@ -302,6 +390,27 @@ __device__ inline float down_row(const uint32_t *row, int c0, const HOps &ho)
     acc += down_block<8>(row + 18, sel, sh, ho.d[2], ho.sh0, ho.nq0);
     acc += down_block<12>(row + 27, sel, sh, ho.d[3], ho.sh0, ho.nq0);
     acc += down_block<0>(row + 36, sel, sh, ho.d[4], ho.sh1, ho.nq1);
+    return acc;
+}
+
+// down_row for two slots.
+__device__ inline float2 down_row2(const uint32_t *row, int c0, const HOps &a, const HOps &b)
+{
+    const uint32_t sel = c0 ? 0x07060504u : 0x05040302u;
+    const uint32_t sh = c0 ? 16u : 0u;
+    float2 acc = down_block2<0>(row, sel, sh, a.d[0], b.d[0], a.sh0, a.nq0, b.sh0, b.nq0);
+    float2 t = down_block2<4>(row + 9, sel, sh, a.d[1], b.d[1], a.sh0, a.nq0, b.sh0, b.nq0);
+    acc.x += t.x;
+    acc.y += t.y;
+    t = down_block2<8>(row + 18, sel, sh, a.d[2], b.d[2], a.sh0, a.nq0, b.sh0, b.nq0);
+    acc.x += t.x;
+    acc.y += t.y;
+    t = down_block2<12>(row + 27, sel, sh, a.d[3], b.d[3], a.sh0, a.nq0, b.sh0, b.nq0);
+    acc.x += t.x;
+    acc.y += t.y;
+    t = down_block2<0>(row + 36, sel, sh, a.d[4], b.d[4], a.sh1, a.nq1, b.sh1, b.nq1);
+    acc.x += t.x;
+    acc.y += t.y;
     return acc;
 }
 
@@ -317,6 +426,50 @@ struct Combine {
     float *y;           // [T][H] or NULL
     float *res;         // [T][H] or NULL: res += y
 };
+
+// A wave's output rows ch * 32 .. + 31 of one slot (lanes < 32 hold them):
+// stored, and -- when the combine is fused -- counted, and the wave that
+// completes a token's K slots for these rows writes their weighted sum.
+__device__ inline void finish_slot(int slot, float acc, int ch, float *__restrict__ out, int T,
+                                   const Combine &cb)
+{
+    const int lane = threadIdx.x & 63;
+    if (slot < 0 || slot >= T * K)
+        return;   // only a corrupt grouping gets here; uniform per wave
+    float *orow = out + (size_t)slot * H + ch * DD_ROWS;
+    if (!cb.cdone) {
+        if (lane < DD_ROWS)
+            orow[lane] = acc;
+        return;
+    }
+    if (lane < DD_ROWS)
+        __hip_atomic_store(orow + lane, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the rows are in memory
+    const int t = slot / K;
+    int done = 0;
+    if (lane == 0)
+        done = __hip_atomic_fetch_add(cb.cdone + (size_t)t * (H / DD_ROWS) + ch, 1,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    done = __shfl(done, 0, 64);
+    if (done != K - 1)
+        return;
+    // the last of the token's slots for these rows: combine them
+    if (lane < DD_ROWS) {
+        const int r0 = ch * DD_ROWS + lane;
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float o = __hip_atomic_load(out + ((size_t)t * K + k) * H + r0, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+            sum = fmaf(cb.w[(size_t)t * K + k], o, sum);
+        }
+        if (cb.y)
+            cb.y[(size_t)t * H + r0] = sum;
+        if (cb.res)
+            cb.res[(size_t)t * H + r0] += sum;
+    }
+}
 
 // One down group: DD_WAVES items (32-row chunks) of one expert, one per wave,
 // each in its own LDS slice wl [DD_ROWS * DD_RS] dwords.  The weights are
@@ -369,49 +522,29 @@ __device__ void down_group(int grp, const uint8_t *__restrict__ blobs,
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint32_t *row = wl + ((r & 1) * 16 + l) * DD_RS + 4 * c0;
-    for (int ti = 0; ti < rec.z; ++ti) {
+    // Slots two at a time (the weights of a block decoded once for both).
+    for (int ti = 0; ti < rec.z; ti += 2) {
+        const bool two = ti + 1 < rec.z;   // uniform per wave
         if (ti > 0) {
             slot = slots[rec.y + ti];
-            if (slot >= 0 && slot < nslot)
-                ho = load_hops(hq, slot, c0, l);
+            ho = load_hops(hq, slot >= 0 && slot < nslot ? slot : 0, c0, l);
         }
-        if (slot < 0 || slot >= nslot)
-            continue;   // only a corrupt grouping gets here; uniform per wave
-        float acc = down_row(row, c0, ho);
+        int slot2 = -1;
+        float acc, acc2 = 0.f;
+        if (two) {
+            slot2 = slots[rec.y + ti + 1];
+            const HOps ho2 = load_hops(hq, slot2 >= 0 && slot2 < nslot ? slot2 : 0, c0, l);
+            const float2 r2 = down_row2(row, c0, ho, ho2);
+            acc = r2.x;
+            acc2 = r2.y;
+            acc2 += __shfl_xor(acc2, 32, 64);
+        } else {
+            acc = down_row(row, c0, ho);
+        }
         acc += __shfl_xor(acc, 32, 64);
-        float *orow = out + (size_t)slot * H + ch * DD_ROWS;
-        if (!cb.cdone) {
-            if (lane < DD_ROWS)
-                orow[lane] = acc;
-            continue;
-        }
-        if (lane < DD_ROWS)
-            __hip_atomic_store(orow + lane, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the rows are in memory
-        const int t = slot / K;
-        int done = 0;
-        if (lane == 0)
-            done = __hip_atomic_fetch_add(cb.cdone + (size_t)t * (H / DD_ROWS) + ch, 1,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        done = __shfl(done, 0, 64);
-        if (done != K - 1)
-            continue;
-        // the last of the token's slots for these rows: combine them
-        if (lane < DD_ROWS) {
-            const int r0 = ch * DD_ROWS + lane;
-            float sum = 0.f;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const float o = __hip_atomic_load(out + ((size_t)t * K + k) * H + r0, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-                sum = fmaf(cb.w[(size_t)t * K + k], o, sum);
-            }
-            if (cb.y)
-                cb.y[(size_t)t * H + r0] = sum;
-            if (cb.res)
-                cb.res[(size_t)t * H + r0] += sum;
-        }
+        finish_slot(slot, acc, ch, out, T, cb);
+        if (two)
+            finish_slot(slot2, acc2, ch, out, T, cb);
     }
 }
 
@@ -419,7 +552,7 @@ constexpr int EX_THREADS = 64 * DG_WAVES;
 static_assert(DD_WAVES == DG_WAVES, "gate/up and down workgroups have one shape");
 static_assert(DD_ITEMS_PER_E % DD_WAVES == 0, "a down group stays within one expert");
 constexpr int EX_DN_PER_E = DD_ITEMS_PER_E / DD_WAVES;   // 20 down groups per expert
-constexpr size_t EX_LDS_GU = (size_t)DG_ROWS * DG_RS * 4 + (size_t)DG_WAVES * DG_ROWS * 4;
+constexpr size_t EX_LDS_GU = (size_t)DG_ROWS * DG_RS * 4 + (size_t)2 * DG_WAVES * DG_ROWS * 4;
 constexpr size_t EX_LDS_DN = (size_t)DD_WAVES * DD_ROWS * DD_RS * 4;
 constexpr size_t EX_LDS = EX_LDS_GU > EX_LDS_DN ? EX_LDS_GU : EX_LDS_DN;
 
