@@ -158,6 +158,16 @@ __global__ __launch_bounds__(RG_THREADS) void rdec_gemv(const float *__restrict_
 
 constexpr int RT_THREADS = 64 * DECODE_T_MAX;     // one wave per token
 
+// Workgroup barrier for LDS data only: unlike __syncthreads it does not make
+// every wave wait for its outstanding global stores (here the zeroing of the
+// experts kernel's counters, which only that later launch reads).
+__device__ inline void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // (p, e) ranks before (q, f): larger probability, or equal and lower id.
 __device__ inline bool ranks_before(float p, int e, float q, int f)
 {
@@ -176,18 +186,12 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
     __shared__ int first[E];                // first slot of each expert
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = T * K;
-    if (cdone)   // the down kernel's per-(token, 32 rows) slot counters start at zero
-        for (int i = tid; i < T * (H / 32); i += RT_THREADS)
-            cdone[i] = 0;
-    if (esync)   // so do the experts kernel's per-expert counters
-        for (int i = tid; i <= 32 * E; i += RT_THREADS)
-            esync[i] = 0;
     if (group) {
         for (int i = tid; i < E; i += RT_THREADS) {
             cnt[i] = 0;
             cur[i] = 0;
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (wave < T) {
         const int t = wave;
@@ -271,9 +275,18 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
             }
         }
     }
+    // The experts kernel's counters start at zero: its per-(token, 32 rows)
+    // slot counters and per-expert item counters.  (Stored after the logits
+    // are read: one counter orders a wave's loads and stores.)
+    if (cdone)
+        for (int i = tid; i < T * (H / 32); i += RT_THREADS)
+            cdone[i] = 0;
+    if (esync)
+        for (int i = tid; i <= 32 * E; i += RT_THREADS)
+            esync[i] = 0;
     if (!group)
         return;
-    __syncthreads();
+    lds_barrier();
     if (wave != 0)
         return;
     // Wave 0: lane l owns experts 8 l .. 8 l + 7.
