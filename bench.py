@@ -84,6 +84,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graphs")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="store copies cycled by single-layer workloads (default: the workload's; "
+                         "1 keeps the layer's experts in cache between steps, a diagnostic)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="only run a device copy of this many MB (counter calibration)")
     return ap.parse_args()
@@ -122,7 +125,7 @@ def main():
 
     # Device state: stores (copies of the same layer for single-layer runs,
     # the 48 distinct layers for stacks), routers, workspace, outputs.
-    copies = wl["copies"] if not stack else 1
+    copies = (a.copies or wl["copies"]) if not stack else 1
     n_store = L if stack else copies
     store = torch.empty(n_store * per_layer, dtype=torch.uint8, device="cuda")
     for i in range(n_store):
