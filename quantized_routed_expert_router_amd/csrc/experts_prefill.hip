@@ -117,14 +117,19 @@ struct PfAct {
     }
 };
 
-// Every LDS read of block b (the 4 activation subtiles x 2 K-halves, and for
-// each of the 4 weight subtiles its scale and this lane's code dword), then
-// the wait for them, in one statement: the compiler sees finished values.
+// The LDS reads of one block: the 4 activation subtiles x 2 K-halves and, for
+// each of the 4 weight subtiles, its scale and this lane's code dword.
 // AOFF: activation buffer offset; BOFF: this block's offset in the weight
 // rows; NS1..NS3: offsets of weight subtiles 1..3 from subtile 0.
+struct PfVals {
+    half8 af[4][2];
+    uint32_t dbits[4], wc[4];
+};
+
+// Issues the reads without waiting for them: the values are not to be used
+// before pf_reads_done on the same PfVals (which is what orders them).
 template <int AOFF, int BOFF, int NS1, int NS2, int NS3>
-__device__ inline void pf_reads(uint32_t a0, uint32_t a1, uint32_t bs, uint32_t bc, half8 af[4][2],
-                                uint32_t dbits[4], uint32_t wc[4])
+__device__ inline void pf_reads_issue(uint32_t a0, uint32_t a1, uint32_t bs, uint32_t bc, PfVals &v)
 {
     asm volatile("ds_read_b128 %0, %16 offset:%20\n\t"
                  "ds_read_b128 %1, %17 offset:%20\n\t"
@@ -141,24 +146,37 @@ __device__ inline void pf_reads(uint32_t a0, uint32_t a1, uint32_t bs, uint32_t 
                  "ds_read_u16 %10, %18 offset:%26\n\t"
                  "ds_read_b32 %14, %19 offset:%26\n\t"
                  "ds_read_u16 %11, %18 offset:%27\n\t"
-                 "ds_read_b32 %15, %19 offset:%27\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(af[0][0]), "=&v"(af[0][1]), "=&v"(af[1][0]), "=&v"(af[1][1]),
-                   "=&v"(af[2][0]), "=&v"(af[2][1]), "=&v"(af[3][0]), "=&v"(af[3][1]),
-                   "=&v"(dbits[0]), "=&v"(dbits[1]), "=&v"(dbits[2]), "=&v"(dbits[3]),
-                   "=&v"(wc[0]), "=&v"(wc[1]), "=&v"(wc[2]), "=&v"(wc[3])
+                 "ds_read_b32 %15, %19 offset:%27"
+                 : "=&v"(v.af[0][0]), "=&v"(v.af[0][1]), "=&v"(v.af[1][0]), "=&v"(v.af[1][1]),
+                   "=&v"(v.af[2][0]), "=&v"(v.af[2][1]), "=&v"(v.af[3][0]), "=&v"(v.af[3][1]),
+                   "=&v"(v.dbits[0]), "=&v"(v.dbits[1]), "=&v"(v.dbits[2]), "=&v"(v.dbits[3]),
+                   "=&v"(v.wc[0]), "=&v"(v.wc[1]), "=&v"(v.wc[2]), "=&v"(v.wc[3])
                  : "v"(a0), "v"(a1), "v"(bs), "v"(bc), "i"(AOFF), "i"(AOFF + 2048),
                    "i"(AOFF + 4096), "i"(AOFF + 6144), "i"(BOFF), "i"(BOFF + NS1),
                    "i"(BOFF + NS2), "i"(BOFF + NS3)
                  : "memory");
 }
 
+// Waits for the reads of v: from here on the compiler sees their values.
+__device__ inline void pf_reads_done(PfVals &v)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v.af[0][0]), "+v"(v.af[0][1]), "+v"(v.af[1][0]), "+v"(v.af[1][1]),
+                   "+v"(v.af[2][0]), "+v"(v.af[2][1]), "+v"(v.af[3][0]), "+v"(v.af[3][1]),
+                   "+v"(v.dbits[0]), "+v"(v.dbits[1]), "+v"(v.dbits[2]), "+v"(v.dbits[3]),
+                   "+v"(v.wc[0]), "+v"(v.wc[1]), "+v"(v.wc[2]), "+v"(v.wc[3])
+                 :
+                 : "memory");
+}
+
 // acc[ns][mi] += A(64 x 64) W(64 x 64) from the values read for one block:
 // the four weight subtiles are dequantised first, then the 32 MFMAs run in
 // an order where one accumulator recurs only every 16 instructions.
-__device__ inline void pf_math(const half8 af[4][2], const uint32_t dbits[4], const uint32_t wc[4],
-                               floatx4 acc[4][4])
+__device__ inline void pf_math(const PfVals &v, floatx4 acc[4][4])
 {
+    const auto &af = v.af;
+    const auto &dbits = v.dbits;
+    const auto &wc = v.wc;
     half8 bf[4][2];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
@@ -201,13 +219,18 @@ __device__ inline void pf_act_read_addrs(uint32_t abase, uint32_t &a0, uint32_t 
     a1 = abase + (lane & 15) * 128 + 16 * ((q + 4) ^ (lane & 7));
 }
 
-// Gate/up K loop: 40 blocks, weight stage s = blocks 2 s, 2 s + 1.
-// Issue order: prologue A0, W0, A1, A2; iteration b (after its barrier):
-// W(b/2 + 1) if b is even, then A(b + 3) (past the end: the last block or
-// stage again, never read).  At the top of iteration b, the loads younger
-// than W(s = b/2) are A(b+1), A(b+2) (4 lane-loads) when b is even; when b
-// is odd the oldest needed is A(b) and younger are A(b+1), W(s+1), A(b+2):
-// 2 + 9 + 2 = 13.
+// Gate/up K loop: 40 blocks, weight stage t = blocks 2 t, 2 t + 1 (buffer
+// t & 1), activation block j in ring buffer j & 3.  Iteration b waits for the
+// data of block b + 1, passes the barrier (after which every wave has read
+// block b - 1 out of LDS), requests what goes into the freed buffers, issues
+// the LDS reads of block b + 1 and, while they run, computes block b from the
+// values read in iteration b - 1.  Requests of iteration i: the weight stage
+// (i + 3) / 2 if i is odd, then activation block i + 4 (past the end: the last
+// block or stage again, never read).  The prologue issues those of iterations
+// -4 .. -1 (A0; W0, A1; A2; W1, A3) and reads block 0.  Wait counts at the
+// top of iteration b, in lane-loads younger than the oldest one needed:
+//  b even: A(b+1) is the oldest; younger A(b+2), W((b+2)/2), A(b+3): 13.
+//  b odd:  W((b+1)/2) (issued in iteration b-2) is; younger A(b+2), A(b+3): 4.
 __device__ inline void pf_gateup_loop(const uint8_t *blob, const uint32_t goff[PF_GNB],
                                       const PfAct &act, uint8_t *lds, uint32_t bs, uint32_t bc,
                                       floatx4 acc[4][4])
@@ -223,28 +246,36 @@ __device__ inline void pf_gateup_loop(const uint8_t *blob, const uint32_t goff[P
                                              4, 0, 0);
     };
     constexpr int NST = NB_G / 2;
+    constexpr int NS1 = 16 * PF_GSROW, NS2 = 128 * PF_GSROW, NS3 = 144 * PF_GSROW;
     uint32_t a0, a1;
     pf_act_read_addrs(lds_addr(lds), a0, a1);
     act.request(lds, 0);
     wreq(0, 0);
     act.request(lds + PF_ABYTES, 1);
     act.request(lds + 2 * PF_ABYTES, 2);
-    constexpr int NS1 = 16 * PF_GSROW, NS2 = 128 * PF_GSROW, NS3 = 144 * PF_GSROW;
+    wreq(1, 1);
+    act.request(lds + 3 * PF_ABYTES, 3);
+    vm_wait<15>();   // A0 and W0: younger A1, A2, W1, A3
+    __builtin_amdgcn_s_barrier();
+    PfVals cur, nxt;
+    pf_reads_issue<0, 0, NS1, NS2, NS3>(a0, a1, bs, bc, cur);
+    pf_reads_done(cur);
 #define STRATA_PF_STEP(R)                                                                          \
     {                                                                                              \
         const int b = b0 + (R);                                                                    \
-        vm_wait<((R) & 1) ? 13 : 4>();                                                             \
+        vm_wait<((R) & 1) ? 4 : 13>();                                                             \
         __builtin_amdgcn_s_barrier();                                                              \
-        if (!((R) & 1)) {                                                                          \
-            const int s1 = b / 2 + 1;                                                              \
-            wreq(s1 < NST ? s1 : NST - 1, (((R) >> 1) + 1) & 1);                                   \
+        if ((R) & 1) {                                                                             \
+            const int t = (b + 3) / 2;                                                             \
+            wreq(t < NST ? t : NST - 1, t & 1);                                                    \
         }                                                                                          \
-        act.request(lds + (((R) + 3) & 3) * PF_ABYTES, b + 3 < NB_G ? b + 3 : NB_G - 1);           \
-        half8 af[4][2];                                                                            \
-        uint32_t dbits[4], wc[4];                                                                  \
-        pf_reads<(R) * PF_ABYTES, ((R) >> 1) * PF_GSTAGE + BB * ((R) & 1), NS1, NS2, NS3>(          \
-            a0, a1, bs, bc, af, dbits, wc);                                                        \
-        pf_math(af, dbits, wc, acc);                                                               \
+        act.request(lds + ((R) & 3) * PF_ABYTES, b + 4 < NB_G ? b + 4 : NB_G - 1);                 \
+        pf_reads_issue<(((R) + 1) & 3) * PF_ABYTES, ((((R) + 1) >> 1) & 1) * PF_GSTAGE +           \
+                                                        BB * (((R) + 1) & 1),                      \
+                       NS1, NS2, NS3>(a0, a1, bs, bc, nxt);                                        \
+        pf_math(cur, acc);                                                                         \
+        pf_reads_done(nxt);                                                                        \
+        cur = nxt;                                                                                 \
     }
 #pragma unroll 1
     for (int b0 = 0; b0 < NB_G; b0 += 4) {
@@ -257,9 +288,9 @@ __device__ inline void pf_gateup_loop(const uint8_t *blob, const uint32_t goff[P
     vm_wait<0>();   // the trailing requests land before the LDS is released
 }
 
-// Down K loop: 10 blocks; all weights requested first.  Issue order: W, A0,
-// A1, A2; iteration b (after its barrier): A(b + 3) (clamped).  At the top of
-// iteration b the loads younger than A(b) are A(b+1), A(b+2): 4.
+// Down K loop: 10 blocks; all weights requested first, then A0 .. A3.
+// Iteration b: wait for A(b+1) (younger: A(b+2), A(b+3): 4), barrier, request
+// A(b+4) into block b's buffer, issue the reads of block b+1, compute block b.
 __device__ inline void pf_down_loop(const uint8_t *wsrc, const PfAct &act, uint8_t *lds,
                                     uint32_t bs, uint32_t bc, floatx4 acc[4][4])
 {
@@ -275,16 +306,23 @@ __device__ inline void pf_down_loop(const uint8_t *wsrc, const PfAct &act, uint8
     act.request(lds, 0);
     act.request(lds + PF_ABYTES, 1);
     act.request(lds + 2 * PF_ABYTES, 2);
+    act.request(lds + 3 * PF_ABYTES, 3);
     constexpr int NS1 = 16 * ROW_D, NS2 = 32 * ROW_D, NS3 = 48 * ROW_D;
+    vm_wait<6>();   // the weights and A0: younger A1, A2, A3
+    __builtin_amdgcn_s_barrier();
+    PfVals cur, nxt;
+    pf_reads_issue<0, 0, NS1, NS2, NS3>(a0, a1, bs, bc, cur);
+    pf_reads_done(cur);
 #define STRATA_PF_DSTEP(B)                                                                         \
     {                                                                                              \
         vm_wait<4>();                                                                              \
         __builtin_amdgcn_s_barrier();                                                              \
-        act.request(lds + (((B) + 3) & 3) * PF_ABYTES, (B) + 3 < NB_D ? (B) + 3 : NB_D - 1);       \
-        half8 af[4][2];                                                                            \
-        uint32_t dbits[4], wc[4];                                                                  \
-        pf_reads<((B) & 3) * PF_ABYTES, BB * (B), NS1, NS2, NS3>(a0, a1, bs, bc, af, dbits, wc);   \
-        pf_math(af, dbits, wc, acc);                                                               \
+        act.request(lds + ((B) & 3) * PF_ABYTES, (B) + 4 < NB_D ? (B) + 4 : NB_D - 1);             \
+        pf_reads_issue<(((B) + 1) & 3) * PF_ABYTES, BB * ((B) + 1 < NB_D ? (B) + 1 : NB_D - 1),    \
+                       NS1, NS2, NS3>(a0, a1, bs, bc, nxt);                                        \
+        pf_math(cur, acc);                                                                         \
+        pf_reads_done(nxt);                                                                        \
+        cur = nxt;                                                                                 \
     }
     STRATA_PF_DSTEP(0)
     STRATA_PF_DSTEP(1)
