@@ -172,6 +172,7 @@ __device__ inline void pf_reads_done(PfVals &v)
 // acc[ns][mi] += A(64 x 64) W(64 x 64) from the values read for one block:
 // the four weight subtiles are dequantised first, then the 32 MFMAs run in
 // an order where one accumulator recurs only every 16 instructions.
+template <int MS>
 __device__ inline void pf_math(const PfVals &v, floatx4 acc[4][4])
 {
     const auto &af = v.af;
@@ -192,7 +193,7 @@ __device__ inline void pf_math(const PfVals &v, floatx4 acc[4][4])
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < MS; ++mi)   // only the 16-row groups holding item rows
                 acc[ns][mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mi][j], bf[ns][j], acc[ns][mi],
                                                                       0, 0, 0);
 #ifdef PF_INTERLEAVE
@@ -231,6 +232,7 @@ __device__ inline void pf_act_read_addrs(uint32_t abase, uint32_t &a0, uint32_t 
 // top of iteration b, in lane-loads younger than the oldest one needed:
 //  b even: A(b+1) is the oldest; younger A(b+2), W((b+2)/2), A(b+3): 13.
 //  b odd:  W((b+1)/2) (issued in iteration b-2) is; younger A(b+2), A(b+3): 4.
+template <int MS>
 __device__ inline void pf_gateup_loop(const uint8_t *blob, const uint32_t goff[PF_GNB],
                                       const PfAct &act, uint8_t *lds, uint32_t bs, uint32_t bc,
                                       floatx4 acc[4][4])
@@ -273,7 +275,7 @@ __device__ inline void pf_gateup_loop(const uint8_t *blob, const uint32_t goff[P
         pf_reads_issue<(((R) + 1) & 3) * PF_ABYTES, ((((R) + 1) >> 1) & 1) * PF_GSTAGE +           \
                                                         BB * (((R) + 1) & 1),                      \
                        NS1, NS2, NS3>(a0, a1, bs, bc, nxt);                                        \
-        pf_math(cur, acc);                                                                         \
+        pf_math<MS>(cur, acc);                                                                     \
         pf_reads_done(nxt);                                                                        \
         cur = nxt;                                                                                 \
     }
@@ -291,6 +293,7 @@ __device__ inline void pf_gateup_loop(const uint8_t *blob, const uint32_t goff[P
 // Down K loop: 10 blocks; all weights requested first, then A0 .. A3.
 // Iteration b: wait for A(b+1) (younger: A(b+2), A(b+3): 4), barrier, request
 // A(b+4) into block b's buffer, issue the reads of block b+1, compute block b.
+template <int MS>
 __device__ inline void pf_down_loop(const uint8_t *wsrc, const PfAct &act, uint8_t *lds,
                                     uint32_t bs, uint32_t bc, floatx4 acc[4][4])
 {
@@ -320,7 +323,7 @@ __device__ inline void pf_down_loop(const uint8_t *wsrc, const PfAct &act, uint8
         act.request(lds + ((B) & 3) * PF_ABYTES, (B) + 4 < NB_D ? (B) + 4 : NB_D - 1);             \
         pf_reads_issue<(((B) + 1) & 3) * PF_ABYTES, BB * ((B) + 1 < NB_D ? (B) + 1 : NB_D - 1),    \
                        NS1, NS2, NS3>(a0, a1, bs, bc, nxt);                                        \
-        pf_math(cur, acc);                                                                         \
+        pf_math<MS>(cur, acc);                                                                     \
         pf_reads_done(nxt);                                                                        \
         cur = nxt;                                                                                 \
     }
@@ -411,7 +414,21 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
             acc[ns][mi] = (floatx4){0.f, 0.f, 0.f, 0.f};
-    pf_gateup_loop(blob, goff, act, lds, bs, bc, acc);
+    // one straight-line loop per number of 16-row groups holding item rows
+    switch ((it.rows + 15) >> 4) {
+    case 1:
+        pf_gateup_loop<1>(blob, goff, act, lds, bs, bc, acc);
+        break;
+    case 2:
+        pf_gateup_loop<2>(blob, goff, act, lds, bs, bc, acc);
+        break;
+    case 3:
+        pf_gateup_loop<3>(blob, goff, act, lds, bs, bc, acc);
+        break;
+    default:
+        pf_gateup_loop<4>(blob, goff, act, lds, bs, bc, acc);
+        break;
+    }
     // Epilogue: h = silu(g) * u for FF rows jw + 16 h2 + lane%16.
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -464,7 +481,20 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
             acc[ns][mi] = (floatx4){0.f, 0.f, 0.f, 0.f};
-    pf_down_loop(wsrc, act, lds, bs, bc, acc);
+    switch ((it.rows + 15) >> 4) {
+    case 1:
+        pf_down_loop<1>(wsrc, act, lds, bs, bc, acc);
+        break;
+    case 2:
+        pf_down_loop<2>(wsrc, act, lds, bs, bc, acc);
+        break;
+    case 3:
+        pf_down_loop<3>(wsrc, act, lds, bs, bc, acc);
+        break;
+    default:
+        pf_down_loop<4>(wsrc, act, lds, bs, bc, acc);
+        break;
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
