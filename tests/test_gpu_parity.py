@@ -89,7 +89,7 @@ def test_prefill_skewed_multi_chunk_experts():
 @pytest.mark.timeout(600)
 def test_config3_prefill_sampled():
     c = inputs.CONFIGS[3]
-    _say(f"case: config 3 T={c['T']} seed {c['seed']}")
+    _say(f"case: layer-T2048-prefill T={c['T']} seed {c['seed']}")
     x, R, redrawn = hz.single_layer_case(c["seed"], c["T"])
     ids, w, y, _ = hz.gpu_layer(x, R, hz.store(c["seed"]))
     import oracle
@@ -99,9 +99,9 @@ def test_config3_prefill_sampled():
     rows = np.random.default_rng(3).choice(c["T"], 64, replace=False)
     rows = np.sort(np.concatenate([rows, [0, c["T"] - 1]]))
     sids, sw, sy = hz.oracle_rows(x, R, c["seed"], rows)
-    hz.check("config 3 sampled", ids[rows], w[rows], y[rows], sids, sw, sy)
+    hz.check("layer-T2048-prefill sampled", ids[rows], w[rows], y[rows], sids, sw, sy)
     load = np.bincount(ids.ravel(), minlength=512)
-    _say(f"config 3: {redrawn} rows redrawn; tokens per expert {load.min()}..{load.max()}")
+    _say(f"layer-T2048-prefill: {redrawn} rows redrawn; tokens per expert {load.min()}..{load.max()}")
 
 
 @pytest.mark.timeout(600)

@@ -77,21 +77,21 @@ def test_config2_stack_t1():
     st = inputs.Streams(seed)
     x0 = inputs.draw_x(st.x, 1)
     src = scr.BlobSource(seed)
-    print("case: config 2 screening routers on the oracle trajectory", flush=True)
+    print("case: stack48-T1 screening routers on the oracle trajectory", flush=True)
     routers, redraws = scr.screened_stack_routers(st, x0, src, 48, STACK_MARGIN_T1)
     traj = scr.stack_trajectory(x0, routers, src)
-    print(f"config 2: {redraws} router redraws; min gap {min(g.min() for g in traj['gap']):.2e}",
+    print(f"stack48-T1: {redraws} router redraws; min gap {min(g.min() for g in traj['gap']):.2e}",
           flush=True)
     store = inputs.layer_store(seed, 0, n_layers=48)
-    print("case: config 2 GPU stack (48 layers, 34 GB store)", flush=True)
+    print("case: stack48-T1 GPU stack (48 layers, 34 GB store)", flush=True)
     got = _run_stack_gpu(x0, routers, store)
     worst = 0.0
     for l in range(48):
-        worst = max(worst, hz.check(f"config 2 e2e layer {l}", got["ids"][l], got["w"][l],
+        worst = max(worst, hz.check(f"stack48-T1 e2e layer {l}", got["ids"][l], got["w"][l],
                                     got["y"][l], traj["ids"][l], traj["w"][l], traj["y"][l],
                                     w_tol=W_TOL_STACK))
     dx = np.max(np.abs(got["x"] - traj["x_out"])) / np.max(np.abs(traj["x_out"]))
-    print(f"config 2: worst end-to-end layer {worst:.3e}, final x {dx:.3e}", flush=True)
+    print(f"stack48-T1: worst end-to-end layer {worst:.3e}, final x {dx:.3e}", flush=True)
     assert dx <= hz.Y_TOL
     # the byte budget: 48 x 10 distinct blobs were read for the token
     assert sum(len(set(i.ravel())) for i in got["ids"]) == 480
@@ -100,7 +100,7 @@ def test_config2_stack_t1():
     for l in range(48):
         ids, w, y, xo = hz.gpu_layer(traj["x_in"][l], routers[l], store[l * per:(l + 1) * per],
                                      flags=3)
-        hz.check(f"config 2 forced layer {l}", ids, w, y, traj["ids"][l], traj["w"][l],
+        hz.check(f"stack48-T1 forced layer {l}", ids, w, y, traj["ids"][l], traj["w"][l],
                  traj["y"][l])
 
 
@@ -114,7 +114,7 @@ def test_config4_stack_sampled():
     biases = [inputs.draw_zipf_bias(st.bias) for _ in range(48)]
     cand = np.sort(np.random.default_rng(44).choice(T, 24, replace=False))
     store = inputs.layer_store(seed, 0, n_layers=48)
-    print("case: config 4 GPU, 16 chunks x 48 layers", flush=True)
+    print("case: stack48-T32768-zipf GPU, 16 chunks x 48 layers", flush=True)
     got = {k: [[] for _ in range(48)] for k in ("ids", "w", "y")}
     gx = []
     for ch in range(T // chunk):
@@ -128,12 +128,12 @@ def test_config4_stack_sampled():
     for k in ("ids", "w", "y"):
         got[k] = [np.concatenate(v) for v in got[k]]
     gx = np.concatenate(gx)
-    print("case: config 4 oracle trajectories of 24 sampled tokens", flush=True)
+    print("case: stack48-T32768-zipf oracle trajectories of 24 sampled tokens", flush=True)
     src = scr.BlobSource(seed, cache=20000)
     traj = scr.stack_trajectory(x[cand], routers, src, biases)
     gaps = np.min(np.stack(traj["gap"]), axis=0)
     keep = np.nonzero(gaps > STACK_MARGIN_PREFILL)[0]
-    print(f"config 4: {keep.size}/24 tokens clear the {STACK_MARGIN_PREFILL} margin at all 48 "
+    print(f"stack48-T32768-zipf: {keep.size}/24 tokens clear the {STACK_MARGIN_PREFILL} margin at all 48 "
           f"layers", flush=True)
     assert keep.size >= 6
     # per layer on the oracle's own inputs, inside a full 2048-token chunk (so
@@ -146,7 +146,7 @@ def test_config4_stack_sampled():
         xin[:k] = traj["x_in"][l][keep]
         ids, w, y, _ = hz.gpu_layer(xin, routers[l], store[l * per:(l + 1) * per],
                                     bias=biases[l], flags=3)
-        hz.check(f"config 4 forced layer {l}", ids[:k], w[:k], y[:k], traj["ids"][l][keep],
+        hz.check(f"stack48-T32768-zipf forced layer {l}", ids[:k], w[:k], y[:k], traj["ids"][l][keep],
                  traj["w"][l][keep], traj["y"][l][keep])
     # end to end on the GPU's own residual stream.  The fp32 stream drifts from
     # the fp64 trajectory (this stack's residual grows to |x| ~ 1e2), so after
@@ -165,12 +165,12 @@ def test_config4_stack_sampled():
         assert np.all(np.isfinite(gy)), l
         same = np.all(gi == traj["ids"][l], axis=1)
         if l == 0:
-            hz.check("config 4 e2e layer 0", gi[keep], gw[keep], gy[keep], traj["ids"][0][keep],
+            hz.check("stack48-T32768-zipf e2e layer 0", gi[keep], gw[keep], gy[keep], traj["ids"][0][keep],
                      traj["w"][0][keep], traj["y"][0][keep])
         on = keep[same[keep]]
         dy = (float(np.max(np.abs(gy[on] - traj["y"][l][on])) / np.max(np.abs(traj["y"][l][on])))
               if on.size else 0.0)
-        print(f"[config 4 e2e layer {l}] rows on the oracle trajectory's experts "
+        print(f"[stack48-T32768-zipf e2e layer {l}] rows on the oracle trajectory's experts "
               f"{int(same.sum())}/{len(cand)}, drift max|dy|/max|y| on them {dy:.3e}", flush=True)
         assert dy <= 0.1, (l, dy)
         xs = (xs + gy.astype(np.float32)).astype(np.float32)
