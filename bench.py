@@ -276,7 +276,7 @@ def main():
         "warmup": warm, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16-mfma/f32-acc" if prefill else "i4dot-16bit/f32-acc",
         "data": "synthetic (seeded generator; no trained weights)",
-        "config": {"workload": f"{a.workload}: config {wl['cfg']} ({cfg['name']}), T={T}, "
+        "config": {"workload": f"{a.workload}: {cfg['name']}, T={T}, "
                                f"layers={L}, 512 Q2_0 experts, top-10",
                    "global_batch": T, "seq_len": 1 if not prefill else T,
                    "parallelism": "single GPU", "timing": "eager" if a.eager else "hipGraph replay",

@@ -29,6 +29,9 @@ static_assert((size_t)H * ROW_D == MAT, "down matrix size");
 
 // Decode path: T up to this many tokens runs the dot-product kernels.
 constexpr int DECODE_T_MAX = 16;
+// Decode experts kernel: the counter of active expert a (finished gate/up
+// items) is sync[1 + SYNC_STRIDE * a], one 128-byte line per counter.
+constexpr int SYNC_STRIDE = 32;
 
 // Prefill path tiles.
 constexpr int PF_M = 64;                       // tokens per M-chunk
@@ -61,7 +64,7 @@ struct Ws {
     size_t hperm;      // f16 [Tp*K][FF]     (grouped order)
     size_t out;        // f32 [T*K][H]
     size_t cdone;      // i32 [Td][H/32]      decode layer: finished slots per (token, 32 rows)
-    size_t esync;      // i32 [1+32E]        decode experts: finished gate/up items per expert (128-B apart)
+    size_t esync;      // i32 [1+32E]        decode experts: finished gate/up items per active expert (128-B apart)
     size_t total;
     int max_items;
 };

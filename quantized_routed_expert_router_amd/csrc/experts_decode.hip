@@ -111,9 +111,8 @@ __device__ inline float2 block_dot2(const uint32_t *p, uint32_t sel, uint32_t sh
 }
 
 // Per-call counters of the fused kernel (zeroed by the router / prep kernel):
-// sync[1 + a] counts the finished gate/up items of active expert a.
+// sync[1 + SYNC_STRIDE * a] counts the finished gate/up items of active expert a.
 constexpr int EX_WAIT_LIMIT = 1 << 18;   // bounded wait (~0.2 s), never reached in a correct call
-constexpr int EX_GD_STRIDE = 32;         // one 128-byte line per expert counter
 
 // h values are stored and read at agent scope (coherent across the XCDs'
 // L2 caches): the down part of the same launch reads them.
@@ -270,7 +269,7 @@ __device__ void gateup_item(int item, const uint8_t *__restrict__ blobs,
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (lane == 0)
-            __hip_atomic_fetch_add(gdone + EX_GD_STRIDE * (item / DG_SEGS), 1, __ATOMIC_RELAXED,
+            __hip_atomic_fetch_add(gdone + SYNC_STRIDE * (item / DG_SEGS), 1, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -510,7 +509,7 @@ __device__ void down_group(int grp, const uint8_t *__restrict__ blobs,
     // lane of the workgroup polls, sparsely.
     if (threadIdx.x == 0) {
         int n = 0;
-        while (__hip_atomic_load(gdone + EX_GD_STRIDE * a, __ATOMIC_RELAXED,
+        while (__hip_atomic_load(gdone + SYNC_STRIDE * a, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT) < DG_SEGS &&
                ++n < EX_WAIT_LIMIT)
             __builtin_amdgcn_s_sleep(32);

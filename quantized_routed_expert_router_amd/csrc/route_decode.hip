@@ -42,15 +42,15 @@ static_assert(RG_SPAN == 64 * 8, "8 elements per lane");
 struct GroupIn {
     const int32_t *offsets, *slots, *active;
     int4 *erec;
-    int32_t *esync;   // [1+E] counters of the experts kernel, zeroed here
+    int32_t *esync;   // counters of the experts kernel (one per active expert), zeroed here
 };
 
 __device__ inline void build_records(const GroupIn &gi, int T, int tid0, int nthreads)
 {
     const int nslot = T * K;
     const int na = min(max(gi.active[0], 0), min(nslot, E));
-    for (int i = tid0; i <= 32 * na; i += nthreads)
-        gi.esync[i] = 0;
+    for (int i = tid0; i < na; i += nthreads)
+        gi.esync[1 + SYNC_STRIDE * i] = 0;
     for (int i = tid0; i <= na; i += nthreads) {
         if (i == 0) {
             gi.erec[0] = make_int4(na, 0, 0, 0);
@@ -174,6 +174,43 @@ __device__ inline bool ranks_before(float p, int e, float q, int f)
     return p > q || (p == q && e < f);
 }
 
+// Maximum of v over the wave as signed integers, returned uniform.  For the
+// bits of floats that are >= 0 or negative (a removed candidate is -1) the
+// integer order is the float order, and the integer maximum needs no NaN
+// canonicalisation: each step is one v_max_i32 with the DPP operand folded in.
+__device__ inline int wave_max_i(int v)
+{
+    asm("s_nop 1\n\t"
+        "v_max_i32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_i32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_i32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_i32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_i32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_i32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+v"(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Zero the experts kernel's per-call counters: the per-(token, 32 output
+// rows) slot counters and the per-active-expert item counters.
+__device__ inline void zero_counters(int32_t *cdone, int32_t *esync, int T, int i0, int n)
+{
+    if (cdone)
+        for (int i = i0; i < T * (H / 32); i += n)
+            cdone[i] = 0;
+    if (esync) {
+        const int amax = T * K < E ? T * K : E;
+        for (int i = i0; i < amax; i += n)
+            esync[1 + SYNC_STRIDE * i] = 0;
+    }
+}
+
 __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
     const float *__restrict__ lraw, const float *__restrict__ inv_rms, const float *__restrict__ bias,
     int T, int32_t *__restrict__ ids, float *__restrict__ wout, int group,
@@ -186,6 +223,12 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
     __shared__ int first[E];                // first slot of each expert
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = T * K;
+    // Waves without a token zero the counters at once; with a full window the
+    // token waves do it after reading the logits (one counter orders a wave's
+    // loads and stores).
+    const bool zero_early = T < DECODE_T_MAX;
+    if (zero_early && wave >= T)
+        zero_counters(cdone, esync, T, tid - 64 * T, RT_THREADS - 64 * T);
     if (group) {
         for (int i = tid; i < E; i += RT_THREADS) {
             cnt[i] = 0;
@@ -249,8 +292,14 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             // the best head: the largest p, and among equal p the lowest id
-            const float bp = wave_max63(p[0]);
-            const int be = wave_min63(p[0] == bp ? e[0] : 0x7fffffff);
+            // (the one lane holding the maximum, else a reduction over ids)
+            const int hb = __float_as_int(p[0]);
+            const int bb = wave_max_i(hb);
+            const float bp = __int_as_float(bb);
+            const unsigned long long tie = __ballot(hb == bb);
+            const int be = __popcll(tie) == 1
+                               ? __builtin_amdgcn_readlane(e[0], (int)__builtin_ctzll(tie))
+                               : wave_min63(hb == bb ? e[0] : 0x7fffffff);
             const bool pop = e[0] == be;
 #pragma unroll
             for (int i = 0; i < 7; ++i) {
@@ -275,15 +324,8 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
             }
         }
     }
-    // The experts kernel's counters start at zero: its per-(token, 32 rows)
-    // slot counters and per-expert item counters.  (Stored after the logits
-    // are read: one counter orders a wave's loads and stores.)
-    if (cdone)
-        for (int i = tid; i < T * (H / 32); i += RT_THREADS)
-            cdone[i] = 0;
-    if (esync)
-        for (int i = tid; i <= 32 * E; i += RT_THREADS)
-            esync[i] = 0;
+    if (!zero_early)
+        zero_counters(cdone, esync, T, tid, RT_THREADS);
     if (!group)
         return;
     lds_barrier();
