@@ -16,9 +16,8 @@ hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_it
                        int32_t *mlist, int32_t *nitems, hipStream_t st);
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
                                int rmsnorm, float *lraw, XQ xq, bool prep, int32_t *ids,
-                               float *w, int group, int32_t *offsets, int32_t *slots,
-                               int32_t *active, int4 *erec, int32_t *cdone, int32_t *esync,
-                               hipStream_t st);
+                               float *w, int group, int32_t *slots, int4 *erec, int32_t *cdone,
+                               int32_t *esync, hipStream_t st);
 hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const int32_t *offsets,
                               const int32_t *slots, const int32_t *active, int4 *erec,
                               int32_t *esync, hipStream_t st);
@@ -171,7 +170,7 @@ int strata_moe_route(const float *x, int T, const uint16_t *router, const float 
     const int rms = flags & STRATA_RMSNORM;
     if (is_decode(T)) {
         STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, false, ids, w, 0,
-                                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st));
+                                       nullptr, nullptr, nullptr, nullptr, st));
     } else {
         STRATA_TRY(launch_prep(x, T, rms, c.xsplit, nullptr, st));
         STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
@@ -256,8 +255,7 @@ int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
     const int rms = flags & STRATA_RMSNORM;
     if (is_decode(T)) {
         STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, true, ids_o, w_o, 1,
-                                       c.offsets, c.slots, c.active, c.erec, c.cdone, c.esync,
-                                       st));
+                                       c.slots, c.erec, c.cdone, c.esync, st));
     } else {
         STRATA_TRY(launch_prep(x, T, rms, c.xsplit, c.xperm, st));
         STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));

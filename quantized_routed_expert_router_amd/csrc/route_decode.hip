@@ -19,10 +19,11 @@
 //              reductions, a sorting network on each lane's 8 candidates, then
 //              ten rounds of a wave-wide max of p and min of the id among the
 //              maxima -- the order (p desc, id asc) -- and the clamped renorm).
-//              Wave 0 then groups the T*10 slots by expert: counts, offsets,
-//              the active list, stable slot order and one work record per
-//              active expert for the expert kernels (and, for the layer, the
-//              zeroed slot counters with which dec_down finishes the combine).
+//              For the layer, wave 0 then groups the T*10 slots by expert
+//              with ballots over the bits of the expert ids (stable slot
+//              order and one work record per active expert for the experts
+//              kernel), and the waves without a token zero the experts
+//              kernel's counters.
 #include "common.hpp"
 #include "quant.hpp"
 
@@ -211,16 +212,101 @@ __device__ inline void zero_counters(int32_t *cdone, int32_t *esync, int T, int 
     }
 }
 
+// Grouping of the N = T * K slots by expert, in one wave: slot s (lane s % 64
+// of chunk s / 64) has expert sid[s].  Ten ballots over the bits of a chunk's
+// ids (1023 past the end) give every lane the masks of that chunk's slots
+// whose expert is below its own (lt) and equal to it (eq), comparing bits
+// from the top.  Then, for slot s of expert e:
+//   less  = slots of the experts below e       (where e's run starts)
+//   rank  = slots of e before s                (stable order)
+//   below = active experts below e             (e's record index)
+// slots[less + rank] = s, and the first slot of e writes e's record
+// {e, less, slots of e, s}; erec[0].x is the number of active experts.
+__device__ inline int chunk_expert(const int *sid, int N, int c, int lane)
+{
+    return 64 * c + lane < N ? sid[64 * c + lane] : 1023;
+}
+
+// lt / eq masks of the lane's expert e against the experts m of one chunk.
+__device__ inline void compare_chunk(int e, int m, unsigned long long &lt, unsigned long long &eq)
+{
+    unsigned long long l = 0, q = ~0ull;
+#pragma unroll
+    for (int b = 9; b >= 0; --b) {
+        const unsigned long long bm = __ballot((m >> b) & 1);
+        const bool one = (e >> b) & 1;
+        l |= one ? (q & ~bm) : 0ull;
+        q &= one ? bm : ~bm;
+    }
+    lt = l;
+    eq = q;
+}
+
+template <int NC>
+__device__ inline void group_slots(const int *sid, int N, int32_t *slots, int4 *erec, int lane)
+{
+    unsigned long long first[NC], lt0 = 0;
+    int less[NC], rank[NC], cnt[NC];
+#pragma unroll
+    for (int c0 = 0; c0 < NC; ++c0) {
+        const int e = chunk_expert(sid, N, c0, lane);
+        less[c0] = 0;
+        rank[c0] = 0;
+        cnt[c0] = 0;
+        unsigned long long self = 0;
+#pragma unroll 1
+        for (int c = 0; c < NC; ++c) {
+            unsigned long long lt, eq;
+            compare_chunk(e, chunk_expert(sid, N, c, lane), lt, eq);
+            less[c0] += __popcll(lt);
+            cnt[c0] += __popcll(eq);
+            if (c < c0)
+                rank[c0] += __popcll(eq);
+            if (c == c0)
+                self = eq;
+            if (NC == 1)
+                lt0 = lt;
+        }
+        rank[c0] += __builtin_amdgcn_mbcnt_hi((uint32_t)(self >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)self, 0));
+        first[c0] = __ballot(64 * c0 + lane < N && rank[c0] == 0);
+    }
+    int na = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        na += __popcll(first[c]);
+#pragma unroll
+    for (int c0 = 0; c0 < NC; ++c0) {
+        const int e = chunk_expert(sid, N, c0, lane);
+        int below = 0;
+        if (NC == 1) {
+            below = __popcll(lt0 & first[0]);
+        } else {
+#pragma unroll 1
+            for (int c = 0; c < NC; ++c) {
+                unsigned long long lt, eq;
+                compare_chunk(e, chunk_expert(sid, N, c, lane), lt, eq);
+                below += __popcll(lt & first[c]);
+            }
+        }
+        const int s = 64 * c0 + lane;
+        if (s < N) {
+            slots[less[c0] + rank[c0]] = s;
+            if (rank[c0] == 0)
+                erec[1 + below] = make_int4(e, less[c0], cnt[c0], s);
+        }
+    }
+    if (lane == 0)
+        erec[0] = make_int4(na, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
     const float *__restrict__ lraw, const float *__restrict__ inv_rms, const float *__restrict__ bias,
     int T, int32_t *__restrict__ ids, float *__restrict__ wout, int group,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ slots, int32_t *__restrict__ active,
-    int4 *__restrict__ erec, int32_t *__restrict__ cdone, int32_t *__restrict__ esync)
+    int32_t *__restrict__ slots, int4 *__restrict__ erec, int32_t *__restrict__ cdone,
+    int32_t *__restrict__ esync)
 {
     __shared__ int sid[DECODE_T_MAX * K];   // expert of each slot
-    __shared__ int cnt[E];                  // slots per expert
-    __shared__ int cur[E];                  // slots placed so far, per expert
-    __shared__ int first[E];                // first slot of each expert
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = T * K;
     // Waves without a token zero the counters at once; with a full window the
@@ -229,13 +315,6 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
     const bool zero_early = T < DECODE_T_MAX;
     if (zero_early && wave >= T)
         zero_counters(cdone, esync, T, tid - 64 * T, RT_THREADS - 64 * T);
-    if (group) {
-        for (int i = tid; i < E; i += RT_THREADS) {
-            cnt[i] = 0;
-            cur[i] = 0;
-        }
-        lds_barrier();
-    }
     if (wave < T) {
         const int t = wave;
         const float sc = inv_rms[t];
@@ -318,10 +397,8 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
         if (lane < K) {
             ids[(size_t)t * K + lane] = my_id;
             wout[(size_t)t * K + lane] = my_p / den;
-            if (group) {
+            if (group)
                 sid[t * K + lane] = my_id;
-                atomicAdd(&cnt[my_id], 1);
-            }
         }
     }
     if (!zero_early)
@@ -331,70 +408,18 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
     lds_barrier();
     if (wave != 0)
         return;
-    // Wave 0: lane l owns experts 8 l .. 8 l + 7.
-    int c[8], incl = 0, fl = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        c[j] = cnt[8 * lane + j];
-        incl += c[j];
-        fl += c[j] > 0;
-    }
-    const int cbase = wave_incl_scan(incl) - incl;   // slots of the lower experts
-    const int abase = wave_incl_scan(fl) - fl;       // active experts below
-    {
-        int o = cbase, a = abase;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int ex = 8 * lane + j;
-            offsets[ex] = o;
-            cnt[ex] = o;   // from here on: the expert's first grouped slot
-            if (c[j] > 0)
-                active[1 + a++] = ex;
-            o += c[j];
-        }
-        if (lane == 63) {
-            offsets[E] = o;
-            active[0] = a;
-            erec[0] = make_int4(a, 0, 0, 0);
-        }
-    }
-    // Stable placement: slot s goes after the earlier slots of its expert.
-    for (int s0 = 0; s0 < N; s0 += 64) {
-        const int s = s0 + lane;
-        const int my_e = s < N ? sid[s] : -1;
-        unsigned long long same = __ballot(my_e >= 0);
-#pragma unroll
-        for (int bit = 0; bit < 9; ++bit) {
-            const unsigned long long bits = __ballot(my_e >= 0 && ((my_e >> bit) & 1));
-            same &= ((my_e >> bit) & 1) ? bits : ~bits;
-        }
-        if (my_e >= 0) {
-            const int before = __popcll(same & ((1ull << lane) - 1ull));
-            const int rank = cur[my_e] + before;
-            slots[cnt[my_e] + rank] = s;
-            if (rank == 0)
-                first[my_e] = s;
-            if (before == 0)   // the lowest lane of the group advances the count
-                cur[my_e] += __popcll(same);
-        }
-    }
-    // one work record per active expert: {e, first grouped slot, count, first slot}
-    {
-        int a = abase;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int ex = 8 * lane + j;
-            if (c[j] > 0)
-                erec[1 + a++] = make_int4(ex, cnt[ex], c[j], first[ex]);
-        }
-    }
+    if (N <= 64)
+        group_slots<1>(sid, N, slots, erec, lane);
+    else if (N <= 128)
+        group_slots<2>(sid, N, slots, erec, lane);
+    else
+        group_slots<3>(sid, N, slots, erec, lane);
 }
 
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
                                int rmsnorm, float *lraw, XQ xq, bool prep, int32_t *ids,
-                               float *w, int group, int32_t *offsets, int32_t *slots,
-                               int32_t *active, int4 *erec, int32_t *cdone, int32_t *esync,
-                               hipStream_t st)
+                               float *w, int group, int32_t *slots, int4 *erec, int32_t *cdone,
+                               int32_t *esync, hipStream_t st)
 {
     const GroupIn none{nullptr, nullptr, nullptr, nullptr, nullptr};
     if (prep)
@@ -404,7 +429,7 @@ hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const f
         hipLaunchKernelGGL((rdec_gemv<true, false>), dim3(E), dim3(RG_THREADS), 0, st, x, T, R,
                            lraw, xq, rmsnorm, none);
     hipLaunchKernelGGL(rdec_topk, dim3(1), dim3(RT_THREADS), 0, st, lraw, xq.inv_rms, bias, T, ids,
-                       w, group, offsets, slots, active, erec, cdone, esync);
+                       w, group, slots, erec, cdone, esync);
     return hipGetLastError();
 }
 
