@@ -92,83 +92,163 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
 // x1 + x2 + x3 (x1 = bf16(x), x2 = bf16(x - x1), x3 = bf16(x - x1 - x2):
 // together all 24 bits of the fp32 significand), and bf16 x bf16 products are
 // exact in the fp32 accumulation, so the logits keep fp32 accuracy.  Every
-// logit is the same sequence of MFMAs over K, so identical router rows give
-// identical logits.  Workgroup: 16 tokens x 128 experts, wave w owns experts
-// 32 w .. 32 w + 31 (two 16-expert subtiles); K in steps of 32, the operands
-// of four steps in flight.
+// logit is the same sequence of MFMAs (K ascending in steps of 32, the three
+// terms in turn), so identical router rows give identical logits.
+//
+// Workgroup tile: 32 tokens x 128 experts; wave w owns experts 32 w .. + 31,
+// all 32 tokens (2 x 2 subtiles of 16 x 16).  K goes in stages of 64: both
+// operands of a stage (the three x terms of 32 rows and 128 router rows, 64
+// bf16 each) reach LDS by direct global-to-LDS loads into one of four
+// buffers, three stages ahead, one barrier per stage.  Rows are 128 bytes in
+// LDS with 16-byte chunk c of row r at position c ^ (r % 8), so the fragment
+// reads of 16 consecutive rows fall in distinct banks.  The LDS reads are
+// inline assembly because the compiler would otherwise wait for every
+// outstanding LDS-bound load before each of them.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-constexpr int GR_M = 16, GR_N = 128, GR_KS = 32, GR_STEPS = H / GR_KS;
-static_assert(GR_STEPS % 4 == 0 && E % GR_N == 0, "router GEMM tiling");
+constexpr int GR_M = 32, GR_N = 128, GR_SK = 64, GR_STAGES = H / GR_SK;
+constexpr int GR_NBUF = 4;
+constexpr int GR_ABYTES = 3 * GR_M * GR_SK * 2;                 // 12,288
+constexpr int GR_BBYTES = GR_N * GR_SK * 2;                     // 16,384
+constexpr int GR_BUF = GR_ABYTES + GR_BBYTES;                   // 28,672
+constexpr int GR_REQ = GR_BUF / 16 / 256;                       // 7 requests per lane per stage
+static_assert(GR_REQ * 16 * 256 == GR_BUF && GR_ABYTES == 3 * 256 * 16, "request split");
+static_assert(E % GR_N == 0 && H % GR_SK == 0 && GR_STAGES >= GR_NBUF - 1, "router GEMM tiling");
 
-struct GrOps {
-    uint4 a[3];   // x1, x2, x3: 8 bf16 of row lane % 16 at K 8 (lane / 16) ..
-    uint4 b[2];   // 8 bf16 router values per expert subtile
-};
-
-__device__ inline void gr_load(GrOps &o, const uint16_t *xa, const uint16_t *rb0, const uint16_t *rb1,
-                               int step)
+typedef __attribute__((address_space(3))) uint8_t gr_lds_u8;
+__device__ inline uint32_t gr_lds_addr(uint8_t *p)
 {
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-        o.a[j] = *reinterpret_cast<const uint4 *>(xa + (size_t)j * H + GR_KS * step);
-    o.b[0] = *reinterpret_cast<const uint4 *>(rb0 + GR_KS * step);
-    o.b[1] = *reinterpret_cast<const uint4 *>(rb1 + GR_KS * step);
+    return (uint32_t)(uintptr_t)(gr_lds_u8 *)p;
 }
 
-__device__ inline void gr_step(const GrOps &o, floatx4 acc[2])
+template <int N> __device__ inline void gr_vm_wait()
 {
-    const bf16x8 b0 = __builtin_bit_cast(bf16x8, o.b[0]);
-    const bf16x8 b1 = __builtin_bit_cast(bf16x8, o.b[1]);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// The operand fragments of one stage for one wave: a[s][term][mi], b[s][ni]
+// (K-step s of the stage, token subtile mi, expert subtile ni).
+struct GrFrag {
+    uint4 a[2][3][2];
+    uint4 b[2][2];
+};
+
+// Reads of one stage's fragments; va[s] / vb[s] are this lane's A / B read
+// addresses for K-step s (the subtile and term offsets are immediates).
+__device__ inline void gr_reads(uint32_t va0, uint32_t va1, uint32_t vb0, uint32_t vb1, GrFrag &f)
+{
+    asm volatile("ds_read_b128 %0, %16 offset:0\n\t"
+                 "ds_read_b128 %1, %16 offset:2048\n\t"
+                 "ds_read_b128 %2, %16 offset:4096\n\t"
+                 "ds_read_b128 %3, %16 offset:6144\n\t"
+                 "ds_read_b128 %4, %16 offset:8192\n\t"
+                 "ds_read_b128 %5, %16 offset:10240\n\t"
+                 "ds_read_b128 %6, %18 offset:0\n\t"
+                 "ds_read_b128 %7, %18 offset:2048\n\t"
+                 "ds_read_b128 %8, %17 offset:0\n\t"
+                 "ds_read_b128 %9, %17 offset:2048\n\t"
+                 "ds_read_b128 %10, %17 offset:4096\n\t"
+                 "ds_read_b128 %11, %17 offset:6144\n\t"
+                 "ds_read_b128 %12, %17 offset:8192\n\t"
+                 "ds_read_b128 %13, %17 offset:10240\n\t"
+                 "ds_read_b128 %14, %19 offset:0\n\t"
+                 "ds_read_b128 %15, %19 offset:2048\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(f.a[0][0][0]), "=&v"(f.a[0][0][1]), "=&v"(f.a[0][1][0]), "=&v"(f.a[0][1][1]),
+                   "=&v"(f.a[0][2][0]), "=&v"(f.a[0][2][1]), "=&v"(f.b[0][0]), "=&v"(f.b[0][1]),
+                   "=&v"(f.a[1][0][0]), "=&v"(f.a[1][0][1]), "=&v"(f.a[1][1][0]), "=&v"(f.a[1][1][1]),
+                   "=&v"(f.a[1][2][0]), "=&v"(f.a[1][2][1]), "=&v"(f.b[1][0]), "=&v"(f.b[1][1])
+                 : "v"(va0), "v"(va1), "v"(vb0), "v"(vb1)
+                 : "memory");
+}
+
+__device__ inline void gr_math(const GrFrag &f, floatx4 acc[2][2])
+{
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const bf16x8 xj = __builtin_bit_cast(bf16x8, o.a[j]);
-        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xj, b0, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xj, b1, acc[1], 0, 0, 0);
-    }
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, f.a[s][j][mi]),
+                        __builtin_bit_cast(bf16x8, f.b[s][ni]), acc[mi][ni], 0, 0, 0);
 }
 
 __global__ __launch_bounds__(256) void gemm_kernel(
     const uint16_t *__restrict__ xsplit, int T, const uint16_t *__restrict__ R,
     const float *__restrict__ bias, float *__restrict__ logits)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[GR_NBUF * GR_BUF];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int l = lane & 15, q = lane >> 4;
-    const int m0 = blockIdx.x * GR_M;
-    const int n0 = blockIdx.y * GR_N + 32 * wave;
-    const int m = min(m0 + l, T - 1);   // rows past T compute a copy and are not stored
-    const uint16_t *xa = xsplit + (size_t)m * 3 * H + 8 * q;
-    const uint16_t *rb0 = R + (size_t)(n0 + l) * H + 8 * q;
-    const uint16_t *rb1 = rb0 + (size_t)16 * H;
-    floatx4 acc[2] = {(floatx4){0.f, 0.f, 0.f, 0.f}, (floatx4){0.f, 0.f, 0.f, 0.f}};
-    GrOps p0, p1, p2, p3;
-    gr_load(p0, xa, rb0, rb1, 0);
-    gr_load(p1, xa, rb0, rb1, 1);
-    gr_load(p2, xa, rb0, rb1, 2);
-    gr_load(p3, xa, rb0, rb1, 3);
-    // the last four loads re-read the last step (never used), so every
-    // iteration issues the same loads
-#pragma unroll 1
-    for (int s = 0; s < GR_STEPS; s += 4) {
-        gr_step(p0, acc);
-        gr_load(p0, xa, rb0, rb1, min(s + 4, GR_STEPS - 1));
-        gr_step(p1, acc);
-        gr_load(p1, xa, rb0, rb1, min(s + 5, GR_STEPS - 1));
-        gr_step(p2, acc);
-        gr_load(p2, xa, rb0, rb1, min(s + 6, GR_STEPS - 1));
-        gr_step(p3, acc);
-        gr_load(p3, xa, rb0, rb1, min(s + 7, GR_STEPS - 1));
-    }
+    const int m0 = blockIdx.x * GR_M, n0 = blockIdx.y * GR_N;
+    // This lane's source of LDS chunk Q = 256 i + 64 wave + lane of a stage
+    // buffer, i = 0..6: chunks 0..767 are the x terms (term, row, position),
+    // the rest the router rows (row, position); chunk c = position ^ (row % 8).
+    const uint8_t *src[GR_REQ];
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
-        const int n = n0 + 16 * ns + l;
+    for (int i = 0; i < GR_REQ; ++i) {
+        const int Q = 256 * i + 64 * wave + lane;
+        if (i < 3) {
+            const int row = (Q >> 3) & 31, c = (Q & 7) ^ (row & 7);
+            const int m = min(m0 + row, T - 1);   // rows past T load a copy, never stored
+            src[i] = reinterpret_cast<const uint8_t *>(xsplit + ((size_t)m * 3 + i) * H + 8 * c);
+        } else {
+            const int row = (Q - 768) >> 3, c = (Q & 7) ^ (row & 7);
+            src[i] = reinterpret_cast<const uint8_t *>(R + (size_t)(n0 + row) * H + 8 * c);
+        }
+    }
+    // stage k of K into the buffer of stage slot
+    auto request = [&](int k, int slot) {
+        uint8_t *buf = lds + (slot % GR_NBUF) * GR_BUF;
+#pragma unroll
+        for (int i = 0; i < GR_REQ; ++i)
+            __builtin_amdgcn_global_load_lds(src[i] + GR_SK * 2 * k,
+                                             buf + (256 * i + 64 * wave) * 16, 16, 0, 0);
+    };
+    // this lane's fragment read addresses in buffer 0, per K-step s of a stage
+    const uint32_t off0 = 16 * ((0 + q) ^ (l & 7)), off1 = 16 * ((4 + q) ^ (l & 7));
+    const uint32_t ra = gr_lds_addr(lds) + l * 128;
+    const uint32_t rb = gr_lds_addr(lds) + GR_ABYTES + (32 * wave + l) * 128;
+    floatx4 acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    request(0, 0);
+    request(1, 1);
+    request(2, 2);
+#pragma unroll 1
+    for (int st = 0; st < GR_STAGES; ++st) {
+        gr_vm_wait<2 * GR_REQ>();   // this stage landed; the two younger stages may not have
+        __builtin_amdgcn_s_barrier();
+        // the buffer of stage st - 1 is free: stage st + 3 goes there (past
+        // the end the last stage again, into that same free buffer, never
+        // read: every iteration issues the same number of requests)
+        request(min(st + GR_NBUF - 1, GR_STAGES - 1), st + GR_NBUF - 1);
+        const uint32_t bo = (st % GR_NBUF) * GR_BUF;
+        GrFrag f;
+        gr_reads(ra + bo + off0, ra + bo + off1, rb + bo + off0, rb + bo + off1, f);
+        gr_math(f, acc);
+    }
+    gr_vm_wait<0>();
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        const int n = n0 + 32 * wave + 16 * ni + l;
         const float bn = bias ? bias[n] : 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int mr = m0 + 4 * q + r;
-            if (mr < T)
-                logits[(size_t)mr * E + n] = acc[ns][r] + bn;
-        }
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int mr = m0 + 16 * mi + 4 * q + r;
+                if (mr < T)
+                    logits[(size_t)mr * E + n] = acc[mi][ni][r] + bn;
+            }
     }
 }
 
