@@ -17,7 +17,7 @@ namespace strata {
 
 constexpr int GR_THREADS = 1024;
 constexpr int GR_WAVES = GR_THREADS / 64;
-constexpr int GR_BATCH = 8;   // 64-slot steps whose ids are loaded together
+constexpr int GR_BATCH = 24;  // 64-slot steps whose ids are loaded together
 
 __device__ inline int block_exclusive_scan_512(int v, int tid, int *tmp, int *total)
 {
@@ -64,15 +64,24 @@ __global__ __launch_bounds__(GR_THREADS) void group_kernel(const int32_t *__rest
 
     for (int i = tid; i < GR_WAVES * E; i += GR_THREADS)
         (&hist[0][0])[i] = 0;
-    __syncthreads();
-    // the ids are read eight 64-slot steps at a time, so their loads overlap
+    // The ids are read GR_BATCH 64-slot steps at a time, so their loads
+    // overlap; when a wave's slice fits one batch (T <= 2457), the ids stay in
+    // registers for the scatter too.
     const int steps = (S + 63) / 64;
-    for (int it0 = 0; it0 < steps; it0 += GR_BATCH) {
-        int ev[GR_BATCH];
+    int ev[GR_BATCH];
 #pragma unroll
-        for (int j = 0; j < GR_BATCH; ++j) {
-            const int i = beg + (it0 + j) * 64 + lane;
-            ev[j] = i < end ? ids[i] : -1;
+    for (int j = 0; j < GR_BATCH; ++j) {
+        const int i = beg + j * 64 + lane;
+        ev[j] = i < end ? ids[i] : -1;
+    }
+    __syncthreads();
+    for (int it0 = 0; it0 < steps; it0 += GR_BATCH) {
+        if (it0 > 0) {
+#pragma unroll
+            for (int j = 0; j < GR_BATCH; ++j) {
+                const int i = beg + (it0 + j) * 64 + lane;
+                ev[j] = i < end ? ids[i] : -1;
+            }
         }
 #pragma unroll
         for (int j = 0; j < GR_BATCH; ++j)
@@ -111,11 +120,12 @@ __global__ __launch_bounds__(GR_THREADS) void group_kernel(const int32_t *__rest
     // (hist[wave]) are its own, and LDS keeps one wave's accesses in order.
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
     for (int it0 = 0; it0 < steps; it0 += GR_BATCH) {
-        int ev[GR_BATCH];
+        if (steps > GR_BATCH) {
 #pragma unroll
-        for (int j = 0; j < GR_BATCH; ++j) {
-            const int i = beg + (it0 + j) * 64 + lane;
-            ev[j] = i < end ? ids[i] : -1;
+            for (int j = 0; j < GR_BATCH; ++j) {
+                const int i = beg + (it0 + j) * 64 + lane;
+                ev[j] = i < end ? ids[i] : -1;
+            }
         }
 #pragma unroll
         for (int j = 0; j < GR_BATCH; ++j) {
