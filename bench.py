@@ -38,6 +38,7 @@ WORKLOADS = {
     "window-corr": dict(cfg=5, T=4, layers=1, copies=48),
     "token": dict(cfg=0, T=1, layers=1, copies=48),
     "stack-decode": dict(cfg=2, T=1, layers=48, copies=1),
+    "stack-decode-lookahead": dict(cfg=2, T=1, layers=48, copies=1, lookahead=True),
     "prefill": dict(cfg=3, T=2048, layers=1, copies=4),
     "stack-prefill": dict(cfg=4, T=2048, layers=48, copies=1),
 }
@@ -143,12 +144,27 @@ def main():
     w = torch.empty((T, 10), device="cuda")
     torch.cuda.synchronize()
 
+    lookahead = bool(wl.get("lookahead"))
+    pred_t = [torch.empty((T, 10), dtype=torch.int32, device="cuda") for _ in range(L)]
+
+    def layer_call(l, i, ids_o, stream):
+        """Layer l (store copy i for single layers); with the lookahead, layers
+        0 .. L-2 also predict layer l+1's experts and warm its blobs."""
+        if lookahead and l + 1 < L:
+            m.strata_moe_layer_lookahead(
+                xd, Rd[i], store[i * per_layer:(i + 1) * per_layer], ws, Rd[i + 1],
+                store[(i + 1) * per_layer:(i + 2) * per_layer],
+                bias=None if bd is None else bd[l], bias_next=None if bd is None else bd[l + 1],
+                flags=flags, y=y, ids=ids_o, w=w, pred=pred_t[l], stream=stream)
+        else:
+            m.strata_moe_layer(xd, Rd[i], store[i * per_layer:(i + 1) * per_layer], ws,
+                               bias=None if bd is None else bd[l], flags=flags, y=y, ids=ids_o,
+                               w=w, stream=stream)
+
     def one_step(i, stream=None):
         if stack:
             for l in range(L):
-                m.strata_moe_layer(xd, Rd[l], store[l * per_layer:(l + 1) * per_layer], ws,
-                                   bias=None if bd is None else bd[l], flags=flags, y=y, ids=ids,
-                                   w=w, stream=stream)
+                layer_call(l, l, ids, stream)
         else:
             c = i % copies
             m.strata_moe_layer(xd, Rd[c], store[c * per_layer:(c + 1) * per_layer], ws,
@@ -217,9 +233,7 @@ def main():
                 e1.record(stream)
                 m.strata_moe_time_next_kernel(e0, e1)
                 l = i if stack else 0                  # layer (store copy i otherwise)
-                m.strata_moe_layer(xd, Rd[i], store[i * per_layer:(i + 1) * per_layer], ws,
-                                   bias=None if bd is None else bd[l], flags=flags, y=y,
-                                   ids=ids_t[l], w=w, stream=stream)
+                layer_call(l, i, ids_t[l], stream)
                 if p > 0:
                     evs.append((e0, e1, l))
     torch.cuda.synchronize()
@@ -285,6 +299,19 @@ def main():
         "expert_bytes_per_step": step_bytes, "wall_s": wall,
         "roofline": roof,
     }
+    if lookahead:
+        # How often a routed expert of layer l+1 was among those predicted
+        # (and warmed) while layer l ran, over the eager pass's tokens.
+        hits = []
+        pbytes = 0
+        for l in range(L - 1):
+            nxt, prd = ids_t[l + 1].cpu().numpy(), pred_t[l].cpu().numpy()
+            hits += [len(set(nxt[t]) & set(prd[t])) / 10.0 for t in range(T)]
+            pbytes += int(np.unique(prd).size) * blob
+        res["lookahead"] = {"hit_rate": float(np.mean(hits)),
+                            "prefetched_bytes_per_step": pbytes,
+                            "note": "prefetched bytes are read in addition to the routed "
+                                    "experts' own; tok/s counts the whole 48-layer step"}
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(a, x, routers, biases, seed, stack, T, blob)
     print(json.dumps(res))

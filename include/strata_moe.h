@@ -54,6 +54,7 @@ extern "C" {
 #define STRATA_MOE_BB 18       /* bytes per Q2_0 block: fp16 scale, 16 code bytes */
 #define STRATA_MOE_BLOB 1382400 /* bytes per expert blob: gate, up, down */
 #define STRATA_MOE_T_MAX 8192  /* largest token count per call (one prefill chunk) */
+#define STRATA_LOOKAHEAD_T_MAX 8 /* largest token count of strata_moe_layer_lookahead */
 
 /* Status codes. */
 #define STRATA_OK 0
@@ -138,6 +139,27 @@ STRATA_API int strata_moe_combine(const float *out, const float *w, int T, int f
 STRATA_API int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
                      const uint8_t *blobs, int flags, float *y, int32_t *ids, float *w,
                      void *ws, size_t ws_bytes, void *stream);
+
+/* The layer with a router lookahead ([ZW], the passage on prefetching and
+ * warm-up: the next layer's router is run on this layer's MoE input, because
+ * the residual stream changes little between adjacent layers, to predict the
+ * next layer's experts and warm their bytes without changing any result).
+ * Does exactly what strata_moe_layer does with the first nine arguments, with
+ * bitwise the same outputs, and in the same launches:
+ *  - routes the same normalised input through router_next [E][H] bf16 (plus
+ *    bias_next [E] fp32, or NULL) to that layer's ten ids per token, written
+ *    to pred_ids [T][K] int32 (or kept in the workspace when NULL);
+ *  - reads the predicted experts' blobs in blobs_next (the next layer's store,
+ *    [E][BLOB], 256-byte aligned) once, line by line, in the experts kernel's
+ *    tail, so that they sit in the memory-side cache when the next layer runs.
+ * Nothing is written to blobs_next and no result depends on it.
+ * T must be 1..STRATA_LOOKAHEAD_T_MAX (decode); other T return STRATA_E_SHAPE.
+ * router_next and blobs_next must not be NULL (STRATA_E_ARG). */
+STRATA_API int strata_moe_layer_lookahead(float *x, int T, const uint16_t *router,
+                               const float *bias, const uint8_t *blobs, int flags, float *y,
+                               int32_t *ids, float *w, const uint16_t *router_next,
+                               const float *bias_next, const uint8_t *blobs_next,
+                               int32_t *pred_ids, void *ws, size_t ws_bytes, void *stream);
 
 /* Measurement hook (not part of the layer's math): arms the next
  * strata_moe_experts or strata_moe_layer call made by this host thread to

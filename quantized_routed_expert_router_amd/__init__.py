@@ -16,12 +16,14 @@ LIB_PATH = os.path.join(HERE, "libstrata_moe.so")
 H, FF, E, K, QK, BB = 2560, 640, 512, 10, 64, 18
 BLOB = 1382400
 T_MAX = 8192
+LOOKAHEAD_T_MAX = 8
 RMSNORM, RESIDUAL = 1, 2
 OK, E_ARG, E_SHAPE, E_WORKSPACE, E_HIP, E_ALIGN = 0, -1, -2, -3, -4, -5
 
 EXPORTS = ("strata_moe_blob_bytes", "strata_moe_workspace_bytes", "strata_moe_route",
            "strata_moe_group", "strata_moe_experts", "strata_moe_combine", "strata_moe_layer",
-           "strata_moe_time_next_kernel", "strata_moe_status_string")
+           "strata_moe_layer_lookahead", "strata_moe_time_next_kernel",
+           "strata_moe_status_string")
 
 _lib = None
 
@@ -55,6 +57,9 @@ def lib():
         L.strata_moe_combine.argtypes = [vp, vp, i32, i32, vp, vp]
         L.strata_moe_layer.restype = i32
         L.strata_moe_layer.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.strata_moe_layer_lookahead.restype = i32
+        L.strata_moe_layer_lookahead.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                                 vp, vp, sz, vp]
         L.strata_moe_time_next_kernel.restype = i32
         L.strata_moe_time_next_kernel.argtypes = [vp, vp]
         L.strata_moe_status_string.restype = ctypes.c_char_p
@@ -182,3 +187,16 @@ def strata_moe_layer(x, router, blobs, ws, bias=None, flags=0, y=None, ids=None,
                                 _p(y, torch.float32), _p(ids, torch.int32), _p(w, torch.float32),
                                 _p(ws), _nbytes(ws), _s(stream))
     _check("strata_moe_layer", rc)
+
+
+def strata_moe_layer_lookahead(x, router, blobs, ws, router_next, blobs_next, bias=None,
+                               bias_next=None, flags=0, y=None, ids=None, w=None, pred=None,
+                               stream=None):
+    import torch
+    T = x.shape[0]
+    rc = lib().strata_moe_layer_lookahead(
+        _p(x, torch.float32), T, _p_router(router), _p(bias, torch.float32),
+        _p(blobs, torch.uint8), flags, _p(y, torch.float32), _p(ids, torch.int32),
+        _p(w, torch.float32), _p_router(router_next), _p(bias_next, torch.float32),
+        _p(blobs_next, torch.uint8), _p(pred, torch.int32), _p(ws), _nbytes(ws), _s(stream))
+    _check("strata_moe_layer_lookahead", rc)

@@ -17,14 +17,16 @@ hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_it
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
                                int rmsnorm, float *lraw, XQ xq, bool prep, int32_t *ids,
                                float *w, int group, int32_t *slots, int4 *erec, int32_t *cdone,
-                               int32_t *esync, hipStream_t st);
+                               int32_t *esync, const uint16_t *R2, const float *bias2,
+                               float *lraw2, int32_t *pred, hipStream_t st);
 hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const int32_t *offsets,
                               const int32_t *slots, const int32_t *active, int4 *erec,
                               int32_t *esync, hipStream_t st);
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
                                  XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
-                                 const float *w, float *y, float *res, hipEvent_t ev0,
-                                 hipEvent_t ev1, hipStream_t st);
+                                 const float *w, float *y, float *res, const int32_t *pred,
+                                 const uint8_t *blobs_next, hipEvent_t ev0, hipEvent_t ev1,
+                                 hipStream_t st);
 hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
@@ -71,6 +73,8 @@ struct Carve {
     int32_t *offsets, *slots, *active, *ids, *mlist, *nitems;
     int4 *erec;
     int32_t *cdone, *esync;
+    float *lraw2;
+    int32_t *pred;
 };
 
 Carve carve(void *ws, int T)
@@ -91,6 +95,8 @@ Carve carve(void *ws, int T)
     c.erec = at<int4>(ws, L.erec);
     c.cdone = at<int32_t>(ws, L.cdone);
     c.esync = at<int32_t>(ws, L.esync);
+    c.lraw2 = at<float>(ws, L.lraw2);
+    c.pred = at<int32_t>(ws, L.pred);
     c.ids = at<int32_t>(ws, L.ids);
     c.w = at<float>(ws, L.w);
     c.mlist = at<int32_t>(ws, L.mlist);
@@ -114,7 +120,7 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
     take_events(e0, e1);
     if (is_decode(T)) {
         STRATA_TRY(launch_decode_experts(blobs, c.erec, slots, c.xq, c.hq, out, T, c.esync, nullptr,
-                                         nullptr, nullptr, nullptr, e0, e1, st));
+                                         nullptr, nullptr, nullptr, nullptr, nullptr, e0, e1, st));
     } else {
         STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
         STRATA_TRY(launch_prefill_experts(blobs, offsets, slots, active, c.mlist, c.nitems,
@@ -136,6 +142,60 @@ int run_prep(const Carve &c, const float *x, int T, int rms, const int32_t *offs
     return STRATA_OK;
 }
 
+// The layer, with an optional lookahead (decode T <= 8): the next layer's
+// router on the same input predicts its experts (pred) and the experts kernel
+// reads their blobs (blobs2) into the memory-side cache.
+int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const uint8_t *blobs,
+               int flags, float *y, int32_t *ids, float *w, const uint16_t *router2,
+               const float *bias2, const uint8_t *blobs2, int32_t *pred, void *ws,
+               size_t ws_bytes, void *stream)
+{
+    int rc = check_T(T);
+    if (rc)
+        return rc;
+    if (!x || !router || !blobs || (flags & ~(STRATA_RMSNORM | STRATA_RESIDUAL)))
+        return STRATA_E_ARG;
+    if (!y && !(flags & STRATA_RESIDUAL))
+        return STRATA_E_ARG;
+    if ((rc = check_ws(ws, ws_bytes, T)))
+        return rc;
+    if (!aligned(x, 16) || !aligned(router, 16) || !aligned(blobs, 256) || !aligned(y, 16) ||
+        !aligned(ids, 4) || !aligned(w, 4) || !aligned(bias, 4))
+        return STRATA_E_ALIGN;
+    if (router2 && (!aligned(router2, 16) || !aligned(blobs2, 256) || !aligned(bias2, 4) ||
+                    !aligned(pred, 4)))
+        return STRATA_E_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    Carve c = carve(ws, T);
+    int32_t *ids_o = ids ? ids : c.ids;
+    float *w_o = w ? w : c.w;
+    int32_t *pred_o = pred ? pred : c.pred;
+    const int rms = flags & STRATA_RMSNORM;
+    if (is_decode(T)) {
+        STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, true, ids_o, w_o, 1,
+                                       c.slots, c.erec, c.cdone, c.esync, router2, bias2, c.lraw2,
+                                       pred_o, st));
+    } else {
+        STRATA_TRY(launch_prep(x, T, rms, c.xsplit, c.xperm, st));
+        STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
+        STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
+        STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, st));
+    }
+    const bool res = flags & STRATA_RESIDUAL;
+    if (is_decode(T)) {   // the experts kernel finishes the combine
+        hipEvent_t e0, e1;
+        take_events(e0, e1);
+        STRATA_TRY(launch_decode_experts(blobs, c.erec, c.slots, c.xq, c.hq, c.out, T, c.esync,
+                                         c.cdone, w_o, y, res ? x : nullptr,
+                                         router2 ? pred_o : nullptr, router2 ? blobs2 : nullptr,
+                                         e0, e1, st));
+        return STRATA_OK;
+    }
+    if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st)))
+        return rc;
+    STRATA_TRY(launch_combine(c.out, w_o, T, y, res ? x : nullptr, 0, st));
+    return STRATA_OK;
+}
 } // namespace
 } // namespace strata
 
@@ -170,7 +230,8 @@ int strata_moe_route(const float *x, int T, const uint16_t *router, const float 
     const int rms = flags & STRATA_RMSNORM;
     if (is_decode(T)) {
         STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, false, ids, w, 0,
-                                       nullptr, nullptr, nullptr, nullptr, st));
+                                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr, st));
     } else {
         STRATA_TRY(launch_prep(x, T, rms, c.xsplit, nullptr, st));
         STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
@@ -236,44 +297,25 @@ int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
                      const uint8_t *blobs, int flags, float *y, int32_t *ids, float *w,
                      void *ws, size_t ws_bytes, void *stream)
 {
-    int rc = check_T(T);
-    if (rc)
-        return rc;
-    if (!x || !router || !blobs || (flags & ~(STRATA_RMSNORM | STRATA_RESIDUAL)))
+    return strata::layer_impl(x, T, router, bias, blobs, flags, y, ids, w, nullptr, nullptr,
+                              nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+static_assert(2 * STRATA_LOOKAHEAD_T_MAX <= strata::DECODE_T_MAX,
+              "the routing workgroup has a wave per token for each of the two routers");
+
+int strata_moe_layer_lookahead(float *x, int T, const uint16_t *router, const float *bias,
+                               const uint8_t *blobs, int flags, float *y, int32_t *ids, float *w,
+                               const uint16_t *router_next, const float *bias_next,
+                               const uint8_t *blobs_next, int32_t *pred_ids, void *ws,
+                               size_t ws_bytes, void *stream)
+{
+    if (T < 1 || T > STRATA_LOOKAHEAD_T_MAX)
+        return STRATA_E_SHAPE;
+    if (!router_next || !blobs_next)
         return STRATA_E_ARG;
-    if (!y && !(flags & STRATA_RESIDUAL))
-        return STRATA_E_ARG;
-    if ((rc = check_ws(ws, ws_bytes, T)))
-        return rc;
-    if (!aligned(x, 16) || !aligned(router, 16) || !aligned(blobs, 256) || !aligned(y, 16) ||
-        !aligned(ids, 4) || !aligned(w, 4) || !aligned(bias, 4))
-        return STRATA_E_ALIGN;
-    hipStream_t st = (hipStream_t)stream;
-    Carve c = carve(ws, T);
-    int32_t *ids_o = ids ? ids : c.ids;
-    float *w_o = w ? w : c.w;
-    const int rms = flags & STRATA_RMSNORM;
-    if (is_decode(T)) {
-        STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, true, ids_o, w_o, 1,
-                                       c.slots, c.erec, c.cdone, c.esync, st));
-    } else {
-        STRATA_TRY(launch_prep(x, T, rms, c.xsplit, c.xperm, st));
-        STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
-        STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
-        STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, st));
-    }
-    const bool res = flags & STRATA_RESIDUAL;
-    if (is_decode(T)) {   // the experts kernel finishes the combine
-        hipEvent_t e0, e1;
-        take_events(e0, e1);
-        STRATA_TRY(launch_decode_experts(blobs, c.erec, c.slots, c.xq, c.hq, c.out, T, c.esync,
-                                         c.cdone, w_o, y, res ? x : nullptr, e0, e1, st));
-        return STRATA_OK;
-    }
-    if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st)))
-        return rc;
-    STRATA_TRY(launch_combine(c.out, w_o, T, y, res ? x : nullptr, 0, st));
-    return STRATA_OK;
+    return strata::layer_impl(x, T, router, bias, blobs, flags, y, ids, w, router_next, bias_next,
+                              blobs_next, pred_ids, ws, ws_bytes, stream);
 }
 
 int strata_moe_time_next_kernel(void *start, void *stop)

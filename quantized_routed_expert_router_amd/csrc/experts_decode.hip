@@ -555,6 +555,38 @@ constexpr size_t EX_LDS_GU = (size_t)DG_ROWS * DG_RS * 4 + (size_t)2 * DG_WAVES 
 constexpr size_t EX_LDS_DN = (size_t)DD_WAVES * DD_ROWS * DD_RS * 4;
 constexpr size_t EX_LDS = EX_LDS_GU > EX_LDS_DN ? EX_LDS_GU : EX_LDS_DN;
 
+// Lookahead: workgroups past the down groups read the blobs of the experts
+// predicted for the next layer, one request per 128-byte line, so that the
+// next layer's experts kernel finds them in the memory-side cache.  Slot s of
+// the prediction gets XT_PER_SLOT workgroups; a slot whose expert an earlier
+// slot already names is skipped.  Nothing waits for them and they write
+// nothing; they only pull lines in.
+constexpr int XT_PER_SLOT = 16;
+constexpr int XT_LINES = BLOB / 128;                                   // 10,800
+constexpr int XT_LINES_PER_WG = (XT_LINES + XT_PER_SLOT - 1) / XT_PER_SLOT;   // 675
+static_assert(BLOB % 128 == 0, "whole lines");
+
+__device__ void touch_next(int b, int nslot, const int32_t *__restrict__ pred,
+                           const uint8_t *__restrict__ blobs_next)
+{
+    const int s = b / XT_PER_SLOT, part = b % XT_PER_SLOT;
+    if (s >= nslot)
+        return;
+    const int e = pred[s];
+    if (e < 0 || e >= E)
+        return;
+    for (int i = 0; i < s; ++i)   // uniform: every lane reads the same ids
+        if (pred[i] == e)
+            return;
+    const uint8_t *base = blobs_next + (size_t)e * BLOB + (size_t)part * XT_LINES_PER_WG * 128;
+    const int n = min(XT_LINES_PER_WG, XT_LINES - part * XT_LINES_PER_WG);
+    for (int i = threadIdx.x; i < n; i += EX_THREADS) {
+        uint32_t v;
+        asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(base + (size_t)i * 128) : "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // The experts of a decode call in one launch.  Workgroup b < 40 amax runs
 // gate/up item b; workgroup 40 amax + g runs down group g (items beyond the
 // call's na active experts exit at once).  A down group waits only for its
@@ -567,7 +599,9 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
                                                           const int4 *__restrict__ erec,
                                                           const int32_t *__restrict__ slots, XQ xq,
                                                           HQ hq, float *__restrict__ out, int T,
-                                                          Combine cb, int32_t *__restrict__ gdone)
+                                                          Combine cb, int32_t *__restrict__ gdone,
+                                                          const int32_t *__restrict__ pred,
+                                                          const uint8_t *__restrict__ blobs_next)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[EX_LDS];
     const int na = active_count(erec, T);
@@ -580,32 +614,38 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
         float(*part)[DG_ROWS] =
             reinterpret_cast<float(*)[DG_ROWS]>(lds + (size_t)DG_ROWS * DG_RS * 4);
         gateup_item(b, blobs, erec, slots, xq, hq, T, wl, part, gdone);
-    } else {
+    } else if (b < amax * (DG_SEGS + EX_DN_PER_E)) {
         const int g = b - amax * DG_SEGS;
         if (g >= na * EX_DN_PER_E)
             return;
         uint32_t *wl = reinterpret_cast<uint32_t *>(lds) +
                        (size_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DD_ROWS * DD_RS;
         down_group(g, blobs, erec, slots, hq, out, T, cb, wl, gdone);
+    } else {
+        touch_next(b - amax * (DG_SEGS + EX_DN_PER_E), T * K, pred, blobs_next);
     }
 }
 
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
                                  XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
-                                 const float *w, float *y, float *res, hipEvent_t ev0,
-                                 hipEvent_t ev1, hipStream_t st)
+                                 const float *w, float *y, float *res, const int32_t *pred,
+                                 const uint8_t *blobs_next, hipEvent_t ev0, hipEvent_t ev1,
+                                 hipStream_t st)
 {
     Combine cb{cdone, w, y, res};
     const int amax = T * K < E ? T * K : E;
     int32_t *gdone = sync + 1;
-    const dim3 grid(amax * (DG_SEGS + EX_DN_PER_E)), block(EX_THREADS);
+    if (!blobs_next)
+        pred = nullptr;
+    const dim3 grid(amax * (DG_SEGS + EX_DN_PER_E) + (pred ? T * K * XT_PER_SLOT : 0));
+    const dim3 block(EX_THREADS);
     if (ev0) {   // timed launch: the events carry the dispatch's own start and end
-        void *args[] = {&blobs, &erec, &slots, &xq, &hq, &out, &T, &cb, &gdone};
+        void *args[] = {&blobs, &erec, &slots, &xq, &hq, &out, &T, &cb, &gdone, &pred, &blobs_next};
         return hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_experts), grid, block, args,
                                   0, st, ev0, ev1, 0);
     }
     hipLaunchKernelGGL(dec_experts, grid, block, 0, st, blobs, erec, slots, xq, hq, out, T, cb,
-                       gdone);
+                       gdone, pred, blobs_next);
     return hipGetLastError();
 }
 

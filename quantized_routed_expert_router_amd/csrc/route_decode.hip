@@ -19,6 +19,9 @@
 //              reductions, a sorting network on each lane's 8 candidates, then
 //              ten rounds of a wave-wide max of p and min of the id among the
 //              maxima -- the order (p desc, id asc) -- and the clamped renorm).
+//              With a lookahead (the next layer's router, second half of
+//              the GEMV grid), waves T .. 2T-1 route the same tokens through
+//              it and write the predicted ids.
 //              For the layer, wave 0 then groups the T*10 slots by expert
 //              with ballots over the bits of the expert ids (stable slot
 //              order and one work record per active expert for the experts
@@ -70,11 +73,15 @@ __device__ inline void build_records(const GroupIn &gi, int T, int tid0, int nth
     }
 }
 
+// With R2 given (lookahead), workgroups E .. 2E-1 compute the raw logits of a
+// second router (the next layer's) on the same x into lraw2.
 template <bool GEMV, bool PREP>
 __global__ __launch_bounds__(RG_THREADS) void rdec_gemv(const float *__restrict__ x, int T,
                                                         const uint16_t *__restrict__ R,
                                                         float *__restrict__ lraw, XQ xq,
-                                                        int rmsnorm, GroupIn gi)
+                                                        int rmsnorm, GroupIn gi,
+                                                        const uint16_t *__restrict__ R2,
+                                                        float *__restrict__ lraw2)
 {
     __shared__ float part[RG_WAVES][DECODE_T_MAX];
     const int tid = threadIdx.x;
@@ -84,9 +91,12 @@ __global__ __launch_bounds__(RG_THREADS) void rdec_gemv(const float *__restrict_
     if (gi.erec)
         build_records(gi, T, g * 64 + lane, nw * 64);
     if (GEMV) {
-        const int e = blockIdx.x;
+        const bool second = blockIdx.x >= E;
+        const int e = second ? blockIdx.x - E : blockIdx.x;
+        const uint16_t *Rm = second ? R2 : R;
+        float *lout = second ? lraw2 : lraw;
         const int k0 = wave * RG_SPAN + 8 * lane;
-        const uint4 q = *reinterpret_cast<const uint4 *>(R + (size_t)e * H + k0);
+        const uint4 q = *reinterpret_cast<const uint4 *>(Rm + (size_t)e * H + k0);
         const float r0 = bf16_bits_to_float(q.x), r1 = bf16_bits_to_float(q.x >> 16);
         const float r2 = bf16_bits_to_float(q.y), r3 = bf16_bits_to_float(q.y >> 16);
         const float r4 = bf16_bits_to_float(q.z), r5 = bf16_bits_to_float(q.z >> 16);
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(RG_THREADS) void rdec_gemv(const float *__restrict_
         }
         __syncthreads();
         if (tid < T)
-            lraw[(size_t)tid * E + e] =
+            lout[(size_t)tid * E + e] =
                 (((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid]) + part[4][tid];
     }
     // inverse RMS of token g (needed by the router and the experts)
@@ -300,55 +310,44 @@ __device__ inline void group_slots(const int *sid, int N, int32_t *slots, int4 *
         erec[0] = make_int4(na, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(RT_THREADS) void rdec_topk(
-    const float *__restrict__ lraw, const float *__restrict__ inv_rms, const float *__restrict__ bias,
-    int T, int32_t *__restrict__ ids, float *__restrict__ wout, int group,
-    int32_t *__restrict__ slots, int4 *__restrict__ erec, int32_t *__restrict__ cdone,
-    int32_t *__restrict__ esync)
+// One token's routing in one wave: softmax over the 512 logits
+// lrow * sc (+ bias), then the ten (p desc, id asc) heads in order.  Lane k
+// < K gets the k-th id and its p; sel (uniform) is the sum of the ten p.
+__device__ inline void route_token(const float *lrow, float sc, const float *bias, int &my_id,
+                                   float &my_p, float &sel)
 {
-    __shared__ int sid[DECODE_T_MAX * K];   // expert of each slot
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int N = T * K;
-    // Waves without a token zero the counters at once; with a full window the
-    // token waves do it after reading the logits (one counter orders a wave's
-    // loads and stores).
-    const bool zero_early = T < DECODE_T_MAX;
-    if (zero_early && wave >= T)
-        zero_counters(cdone, esync, T, tid - 64 * T, RT_THREADS - 64 * T);
-    if (wave < T) {
-        const int t = wave;
-        const float sc = inv_rms[t];
-        float l[8];
+    const int lane = threadIdx.x & 63;
+    float l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        l[i] = lrow[lane + 64 * i];
+    if (bias) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            l[i] = lraw[(size_t)t * E + lane + 64 * i];
-        if (bias) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                l[i] = l[i] * sc + bias[lane + 64 * i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                l[i] = l[i] * sc;
-        }
-        float m = l[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i)
-            m = fmaxf(m, l[i]);
-        m = wave_max63(m);
-        float p[8], s = 0.f;
-        int e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            p[i] = expf(l[i] - m);
-            s += p[i];
-            e[i] = lane + 64 * i;
-        }
-        s = wave_sum63(s);
+            l[i] = l[i] * sc + bias[lane + 64 * i];
+    } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            p[i] = p[i] / s;
-        // sort the lane's 8 candidates, best first (19-comparator network)
+            l[i] = l[i] * sc;
+    }
+    float m = l[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+        m = fmaxf(m, l[i]);
+    m = wave_max63(m);
+    float p[8], s = 0.f;
+    int e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        p[i] = expf(l[i] - m);
+        s += p[i];
+        e[i] = lane + 64 * i;
+    }
+    s = wave_sum63(s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        p[i] = p[i] / s;
+    // sort the lane's 8 candidates, best first (19-comparator network)
 #define STRATA_CX(i, j)                                                                            \
     {                                                                                              \
         const bool sw = ranks_before(p[j], e[j], p[i], e[i]);                                      \
@@ -359,40 +358,68 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
         e[i] = ei_;                                                                                \
         e[j] = ej_;                                                                                \
     }
-        STRATA_CX(0, 2) STRATA_CX(1, 3) STRATA_CX(4, 6) STRATA_CX(5, 7)
-        STRATA_CX(0, 4) STRATA_CX(1, 5) STRATA_CX(2, 6) STRATA_CX(3, 7)
-        STRATA_CX(0, 1) STRATA_CX(2, 3) STRATA_CX(4, 5) STRATA_CX(6, 7)
-        STRATA_CX(2, 4) STRATA_CX(3, 5)
-        STRATA_CX(1, 4) STRATA_CX(3, 6)
-        STRATA_CX(1, 2) STRATA_CX(3, 4) STRATA_CX(5, 6)
+    STRATA_CX(0, 2) STRATA_CX(1, 3) STRATA_CX(4, 6) STRATA_CX(5, 7)
+    STRATA_CX(0, 4) STRATA_CX(1, 5) STRATA_CX(2, 6) STRATA_CX(3, 7)
+    STRATA_CX(0, 1) STRATA_CX(2, 3) STRATA_CX(4, 5) STRATA_CX(6, 7)
+    STRATA_CX(2, 4) STRATA_CX(3, 5)
+    STRATA_CX(1, 4) STRATA_CX(3, 6)
+    STRATA_CX(1, 2) STRATA_CX(3, 4) STRATA_CX(5, 6)
 #undef STRATA_CX
-        int my_id = 0;
-        float my_p = 0.f, sel = 0.f;
+    my_id = 0;
+    my_p = 0.f;
+    sel = 0.f;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            // the best head: the largest p, and among equal p the lowest id
-            // (the one lane holding the maximum, else a reduction over ids)
-            const int hb = __float_as_int(p[0]);
-            const int bb = wave_max_i(hb);
-            const float bp = __int_as_float(bb);
-            const unsigned long long tie = __ballot(hb == bb);
-            const int be = __popcll(tie) == 1
-                               ? __builtin_amdgcn_readlane(e[0], (int)__builtin_ctzll(tie))
-                               : wave_min63(hb == bb ? e[0] : 0x7fffffff);
-            const bool pop = e[0] == be;
+    for (int k = 0; k < K; ++k) {
+        // the best head: the largest p, and among equal p the lowest id
+        // (the one lane holding the maximum, else a reduction over ids)
+        const int hb = __float_as_int(p[0]);
+        const int bb = wave_max_i(hb);
+        const float bp = __int_as_float(bb);
+        const unsigned long long tie = __ballot(hb == bb);
+        const int be = __popcll(tie) == 1
+                           ? __builtin_amdgcn_readlane(e[0], (int)__builtin_ctzll(tie))
+                           : wave_min63(hb == bb ? e[0] : 0x7fffffff);
+        const bool pop = e[0] == be;
 #pragma unroll
-            for (int i = 0; i < 7; ++i) {
-                p[i] = pop ? p[i + 1] : p[i];
-                e[i] = pop ? e[i + 1] : e[i];
-            }
-            p[7] = pop ? -1.f : p[7];
-            e[7] = pop ? 0x7fffffff : e[7];
-            if (lane == k) {
-                my_id = be;
-                my_p = bp;
-            }
-            sel += bp;
+        for (int i = 0; i < 7; ++i) {
+            p[i] = pop ? p[i + 1] : p[i];
+            e[i] = pop ? e[i + 1] : e[i];
         }
+        p[7] = pop ? -1.f : p[7];
+        e[7] = pop ? 0x7fffffff : e[7];
+        if (lane == k) {
+            my_id = be;
+            my_p = bp;
+        }
+        sel += bp;
+    }
+}
+
+// With pred given (lookahead, 2T <= 16), waves T .. 2T-1 also route token
+// wave - T through the second router's raw logits lraw2 (+ bias2) and write
+// its ten ids to pred.
+__global__ __launch_bounds__(RT_THREADS) void rdec_topk(
+    const float *__restrict__ lraw, const float *__restrict__ inv_rms, const float *__restrict__ bias,
+    int T, int32_t *__restrict__ ids, float *__restrict__ wout, int group,
+    int32_t *__restrict__ slots, int4 *__restrict__ erec, int32_t *__restrict__ cdone,
+    int32_t *__restrict__ esync, const float *__restrict__ lraw2, const float *__restrict__ bias2,
+    int32_t *__restrict__ pred)
+{
+    __shared__ int sid[DECODE_T_MAX * K];   // expert of each slot
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int N = T * K;
+    const int busy = pred ? 2 * T : T;   // waves with a token to route
+    // Waves without a token zero the counters at once; with every wave busy
+    // the token waves do it after reading the logits (one counter orders a
+    // wave's loads and stores).
+    const bool zero_early = busy < DECODE_T_MAX;
+    if (zero_early && wave >= busy)
+        zero_counters(cdone, esync, T, tid - 64 * busy, RT_THREADS - 64 * busy);
+    if (wave < T) {
+        const int t = wave;
+        int my_id;
+        float my_p, sel;
+        route_token(lraw + (size_t)t * E, inv_rms[t], bias, my_id, my_p, sel);
         const float den = fmaxf(sel, 6.103515625e-05f);   // clamp 2^-14
         if (lane < K) {
             ids[(size_t)t * K + lane] = my_id;
@@ -400,6 +427,13 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
             if (group)
                 sid[t * K + lane] = my_id;
         }
+    } else if (wave < busy) {
+        const int t = wave - T;
+        int my_id;
+        float my_p, sel;
+        route_token(lraw2 + (size_t)t * E, inv_rms[t], bias2, my_id, my_p, sel);
+        if (lane < K)
+            pred[(size_t)t * K + lane] = my_id;
     }
     if (!zero_early)
         zero_counters(cdone, esync, T, tid, RT_THREADS);
@@ -419,17 +453,20 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
                                int rmsnorm, float *lraw, XQ xq, bool prep, int32_t *ids,
                                float *w, int group, int32_t *slots, int4 *erec, int32_t *cdone,
-                               int32_t *esync, hipStream_t st)
+                               int32_t *esync, const uint16_t *R2, const float *bias2,
+                               float *lraw2, int32_t *pred, hipStream_t st)
 {
     const GroupIn none{nullptr, nullptr, nullptr, nullptr, nullptr};
+    const dim3 grid(R2 ? 2 * E : E);
     if (prep)
-        hipLaunchKernelGGL((rdec_gemv<true, true>), dim3(E), dim3(RG_THREADS), 0, st, x, T, R,
-                           lraw, xq, rmsnorm, none);
+        hipLaunchKernelGGL((rdec_gemv<true, true>), grid, dim3(RG_THREADS), 0, st, x, T, R, lraw,
+                           xq, rmsnorm, none, R2, lraw2);
     else
-        hipLaunchKernelGGL((rdec_gemv<true, false>), dim3(E), dim3(RG_THREADS), 0, st, x, T, R,
-                           lraw, xq, rmsnorm, none);
+        hipLaunchKernelGGL((rdec_gemv<true, false>), grid, dim3(RG_THREADS), 0, st, x, T, R, lraw,
+                           xq, rmsnorm, none, R2, lraw2);
     hipLaunchKernelGGL(rdec_topk, dim3(1), dim3(RT_THREADS), 0, st, lraw, xq.inv_rms, bias, T, ids,
-                       w, group, slots, erec, cdone, esync);
+                       w, group, slots, erec, cdone, esync, R2 ? lraw2 : nullptr, bias2,
+                       R2 ? pred : nullptr);
     return hipGetLastError();
 }
 
@@ -440,7 +477,8 @@ hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const i
     const int blocks = (T * XBLK + RG_WAVES - 1) / RG_WAVES;
     const GroupIn gi{offsets, slots, active, erec, esync};
     hipLaunchKernelGGL((rdec_gemv<false, true>), dim3(blocks), dim3(RG_THREADS), 0, st, x, T,
-                       (const uint16_t *)nullptr, (float *)nullptr, xq, rmsnorm, gi);
+                       (const uint16_t *)nullptr, (float *)nullptr, xq, rmsnorm, gi,
+                       (const uint16_t *)nullptr, (float *)nullptr);
     return hipGetLastError();
 }
 

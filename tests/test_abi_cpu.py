@@ -31,7 +31,7 @@ def m():
 
 def test_exports_every_declared_symbol(m):
     names = declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     assert set(names) == set(m.EXPORTS)
     for n in names:
         assert hasattr(m.lib(), n), n
@@ -70,6 +70,20 @@ def test_host_validation_rejects_before_launch(m):
     # y may be NULL only with STRATA_RESIDUAL
     assert L.strata_moe_layer(fake, 4, fake, None, fake, 0, None, None, None, fake, ws_need, None) == m.E_ARG
     assert L.strata_moe_layer(fake, 4, fake, None, fake, 3, None, None, None, fake, 0, None) == m.E_WORKSPACE
+    # lookahead: decode sizes only, and both next-layer pointers required
+    LA = L.strata_moe_layer_lookahead
+    assert LA(fake, 9, fake, None, fake, 2, None, None, None, fake, None, fake, None, fake,
+              m.strata_moe_workspace_bytes(9), None) == m.E_SHAPE
+    assert LA(fake, 0, fake, None, fake, 2, None, None, None, fake, None, fake, None, fake,
+              ws_need, None) == m.E_SHAPE
+    assert LA(fake, 4, fake, None, fake, 2, None, None, None, None, None, fake, None, fake,
+              ws_need, None) == m.E_ARG
+    assert LA(fake, 4, fake, None, fake, 2, None, None, None, fake, None, None, None, fake,
+              ws_need, None) == m.E_ARG
+    assert LA(fake, 4, fake, None, fake, 2, None, None, None, fake, None, fake + 16, None, fake,
+              ws_need, None) == m.E_ALIGN
+    assert LA(fake, 4, fake, None, fake, 2, None, None, None, fake, None, fake, None, fake,
+              ws_need - 1, None) == m.E_WORKSPACE
     # the timing hook takes both events or neither (arming touches no device)
     assert L.strata_moe_time_next_kernel(fake, None) == m.E_ARG
     assert L.strata_moe_time_next_kernel(None, fake) == m.E_ARG
