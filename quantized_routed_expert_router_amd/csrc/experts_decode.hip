@@ -7,27 +7,32 @@
 // expert's blob is read once per call however many tokens of the window chose
 // it (the window dedup of section "The plan: three destinations per expert").
 //
-// Both kernels put one weight row on each lane.  A workgroup reads its rows
-// with coalesced 16-byte loads into LDS, then every lane walks its own row
-// block by block: the 16 code bytes give two nibble-masked dwords per 16
-// codes, and v_dot8 multiplies them with the token's 16-bit activation digits
-// (quant.hpp).  The activation operand is the same for the 16 lanes of a row,
-// so it reaches them by a DPP row broadcast inside the v_dot8: per lane, two
-// registers carry a whole 64-value block.
+// One launch, dec_experts, runs three kinds of workgroup.  Each puts one
+// weight row on each lane: the workgroup reads its rows with coalesced 16-byte
+// loads into LDS, then every lane walks its own row block by block.  The 16
+// code bytes give two nibble-masked dwords per 16 codes, and v_dot8
+// multiplies them with the token's 16-bit activation digits (quant.hpp).  The
+// activation operand is the same for the 16 lanes of a row, so it reaches them
+// by a DPP row broadcast inside the v_dot8: per lane, two registers carry a
+// whole 64-value block.
 //
-//  dec_gateup  item = (active expert, 16 FF rows): the 16 gate and 16 up rows
+//  gate/up item  (active expert, 16 FF rows): the 16 gate and 16 up rows
 //              (23 KB).  256 threads = 4 waves; lane (r = lane / 16, l) takes
 //              row l of gate (r even) or up (r odd) and block columns
 //              5 s .. 5 s + 4 with s = 2 w + r / 2.  Partial sums meet in a
 //              fixed order; wave 0 forms h = silu(g) * u for the 16 rows and
-//              quantises them as one 16-value segment.  One item per
-//              workgroup; 4-wave workgroups of 23 KB LDS run six to a CU.
-//  dec_down    item = (active expert, 32 output rows), one wave: lane (r, l)
-//              takes row 16 (r % 2) + l and block columns 2 j + r / 2; the two
-//              halves of each row are added and the row's value written per
-//              slot.  Four items per workgroup.  In a layer call it also
-//              finishes the combine (the last slot of a token's rows to be
-//              done sums the token's K slots).
+//              quantises them as one 16-value segment.  A shared expert's
+//              tokens go two at a time (codes split once).  Workgroups of
+//              23 KB LDS run six to a CU.
+//  down group  four items (active expert, 32 output rows), one per wave:
+//              lane (r, l) takes row 16 (r % 2) + l and block columns
+//              2 j + r / 2; the two halves of each row are added and the
+//              row's value written per slot.  A down group waits for its
+//              expert's gate/up items (a counter per active expert).  In a
+//              layer call it also finishes the combine (the last slot of a
+//              token's rows to be done sums the token's K slots).
+//  lookahead   only for strata_moe_layer_lookahead: reads the next layer's
+//              predicted experts, line by line, and writes nothing.
 // Every sum has a fixed order, so results are bitwise reproducible and do not
 // depend on the other tokens of the call.
 #include "common.hpp"
