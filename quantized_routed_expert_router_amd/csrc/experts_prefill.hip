@@ -78,7 +78,8 @@ __device__ inline int pf_pos_of_col(int c)
 //    MFMA fragment reads of 16 rows hit distinct banks without padding.
 //  - Weights: gate/up in stages of 2 blocks (36 bytes of each of the 256
 //    rows, two stage buffers, requested one stage ahead); down rows are
-//    contiguous in memory and all 10 blocks (46,080 bytes) arrive at once.
+//    contiguous in memory and all 10 blocks (46,080 bytes) arrive at once,
+//    16 bytes a lane.
 // Every LDS read of a block and its wait are one asm statement, and the
 // vector-memory waits are explicit counts that follow from the fixed issue
 // order (derived at each wait below); one barrier per block.
@@ -89,10 +90,11 @@ constexpr int PF_GSROW = 2 * BB;                        // 36 bytes per gate/up 
 constexpr int PF_GSTAGE = PF_ROWS * PF_GSROW;           // 9,216 bytes per gate/up stage
 constexpr int PF_GNB = PF_GSTAGE / 4 / 64 / 4;          // 9 dword loads per wave per stage
 constexpr int PF_DB = PF_ROWS * ROW_D;                  // 46,080 bytes of down rows
-constexpr int PF_DNB = PF_DB / 4 / 64 / 4;              // 45 dword loads per wave
+constexpr int PF_DCH = PF_DB / 16 / 4;                 // 720 16-byte chunks per wave
+constexpr int PF_DNB = (PF_DCH + 63) / 64;              // 12 dwordx4 loads per wave
 constexpr int PF_LDS_G = PF_NABUF * PF_ABYTES + 2 * PF_GSTAGE;   // 51,200
 constexpr int PF_LDS_D = PF_NABUF * PF_ABYTES + PF_DB;           // 78,848
-static_assert(PF_GNB * 64 * 4 * 4 == PF_GSTAGE && PF_DNB * 64 * 4 * 4 == PF_DB, "load split");
+static_assert(PF_GNB * 64 * 4 * 4 == PF_GSTAGE && PF_DCH * 16 * 4 == PF_DB, "load split");
 static_assert(PF_THREADS == 256, "four waves");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -300,10 +302,13 @@ __device__ inline void pf_down_loop(const uint8_t *wsrc, const PfAct &act, uint8
     uint8_t *const wbuf = lds + PF_NABUF * PF_ABYTES;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
+    // the 46,080 contiguous bytes of the tile, 16 bytes a lane (the last
+    // request of a wave has 16 lanes)
 #pragma unroll
     for (int h = 0; h < PF_DNB; ++h)
-        __builtin_amdgcn_global_load_lds(wsrc + 4 * (PF_DNB * 64 * w + 64 * h + lane),
-                                         wbuf + (PF_DNB * 64 * w + 64 * h) * 4, 4, 0, 0);
+        if (64 * h + lane < PF_DCH)
+            __builtin_amdgcn_global_load_lds(wsrc + 16 * (PF_DCH * w + 64 * h + lane),
+                                             wbuf + (PF_DCH * w + 64 * h) * 16, 16, 0, 0);
     uint32_t a0, a1;
     pf_act_read_addrs(lds_addr(lds), a0, a1);
     act.request(lds, 0);
