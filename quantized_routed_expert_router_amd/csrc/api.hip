@@ -11,7 +11,7 @@ hipError_t launch_logits(const uint16_t *xsplit, int T, const uint16_t *R, const
                          float *logits, hipStream_t st);
 hipError_t launch_topk(const float *logits, int T, int32_t *ids, float *w, hipStream_t st);
 hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
-                        int32_t *active, hipStream_t st);
+                        int32_t *active, int32_t *gcount, hipStream_t st);
 hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_items,
                        int32_t *mlist, int32_t *nitems, hipStream_t st);
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
@@ -74,7 +74,7 @@ struct Carve {
     int4 *erec;
     int32_t *cdone, *esync;
     float *lraw2;
-    int32_t *pred;
+    int32_t *pred, *gcount;
 };
 
 Carve carve(void *ws, int T)
@@ -97,6 +97,7 @@ Carve carve(void *ws, int T)
     c.esync = at<int32_t>(ws, L.esync);
     c.lraw2 = at<float>(ws, L.lraw2);
     c.pred = at<int32_t>(ws, L.pred);
+    c.gcount = at<int32_t>(ws, L.gcount);
     c.ids = at<int32_t>(ws, L.ids);
     c.w = at<float>(ws, L.w);
     c.mlist = at<int32_t>(ws, L.mlist);
@@ -179,7 +180,7 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
         STRATA_TRY(launch_prep(x, T, rms, c.xsplit, c.xperm, st));
         STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
         STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
-        STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, st));
+        STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, c.gcount, st));
     }
     const bool res = flags & STRATA_RESIDUAL;
     if (is_decode(T)) {   // the experts kernel finishes the combine
@@ -252,7 +253,8 @@ int strata_moe_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots
         return rc;
     if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(slots, 4) || !aligned(active, 4))
         return STRATA_E_ALIGN;
-    STRATA_TRY(launch_group(ids, T, offsets, slots, active, (hipStream_t)stream));
+    STRATA_TRY(launch_group(ids, T, offsets, slots, active, carve(ws, T).gcount,
+                            (hipStream_t)stream));
     return STRATA_OK;
 }
 

@@ -65,6 +65,7 @@ struct Ws {
     size_t out;        // f32 [T*K][H]
     size_t cdone;      // i32 [Td][H/32]      decode layer: finished slots per (token, 32 rows)
     size_t esync;      // i32 [1+32E]        decode experts: finished gate/up items per active expert (128-B apart)
+    size_t gcount;     // i32 [ceil(Tp*K/256)][E] prefill grouping: per-block expert counts / starts
     size_t lraw2;      // f32 [Td][E]        lookahead: the next layer's raw logits
     size_t pred;       // i32 [Td*K]         lookahead: the next layer's predicted ids
     size_t total;
@@ -112,6 +113,7 @@ inline Ws ws_layout(int T)
     L.out = take((size_t)T * K * H * 4);
     L.cdone = take(Td * (H / 32) * 4);
     L.esync = take(Td ? (size_t)(1 + 32 * E) * 4 : 0);
+    L.gcount = take((Tp * K + 255) / 256 * E * 4);
     L.lraw2 = take(Td * E * 4);
     L.pred = take(Td * K * 4);
     L.total = o;

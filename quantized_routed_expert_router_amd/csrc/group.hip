@@ -6,7 +6,7 @@
 // X = [x1..x4]); for a verify window it is the dedup of routed ids ("Strata in
 // the source...", section "The plan: three destinations per expert").
 //
-// group_kernel is one 1024-thread workgroup: per-wave histograms in LDS
+// group_kernel (decode-sized T) is one 1024-thread workgroup: per-wave histograms in LDS
 // (integer atomics, so the counts are exact), an exclusive scan to offsets, the
 // ascending active-expert list, then a stable scatter in which each wave walks
 // its contiguous slice of slots in order and ranks equal experts inside a
@@ -150,6 +150,99 @@ __global__ __launch_bounds__(GR_THREADS) void group_kernel(const int32_t *__rest
     }
 }
 
+// The same grouping over many workgroups, for prefill-sized T (bitwise the
+// same outputs): 256-slot blocks count their experts in LDS
+// (group_count_kernel); one workgroup turns the per-block counts into each
+// block's start inside every expert, the offsets and the active list
+// (group_scan_kernel); the blocks then place their slots stably -- rank among
+// equal experts inside a wave by ballots over the id bits, plus the earlier
+// waves' counts, plus the block's start and the expert's offset
+// (group_scatter_kernel).
+constexpr int GB_SLOTS = 256;   // slots per block
+
+__global__ __launch_bounds__(GB_SLOTS) void group_count_kernel(const int32_t *__restrict__ ids,
+                                                               int N, int32_t *__restrict__ gcount)
+{
+    __shared__ int hist[E];
+    const int tid = threadIdx.x, b = blockIdx.x;
+    for (int i = tid; i < E; i += GB_SLOTS)
+        hist[i] = 0;
+    __syncthreads();
+    const int s = b * GB_SLOTS + tid;
+    const int e = s < N ? ids[s] : -1;
+    if (e >= 0 && e < E)
+        atomicAdd(&hist[e], 1);
+    __syncthreads();
+    for (int i = tid; i < E; i += GB_SLOTS)
+        gcount[(size_t)b * E + i] = hist[i];
+}
+
+__global__ __launch_bounds__(E) void group_scan_kernel(int nb, int32_t *__restrict__ gcount,
+                                                       int32_t *__restrict__ offsets,
+                                                       int32_t *__restrict__ active)
+{
+    __shared__ int tmp[8];
+    __shared__ int tot;
+    const int e = threadIdx.x;
+    int run = 0;   // expert e's slots in the blocks before b: block b's start
+    for (int b0 = 0; b0 < nb; b0 += 16) {   // 16 counts in flight, then their starts
+        int c[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            c[j] = b0 + j < nb ? gcount[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (b0 + j < nb)
+                gcount[(size_t)(b0 + j) * E + e] = run;
+            run += c[j];
+        }
+    }
+    const int off = block_exclusive_scan_512(run, e, tmp, &tot);
+    offsets[e] = off;
+    if (e == 0)
+        offsets[E] = tot;
+    const int flag = run > 0 ? 1 : 0;
+    const int pos = block_exclusive_scan_512(flag, e, tmp, &tot);
+    if (flag)
+        active[1 + pos] = e;
+    if (e == 0)
+        active[0] = tot;
+}
+
+__global__ __launch_bounds__(GB_SLOTS) void group_scatter_kernel(const int32_t *__restrict__ ids,
+                                                                 int N,
+                                                                 const int32_t *__restrict__ gstart,
+                                                                 const int32_t *__restrict__ offsets,
+                                                                 int32_t *__restrict__ slots)
+{
+    __shared__ int wc[GB_SLOTS / 64][E];   // per-wave counts of each expert
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, b = blockIdx.x;
+    for (int i = tid; i < (GB_SLOTS / 64) * E; i += GB_SLOTS)
+        (&wc[0][0])[i] = 0;
+    const int s = b * GB_SLOTS + tid;
+    const int v = s < N ? ids[s] : -1;
+    const int e = (v >= 0 && v < E) ? v : -1;
+    unsigned long long same = __ballot(e >= 0);
+    if (e < 0)
+        same = 0;
+#pragma unroll
+    for (int bit = 0; bit < 9; ++bit) {
+        const unsigned long long bits = __ballot(e >= 0 && ((e >> bit) & 1));
+        same &= ((e >> bit) & 1) ? bits : ~bits;
+    }
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
+    __syncthreads();   // the counts are zero
+    if (e >= 0 && rank == 0)   // the first lane of each group records the group's size
+        wc[wave][e] = __popcll(same);
+    __syncthreads();
+    if (e >= 0) {
+        int before = rank;
+        for (int w = 0; w < wave; ++w)
+            before += wc[w][e];
+        slots[offsets[e] + gstart[(size_t)b * E + e] + before] = s;
+    }
+}
+
 // Prefill work list: one item per (active expert, 64-token chunk), in active
 // order; nitems[0] = item count.
 __global__ __launch_bounds__(512) void plan_kernel(const int32_t *__restrict__ offsets,
@@ -182,10 +275,18 @@ __global__ __launch_bounds__(512) void plan_kernel(const int32_t *__restrict__ o
 }
 
 hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
-                        int32_t *active, hipStream_t st)
+                        int32_t *active, int32_t *gcount, hipStream_t st)
 {
-    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(GR_THREADS), 0, st, ids, T, offsets, slots,
-                       active);
+    if (is_decode(T) || !gcount) {
+        hipLaunchKernelGGL(group_kernel, dim3(1), dim3(GR_THREADS), 0, st, ids, T, offsets, slots,
+                           active);
+        return hipGetLastError();
+    }
+    const int N = T * K, nb = (N + GB_SLOTS - 1) / GB_SLOTS;
+    hipLaunchKernelGGL(group_count_kernel, dim3(nb), dim3(GB_SLOTS), 0, st, ids, N, gcount);
+    hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(E), 0, st, nb, gcount, offsets, active);
+    hipLaunchKernelGGL(group_scatter_kernel, dim3(nb), dim3(GB_SLOTS), 0, st, ids, N,
+                       (const int32_t *)gcount, (const int32_t *)offsets, slots);
     return hipGetLastError();
 }
 

@@ -178,9 +178,12 @@ def test_group_matches_cpu_counting_sort():
     import torch
     m = hz.qm()
     rng = np.random.default_rng(9)
-    for T in (1, 4, 37, 2048, 8192):
+    for T in (1, 4, 37, 300, 2048, 8192):
         _say(f"case: group T={T}")
         ids = rng.integers(0, 512, (T, 10)).astype(np.int32)
+        if T == 300:   # skewed: most slots on a few experts, across many blocks
+            hot = rng.random((T, 10)) < 0.7
+            ids[hot] = rng.choice([7, 8, 511], size=int(hot.sum()))
         if T == 37:
             ids[3, 4] = 600     # out-of-range ids are dropped
             ids[5, 0] = -1
