@@ -3,6 +3,7 @@
 // Nothing here synchronises, allocates or reads device memory.
 #include "common.hpp"
 #include "quant.hpp"
+#include "workspace.hpp"
 
 namespace strata {
 hipError_t launch_prep(const float *x, int T, int rmsnorm, uint16_t *xsplit, __half *xperm,
