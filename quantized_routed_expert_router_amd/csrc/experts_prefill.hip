@@ -129,33 +129,37 @@ struct PfVals {
 };
 
 // Issues the reads without waiting for them: the values are not to be used
-// before pf_reads_done on the same PfVals (which is what orders them).
-template <int AOFF, int BOFF, int NS1, int NS2, int NS3>
+// before pf_reads_done on the same PfVals (which is what orders them).  Only
+// the MS activation subtiles that hold item rows are read.
+template <int AOFF, int BOFF, int NS1, int NS2, int NS3, int MS>
 __device__ inline void pf_reads_issue(uint32_t a0, uint32_t a1, uint32_t bs, uint32_t bc, PfVals &v)
 {
-    asm volatile("ds_read_b128 %0, %16 offset:%20\n\t"
-                 "ds_read_b128 %1, %17 offset:%20\n\t"
-                 "ds_read_b128 %2, %16 offset:%21\n\t"
-                 "ds_read_b128 %3, %17 offset:%21\n\t"
-                 "ds_read_b128 %4, %16 offset:%22\n\t"
-                 "ds_read_b128 %5, %17 offset:%22\n\t"
-                 "ds_read_b128 %6, %16 offset:%23\n\t"
-                 "ds_read_b128 %7, %17 offset:%23\n\t"
-                 "ds_read_u16 %8, %18 offset:%24\n\t"
-                 "ds_read_b32 %12, %19 offset:%24\n\t"
-                 "ds_read_u16 %9, %18 offset:%25\n\t"
-                 "ds_read_b32 %13, %19 offset:%25\n\t"
-                 "ds_read_u16 %10, %18 offset:%26\n\t"
-                 "ds_read_b32 %14, %19 offset:%26\n\t"
-                 "ds_read_u16 %11, %18 offset:%27\n\t"
-                 "ds_read_b32 %15, %19 offset:%27"
-                 : "=&v"(v.af[0][0]), "=&v"(v.af[0][1]), "=&v"(v.af[1][0]), "=&v"(v.af[1][1]),
-                   "=&v"(v.af[2][0]), "=&v"(v.af[2][1]), "=&v"(v.af[3][0]), "=&v"(v.af[3][1]),
-                   "=&v"(v.dbits[0]), "=&v"(v.dbits[1]), "=&v"(v.dbits[2]), "=&v"(v.dbits[3]),
+#define STRATA_PF_AREAD(MI)                                                                        \
+    asm volatile("ds_read_b128 %0, %2 offset:%4\n\t"                                             \
+                 "ds_read_b128 %1, %3 offset:%4"                                                   \
+                 : "=&v"(v.af[MI][0]), "=&v"(v.af[MI][1])                                          \
+                 : "v"(a0), "v"(a1), "i"(AOFF + 2048 * (MI))                                       \
+                 : "memory")
+    STRATA_PF_AREAD(0);
+    if constexpr (MS > 1)
+        STRATA_PF_AREAD(1);
+    if constexpr (MS > 2)
+        STRATA_PF_AREAD(2);
+    if constexpr (MS > 3)
+        STRATA_PF_AREAD(3);
+#undef STRATA_PF_AREAD
+    asm volatile("ds_read_u16 %0, %8 offset:%10\n\t"
+                 "ds_read_b32 %4, %9 offset:%10\n\t"
+                 "ds_read_u16 %1, %8 offset:%11\n\t"
+                 "ds_read_b32 %5, %9 offset:%11\n\t"
+                 "ds_read_u16 %2, %8 offset:%12\n\t"
+                 "ds_read_b32 %6, %9 offset:%12\n\t"
+                 "ds_read_u16 %3, %8 offset:%13\n\t"
+                 "ds_read_b32 %7, %9 offset:%13"
+                 : "=&v"(v.dbits[0]), "=&v"(v.dbits[1]), "=&v"(v.dbits[2]), "=&v"(v.dbits[3]),
                    "=&v"(v.wc[0]), "=&v"(v.wc[1]), "=&v"(v.wc[2]), "=&v"(v.wc[3])
-                 : "v"(a0), "v"(a1), "v"(bs), "v"(bc), "i"(AOFF), "i"(AOFF + 2048),
-                   "i"(AOFF + 4096), "i"(AOFF + 6144), "i"(BOFF), "i"(BOFF + NS1),
-                   "i"(BOFF + NS2), "i"(BOFF + NS3)
+                 : "v"(bs), "v"(bc), "i"(BOFF), "i"(BOFF + NS1), "i"(BOFF + NS2),
+                   "i"(BOFF + NS3)
                  : "memory");
 }
 
@@ -262,7 +266,7 @@ __device__ inline void pf_gateup_loop(const uint8_t *blob, const uint32_t goff[P
     vm_wait<15>();   // A0 and W0: younger A1, A2, W1, A3
     __builtin_amdgcn_s_barrier();
     PfVals cur, nxt;
-    pf_reads_issue<0, 0, NS1, NS2, NS3>(a0, a1, bs, bc, cur);
+    pf_reads_issue<0, 0, NS1, NS2, NS3, MS>(a0, a1, bs, bc, cur);
     pf_reads_done(cur);
 #define STRATA_PF_STEP(R)                                                                          \
     {                                                                                              \
@@ -276,7 +280,7 @@ __device__ inline void pf_gateup_loop(const uint8_t *blob, const uint32_t goff[P
         act.request(lds + ((R) & 3) * PF_ABYTES, b + 4 < NB_G ? b + 4 : NB_G - 1);                 \
         pf_reads_issue<(((R) + 1) & 3) * PF_ABYTES, ((((R) + 1) >> 1) & 1) * PF_GSTAGE +           \
                                                         BB * (((R) + 1) & 1),                      \
-                       NS1, NS2, NS3>(a0, a1, bs, bc, nxt);                                        \
+                       NS1, NS2, NS3, MS>(a0, a1, bs, bc, nxt);                                        \
         pf_math<MS>(cur, acc);                                                                     \
         pf_reads_done(nxt);                                                                        \
         cur = nxt;                                                                                 \
@@ -319,7 +323,7 @@ __device__ inline void pf_down_loop(const uint8_t *wsrc, const PfAct &act, uint8
     vm_wait<6>();   // the weights and A0: younger A1, A2, A3
     __builtin_amdgcn_s_barrier();
     PfVals cur, nxt;
-    pf_reads_issue<0, 0, NS1, NS2, NS3>(a0, a1, bs, bc, cur);
+    pf_reads_issue<0, 0, NS1, NS2, NS3, MS>(a0, a1, bs, bc, cur);
     pf_reads_done(cur);
 #define STRATA_PF_DSTEP(B)                                                                         \
     {                                                                                              \
@@ -327,7 +331,7 @@ __device__ inline void pf_down_loop(const uint8_t *wsrc, const PfAct &act, uint8
         __builtin_amdgcn_s_barrier();                                                              \
         act.request(lds + ((B) & 3) * PF_ABYTES, (B) + 4 < NB_D ? (B) + 4 : NB_D - 1);             \
         pf_reads_issue<(((B) + 1) & 3) * PF_ABYTES, BB * ((B) + 1 < NB_D ? (B) + 1 : NB_D - 1),    \
-                       NS1, NS2, NS3>(a0, a1, bs, bc, nxt);                                        \
+                       NS1, NS2, NS3, MS>(a0, a1, bs, bc, nxt);                                        \
         pf_math<MS>(cur, acc);                                                                     \
         pf_reads_done(nxt);                                                                        \
         cur = nxt;                                                                                 \
