@@ -18,11 +18,13 @@
 // packed subtract of M_p + 1 and one packed multiply by d finish two weights.
 // So a lane's 16 weights cost 25 VALU ops, once per 64-token M-chunk.
 //
-// K order inside a 64-block: MFMA step j (0, 1) and lane group q (= lane/16)
-// cover positions pi = 32 j + 8 q + s (s = 0..7), which carry input column
-// 16 q + 4 j + s/2 + 8 (s % 2).  Activations are stored in that order once
-// (prep kernel for x, the gate/up epilogue for h), so every A fragment is one
-// 16-byte LDS read.
+// K order: activations are stored once in the order the MFMA fragments take
+// them, so every A fragment is one 16-byte LDS read.  For down (h, written by
+// the gate/up epilogue), inside a 64-block: MFMA step j (0, 1) and lane group
+// q (= lane/16) cover positions pi = 32 j + 8 q + s (s = 0..7), which carry
+// input column 16 q + 4 j + s/2 + 8 (s % 2).  For gate/up (x, written by the
+// prep kernel) the order runs over groups of four blocks (see the gate/up
+// loop below).
 //
 // Work items: (active expert, 64-token chunk) x N-tile.  gate/up tiles hold
 // 128 FF rows of gate and the same 128 rows of up, so SiLU(g) * u happens in
@@ -43,23 +45,33 @@ constexpr int XA_STRIDE = 72;                  // halfs per staged row (144 B, c
 __device__ inline uint32_t as_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ inline half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
-// Eight fp16 pairs (exact (c - 1) * d) from one code dword; pair p holds codes
-// p (low half) and p + 8 (high half).
-__device__ inline void dequant_dword(uint32_t w, uint32_t dbits, uint32_t out[8])
+// Four fp16 pairs (exact (c - 1) * d) from one code dword w and the scale
+// pair d2 = (d, d): pair t of half HF is pair p = 4 HF + t of the dword, which
+// holds codes p (low half) and p + 8 (high half).
+template <int HF>
+__device__ inline void dequant_half(uint32_t w, uint32_t d2bits, uint32_t out[4])
 {
-    const half2v d2 = as_h2(dbits | (dbits << 16));
+    const half2v d2 = as_h2(d2bits);
     const uint32_t w10 = w >> 10;
-    const uint32_t src[8] = {w, w, w, w, w, w10, w10, w10};
-    const int pos[8] = {0, 1, 2, 3, 4, 0, 1, 2};
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int q = pos[p];
+    for (int t = 0; t < 4; ++t) {
+        const int p = 4 * HF + t;
+        const uint32_t src = p < 5 ? w : w10;
+        const int q = p < 5 ? p : p - 5;
         const uint32_t mag = (uint32_t)(25 - 2 * q) << 10;
-        const uint32_t u = (src[p] & (0x00030003u << (2 * q))) | (mag | (mag << 16));
+        const uint32_t u = (src & (0x00030003u << (2 * q))) | (mag | (mag << 16));
         const _Float16 m1 = (_Float16)(float)((1 << (10 - 2 * q)) + 1);
         const half2v cm1 = as_h2(u) - (half2v){m1, m1};
-        out[p] = as_u32(cm1 * d2);
+        out[t] = as_u32(cm1 * d2);
     }
+}
+
+// All eight pairs of a code dword; dbits is the scale's fp16 bit pattern.
+__device__ inline void dequant_dword(uint32_t w, uint32_t dbits, uint32_t out[8])
+{
+    const uint32_t d2 = dbits | (dbits << 16);
+    dequant_half<0>(w, d2, out);
+    dequant_half<1>(w, d2, out + 4);
 }
 
 // K-order position of input column c (0..63) inside its block.
@@ -70,32 +82,53 @@ __device__ inline int pf_pos_of_col(int c)
     return 32 * (p >> 2) + 8 * q + 2 * (p & 3) + hb;
 }
 
-// Software pipeline of one (item, N-tile), fed by direct global->LDS loads
-// (global_load_lds: the data never passes through registers).
-//  - Activations: one block (64 rows x 64 halfs, 8 KB) per K-step in a ring of
-//    four LDS buffers, requested three blocks ahead.  Rows are packed at 128
-//    bytes; the 16-byte chunk c of row m sits at position c ^ (m & 7), so the
-//    MFMA fragment reads of 16 rows hit distinct banks without padding.
-//  - Weights: gate/up in stages of 2 blocks (36 bytes of each of the 256
-//    rows, two stage buffers, requested one stage ahead); down rows are
-//    contiguous in memory and all 10 blocks (46,080 bytes) arrive at once,
-//    16 bytes a lane.
+// Down: software pipeline of one (item, N-tile), fed by direct global->LDS
+// loads (global_load_lds: the data never passes through registers).
+//  - Activations (h): one block (64 rows x 64 halfs, 8 KB) per K-step in a
+//    ring of four LDS buffers, requested three blocks ahead.  Rows are packed
+//    at 128 bytes; the 16-byte chunk c of row m sits at position c ^ (m & 7),
+//    so the MFMA fragment reads of 16 rows hit distinct banks without padding.
+//  - Weights: the tile's down rows are contiguous in memory and all 10 blocks
+//    (46,080 bytes) arrive at once, 16 bytes a lane.
 // Every LDS read of a block and its wait are one asm statement, and the
 // vector-memory waits are explicit counts that follow from the fixed issue
 // order (derived at each wait below); one barrier per block.
 constexpr int PF_ROWS = 256;                            // weight rows per WG
 constexpr int PF_ABYTES = PF_M * QK * 2;                // 8,192 bytes per activation block
 constexpr int PF_NABUF = 4;                             // activation ring
-constexpr int PF_GSROW = 2 * BB;                        // 36 bytes per gate/up row per stage
-constexpr int PF_GSTAGE = PF_ROWS * PF_GSROW;           // 9,216 bytes per gate/up stage
-constexpr int PF_GNB = PF_GSTAGE / 4 / 64 / 4;          // 9 dword loads per wave per stage
 constexpr int PF_DB = PF_ROWS * ROW_D;                  // 46,080 bytes of down rows
 constexpr int PF_DCH = PF_DB / 16 / 4;                 // 720 16-byte chunks per wave
 constexpr int PF_DNB = (PF_DCH + 63) / 64;              // 12 dwordx4 loads per wave
-constexpr int PF_LDS_G = PF_NABUF * PF_ABYTES + 2 * PF_GSTAGE;   // 51,200
 constexpr int PF_LDS_D = PF_NABUF * PF_ABYTES + PF_DB;           // 78,848
-static_assert(PF_GNB * 64 * 4 * 4 == PF_GSTAGE && PF_DCH * 16 * 4 == PF_DB, "load split");
+static_assert(PF_DCH * 16 * 4 == PF_DB, "load split");
 static_assert(PF_THREADS == 256, "four waves");
+
+// Gate/up: K is walked in groups of four blocks (256 input columns).  In
+// group g the lanes of quarter q (= lane / 16) own block 4 g + q of their
+// weight row whole, loaded straight into registers -- the weights of a wave
+// serve no other wave, so they skip the LDS: 16 + 4 bytes from the dword at
+// or below the block's start (an 18-byte block starts 0 or 2 bytes into that
+// dword, the same for every lane of a quarter), then byte permutes pick out
+// the scale pair and the four code dwords.  MFMA step j (0..7) of a group
+// uses code dword j / 2, codes 4 (j % 2) + s / 2 + 8 (s % 2) along its
+// fragment (s = 0..7), i.e. input column
+// 64 (4 g + q) + 16 (j / 2) + 4 (j % 2) + s / 2 + 8 (s % 2); the prep kernel
+// stores the activations in that order, as 16-byte chunk 8 q + j of each
+// 512-byte group.
+// Activations: one group (64 rows x 512 bytes) per LDS buffer, two buffers,
+// filled by direct global->LDS loads one group ahead, and read by all four
+// waves.  A 1 KB request fills 8 rows (row group r = row / 8) x 8 chunks of
+// one octet; inside the row group chunk c sits at position c ^ (r & 1), so
+// the two row groups of a 16-row fragment read fall on different banks.
+// One barrier per group.
+constexpr int PG_BLK = 4;                               // blocks per K group
+constexpr int PG_NG = NB_G / PG_BLK;                    // 10 groups
+constexpr int PG_GBYTES = PG_BLK * QK * 2;              // 512 bytes of a row per group
+constexpr int PG_ABYTES = PF_M * PG_GBYTES;             // 32,768 bytes per activation group
+constexpr int PF_LDS_G = 2 * PG_ABYTES;                 // 65,536
+static_assert(PG_NG * PG_BLK == NB_G, "whole groups");
+static_assert(BB + 2 <= 20 && PG_BLK * BB * (PG_NG - 1) + 3 * BB - 2 + 20 == ROW_G,
+              "20 loaded bytes hold a block; those of a row's last block end at the row's end");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -226,74 +259,172 @@ __device__ inline void pf_act_read_addrs(uint32_t abase, uint32_t &a0, uint32_t 
     a1 = abase + (lane & 15) * 128 + 16 * ((q + 4) ^ (lane & 7));
 }
 
-// Gate/up K loop: 40 blocks, weight stage t = blocks 2 t, 2 t + 1 (buffer
-// t & 1), activation block j in ring buffer j & 3.  Iteration b waits for the
-// data of block b + 1, passes the barrier (after which every wave has read
-// block b - 1 out of LDS), requests what goes into the freed buffers, issues
-// the LDS reads of block b + 1 and, while they run, computes block b from the
-// values read in iteration b - 1.  Requests of iteration i: the weight stage
-// (i + 3) / 2 if i is odd, then activation block i + 4 (past the end: the last
-// block or stage again, never read).  The prologue issues those of iterations
-// -4 .. -1 (A0; W0, A1; A2; W1, A3) and reads block 0.  Wait counts at the
-// top of iteration b, in lane-loads younger than the oldest one needed:
-//  b even: A(b+1) is the oldest; younger A(b+2), W((b+2)/2), A(b+3): 13.
-//  b odd:  W((b+1)/2) (issued in iteration b-2) is; younger A(b+2), A(b+3): 4.
-template <int MS>
-__device__ inline void pf_gateup_loop(const uint8_t *blob, const uint32_t goff[PF_GNB],
-                                      const PfAct &act, uint8_t *lds, uint32_t bs, uint32_t bc,
-                                      floatx4 acc[4][4])
-{
-    uint8_t *const wbuf = lds + PF_NABUF * PF_ABYTES;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // stage src into stage buffer par
-    auto wreq = [&](int src, int par) {
+// Activation requests of gate/up group g for this wave: 8 requests of 1 KB,
+// request i filling row group 2 w + i / 4, chunk octet i % 4.
+struct PgAct {
+    const uint8_t *row[2];   // rows 16 w + 8 h + lane % 8 (valid memory for every lane)
+    uint32_t coff[2];        // byte offset of this lane's chunk in the octet, h = 0, 1
+    __device__ void request(uint8_t *abuf, int g) const
+    {
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-        for (int h = 0; h < PF_GNB; ++h)
-            __builtin_amdgcn_global_load_lds(blob + goff[h] + PF_GSROW * src,
-                                             wbuf + par * PF_GSTAGE + (PF_GNB * 64 * w + 64 * h) * 4,
-                                             4, 0, 0);
-    };
-    constexpr int NST = NB_G / 2;
-    constexpr int NS1 = 16 * PF_GSROW, NS2 = 128 * PF_GSROW, NS3 = 144 * PF_GSROW;
-    uint32_t a0, a1;
-    pf_act_read_addrs(lds_addr(lds), a0, a1);
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds(row[i >> 2] + PG_GBYTES * g + 128 * (i & 3) + coff[i >> 2],
+                                             abuf + (8 * w + i) * 1024, 16, 0, 0);
+    }
+};
+
+// One group's weight bytes for the wave's four 16-row subtiles.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+struct PgW {
+    u32x4 lo[4];
+    uint32_t hi[4];
+};
+
+// Waits for all of this wave's loads; the compiler then sees r as ready (its
+// own wait for them would otherwise also wait for the loads issued since).
+__device__ inline void pg_wait_all(PgW &r)
+{
+    u32x4 a = r.lo[0], b = r.lo[1], c = r.lo[2], d = r.lo[3];
+    uint32_t e = r.hi[0], f = r.hi[1], g = r.hi[2], h = r.hi[3];
+    asm volatile("s_waitcnt vmcnt(0)"
+                 : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
+                 :
+                 : "memory");
+    r.lo[0] = a, r.lo[1] = b, r.lo[2] = c, r.lo[3] = d;
+    r.hi[0] = e, r.hi[1] = f, r.hi[2] = g, r.hi[3] = h;
+}
+
+__device__ inline void pg_wload(const uint8_t *blob, const uint32_t woff[4], int g, PgW &r)
+{
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+        const uint8_t *p = blob + woff[ns] + PG_BLK * BB * g;
+        r.lo[ns] = *reinterpret_cast<const u32x4 *>(p);
+        r.hi[ns] = *reinterpret_cast<const uint32_t *>(p + 16);
+    }
+}
+
+// LDS reads of the MS activation fragments of one MFMA step (without waiting);
+// 16-row group mi is two row groups, 8 KB, further on.
+template <int OFF, int MS>
+__device__ inline void pg_aread(uint32_t a, half8 af[4])
+{
+#define STRATA_PG_AREAD(MI)                                                                        \
+    asm volatile("ds_read_b128 %0, %1 offset:%2"                                                   \
+                 : "=&v"(af[MI])                                                                   \
+                 : "v"(a), "i"(OFF + 8192 * (MI))                                                  \
+                 : "memory")
+    STRATA_PG_AREAD(0);
+    if constexpr (MS > 1)
+        STRATA_PG_AREAD(1);
+    if constexpr (MS > 2)
+        STRATA_PG_AREAD(2);
+    if constexpr (MS > 3)
+        STRATA_PG_AREAD(3);
+#undef STRATA_PG_AREAD
+}
+
+// Waits for pg_aread: from here on the compiler sees the values.
+template <int MS>
+__device__ inline void pg_await(half8 af[4])
+{
+    if constexpr (MS == 1)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(af[0]) : : "memory");
+    else if constexpr (MS == 2)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(af[0]), "+v"(af[1]) : : "memory");
+    else if constexpr (MS == 3)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]) : : "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3])
+                     :
+                     : "memory");
+}
+
+// MFMA step J of a group: issue the reads of step J + 1, dequantise this
+// step's four weight fragments, issue its 4 x MS MFMAs, wait for the reads.
+template <int BUF, int MS, int J>
+__device__ inline void pg_step(uint32_t ae, uint32_t ao, const uint32_t d2[4], const uint32_t cw[4][4],
+                               half8 af[2][4], floatx4 acc[4][4])
+{
+    if constexpr (J < 7)
+        pg_aread<BUF * PG_ABYTES + 128 * (J + 1), MS>(((J + 1) & 1) ? ao : ae, af[(J + 1) & 1]);
+    uint32_t pr[4][4];
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns)
+        dequant_half<J & 1>(cw[ns][J >> 1], d2[ns], pr[ns]);
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+        const half8 bf = __builtin_bit_cast(half8, make_uint4(pr[ns][0], pr[ns][1], pr[ns][2], pr[ns][3]));
+#pragma unroll
+        for (int mi = 0; mi < MS; ++mi)   // only the 16-row groups holding item rows
+            acc[ns][mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[J & 1][mi], bf, acc[ns][mi], 0, 0, 0);
+    }
+    if constexpr (J < 7)
+        pg_await<MS>(af[(J + 1) & 1]);
+}
+
+// acc[ns][mi] += the products of one group: the scale pairs and code dwords
+// are picked out of the loaded bytes, then each of the 8 MFMA steps reads its
+// activation fragments (the next step's reads run during this step's math),
+// dequantises its four weight fragments and issues 4 x MS MFMAs.
+// ae / ao: this lane's fragment read address for even / odd steps.
+template <int BUF, int MS>
+__device__ inline void pg_group(uint32_t ae, uint32_t ao, const PgW &wr, uint32_t sel_c,
+                                uint32_t sel_d, floatx4 acc[4][4])
+{
+    uint32_t d2[4], cw[4][4];
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+        const uint32_t L[5] = {wr.lo[ns].x, wr.lo[ns].y, wr.lo[ns].z, wr.lo[ns].w, wr.hi[ns]};
+        d2[ns] = __builtin_amdgcn_perm(L[0], L[0], sel_d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            cw[ns][i] = __builtin_amdgcn_perm(L[i + 1], L[i], sel_c);
+    }
+    half8 af[2][4];
+    pg_aread<BUF * PG_ABYTES, MS>(ae, af[0]);
+    pg_await<MS>(af[0]);
+    pg_step<BUF, MS, 0>(ae, ao, d2, cw, af, acc);
+    pg_step<BUF, MS, 1>(ae, ao, d2, cw, af, acc);
+    pg_step<BUF, MS, 2>(ae, ao, d2, cw, af, acc);
+    pg_step<BUF, MS, 3>(ae, ao, d2, cw, af, acc);
+    pg_step<BUF, MS, 4>(ae, ao, d2, cw, af, acc);
+    pg_step<BUF, MS, 5>(ae, ao, d2, cw, af, acc);
+    pg_step<BUF, MS, 6>(ae, ao, d2, cw, af, acc);
+    pg_step<BUF, MS, 7>(ae, ao, d2, cw, af, acc);
+}
+
+// Gate/up K loop over the 10 groups: group g computes from LDS buffer g % 2
+// and register set g % 2.  At the top of each group the wave waits for all
+// its requests (the group's activations and weights, issued one group
+// earlier) and passes the barrier (every wave's share has landed; every wave
+// is done reading the other buffer), then requests group g + 1 into the
+// other buffer and register set and computes group g.
+template <int MS>
+__device__ inline void pg_gateup_loop(const uint8_t *blob, const uint32_t woff[4], const PgAct &act,
+                                      uint8_t *lds, uint32_t ae, uint32_t ao, uint32_t sel_c,
+                                      uint32_t sel_d, floatx4 acc[4][4])
+{
+    PgW w0, w1;
     act.request(lds, 0);
-    wreq(0, 0);
-    act.request(lds + PF_ABYTES, 1);
-    act.request(lds + 2 * PF_ABYTES, 2);
-    wreq(1, 1);
-    act.request(lds + 3 * PF_ABYTES, 3);
-    vm_wait<15>();   // A0 and W0: younger A1, A2, W1, A3
-    __builtin_amdgcn_s_barrier();
-    PfVals cur, nxt;
-    pf_reads_issue<0, 0, NS1, NS2, NS3, MS>(a0, a1, bs, bc, cur);
-    pf_reads_done(cur);
-#define STRATA_PF_STEP(R)                                                                          \
-    {                                                                                              \
-        const int b = b0 + (R);                                                                    \
-        vm_wait<((R) & 1) ? 4 : 13>();                                                             \
-        __builtin_amdgcn_s_barrier();                                                              \
-        if ((R) & 1) {                                                                             \
-            const int t = (b + 3) / 2;                                                             \
-            wreq(t < NST ? t : NST - 1, t & 1);                                                    \
-        }                                                                                          \
-        act.request(lds + ((R) & 3) * PF_ABYTES, b + 4 < NB_G ? b + 4 : NB_G - 1);                 \
-        pf_reads_issue<(((R) + 1) & 3) * PF_ABYTES, ((((R) + 1) >> 1) & 1) * PF_GSTAGE +           \
-                                                        BB * (((R) + 1) & 1),                      \
-                       NS1, NS2, NS3, MS>(a0, a1, bs, bc, nxt);                                        \
-        pf_math<MS>(cur, acc);                                                                     \
-        pf_reads_done(nxt);                                                                        \
-        cur = nxt;                                                                                 \
-    }
+    pg_wload(blob, woff, 0, w0);
 #pragma unroll 1
-    for (int b0 = 0; b0 < NB_G; b0 += 4) {
-        STRATA_PF_STEP(0)
-        STRATA_PF_STEP(1)
-        STRATA_PF_STEP(2)
-        STRATA_PF_STEP(3)
+    for (int g = 0; g < PG_NG; g += 2) {
+        pg_wait_all(w0);
+        __builtin_amdgcn_s_barrier();
+        act.request(lds + PG_ABYTES, g + 1);
+        pg_wload(blob, woff, g + 1, w1);
+        pg_group<0, MS>(ae, ao, w0, sel_c, sel_d, acc);
+        pg_wait_all(w1);
+        __builtin_amdgcn_s_barrier();
+        if (g + 2 < PG_NG) {
+            act.request(lds, g + 2);
+            pg_wload(blob, woff, g + 2, w0);
+        }
+        pg_group<1, MS>(ae, ao, w1, sel_c, sel_d, acc);
     }
-#undef STRATA_PF_STEP
-    vm_wait<0>();   // the trailing requests land before the LDS is released
 }
 
 // Down K loop: 10 blocks; all weights requested first, then A0 .. A3.
@@ -396,27 +527,32 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
     const int jw = nt * PF_NT_G + 32 * wave;   // this wave's first FF row
     const uint8_t *blob = blobs + (size_t)it.e * BLOB;
     // Activation rows this lane requests (rows past the item's end read its
-    // first row; their results are never stored).
-    PfAct act;
+    // first row; their results are never stored): rows 16 w + 8 h + lane % 8,
+    // chunk (lane / 8) ^ h of each octet.
+    PgAct act;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int r = 16 * wave + 8 * h + (lane >> 3);
+        const int r = 16 * wave + 8 * h + (lane & 7);
         const int sl = slots[it.gp0 + (r < it.rows ? r : 0)];
         const int t = (sl >= 0 && sl < T * K) ? sl / K : 0;
-        act.row[h] = xperm + (size_t)t * H;
+        act.row[h] = reinterpret_cast<const uint8_t *>(xperm + (size_t)t * H);
+        act.coff[h] = 16 * ((lane >> 3) ^ h);
     }
-    act.chunk = (lane & 7) ^ (lane >> 3);
-    // Weight requests: lane-load h of a stage is stage dword p = 576 w + 64 h
-    // + lane = row p / 9, dword p % 9 (rows 0..127 gate, 128..255 up).
-    uint32_t goff[PF_GNB];
+    // Weight bytes: subtile ns is gate (ns < 2) or up rows jw + 16 (ns % 2) +
+    // lane % 16; quarter q loads from the dword at or below block q's start.
+    const int q = lane >> 4, odd = q & 1;
+    uint32_t woff[4];
 #pragma unroll
-    for (int h = 0; h < PF_GNB; ++h) {
-        const int p = PF_GNB * 64 * wave + 64 * h + lane;
-        const int n = p / 9, k = p % 9;
-        goff[h] = (uint32_t)((n >= 128 ? MAT : 0) + (size_t)(nt * PF_NT_G + (n & 127)) * ROW_G + 4 * k);
-    }
-    const uint32_t bs = lds_addr(lds + PF_NABUF * PF_ABYTES) + (32 * wave + (lane & 15)) * PF_GSROW;
-    const uint32_t bc = bs + 2 + 4 * (lane >> 4);
+    for (int ns = 0; ns < 4; ++ns)
+        woff[ns] = (uint32_t)((ns >= 2 ? MAT : 0) + (size_t)(jw + 16 * (ns & 1) + (lane & 15)) * ROW_G +
+                              BB * q - 2 * odd);
+    const uint32_t sel_c = odd ? 0x07060504u : 0x05040302u;   // code dword i: bytes 2..5 or 4..7 of L[i], L[i+1]
+    const uint32_t sel_d = odd ? 0x03020302u : 0x01000100u;   // (d, d) from bytes 0, 1 or 2, 3 of L[0]
+    // Fragment reads: row 16 mi + lane % 16 (row group 2 mi + b), chunk 8 q + j at
+    // position 8 q + (j ^ b) of the row group.
+    const int b = (lane >> 3) & 1;
+    const uint32_t abase = lds_addr(lds) + (32 * b + 8 * q) * 128 + 16 * (lane & 7);
+    const uint32_t ae = abase + 128 * b, ao = abase - 128 * b;
     floatx4 acc[4][4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns)
@@ -426,16 +562,16 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
     // one straight-line loop per number of 16-row groups holding item rows
     switch ((it.rows + 15) >> 4) {
     case 1:
-        pf_gateup_loop<1>(blob, goff, act, lds, bs, bc, acc);
+        pg_gateup_loop<1>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
         break;
     case 2:
-        pf_gateup_loop<2>(blob, goff, act, lds, bs, bc, acc);
+        pg_gateup_loop<2>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
         break;
     case 3:
-        pf_gateup_loop<3>(blob, goff, act, lds, bs, bc, acc);
+        pg_gateup_loop<3>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
         break;
     default:
-        pf_gateup_loop<4>(blob, goff, act, lds, bs, bc, acc);
+        pg_gateup_loop<4>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
         break;
     }
     // Epilogue: h = silu(g) * u for FF rows jw + 16 h2 + lane%16.

@@ -19,12 +19,15 @@
 
 namespace strata {
 
-// Position pi (0..63) of a block in the prefill K order holds input column
-// 16 q + 4 j + s/2 + 8 (s % 2) with pi = 32 j + 8 q + s (see experts_prefill).
-__device__ inline int pf_col_of_pos(int pi)
+// Position pos (0..H-1) of a row in the gate/up activation order holds input
+// column 64 (4 g + q) + 16 (j / 2) + 4 (j % 2) + s / 2 + 8 (s % 2) with
+// pos = 256 g + 64 q + 8 j + s: 16-byte chunk 8 q + j of 256-column group g
+// is the fragment of MFMA step j for the lanes that own block 4 g + q (see
+// experts_prefill).
+__device__ inline int pg_col_of_pos(int pos)
 {
-    const int j = pi >> 5, q = (pi >> 3) & 3, s = pi & 7;
-    return 16 * q + 4 * j + (s >> 1) + 8 * (s & 1);
+    const int g = pos >> 8, q = (pos >> 6) & 3, j = (pos >> 3) & 7, s = pos & 7;
+    return 64 * (4 * g + q) + 16 * (j >> 1) + 4 * (j & 1) + (s >> 1) + 8 * (s & 1);
 }
 
 constexpr int PREP_THREADS = 256;
@@ -79,10 +82,8 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     }
     __syncthreads();
     if (xperm) {
-        for (int pos = tid; pos < H; pos += PREP_THREADS) {
-            const int b = pos >> 6;
-            xperm[(size_t)t * H + pos] = __float2half_rn(xs[b * QK + pf_col_of_pos(pos & 63)]);
-        }
+        for (int pos = tid; pos < H; pos += PREP_THREADS)
+            xperm[(size_t)t * H + pos] = __float2half_rn(xs[pg_col_of_pos(pos)]);
     }
 }
 
