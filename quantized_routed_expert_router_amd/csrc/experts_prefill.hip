@@ -59,7 +59,12 @@ __device__ inline void dequant_half(uint32_t w, uint32_t d2bits, uint32_t out[4]
         const uint32_t src = p < 5 ? w : w10;
         const int q = p < 5 ? p : p - 5;
         const uint32_t mag = (uint32_t)(25 - 2 * q) << 10;
-        const uint32_t u = (src & (0x00030003u << (2 * q))) | (mag | (mag << 16));
+        // (src & mask) | exponent pattern in one v_and_or_b32 (the compiler
+        // would spend an AND and an OR with literal operands)
+        uint32_t u;
+        asm("v_and_or_b32 %0, %1, %2, %3"
+            : "=v"(u)
+            : "v"(src), "s"(0x00030003u << (2 * q)), "v"(mag | (mag << 16)));
         const _Float16 m1 = (_Float16)(float)((1 << (10 - 2 * q)) + 1);
         const half2v cm1 = as_h2(u) - (half2v){m1, m1};
         out[t] = as_u32(cm1 * d2);
@@ -481,6 +486,15 @@ __device__ inline void pf_down_loop(const uint8_t *wsrc, const PfAct &act, uint8
     vm_wait<0>();
 }
 
+// silu(g) * u = g u / (1 + e^-g) with the hardware exp2 and reciprocal (each
+// within about 1 ulp in fp32, far inside the fp16 rounding h gets next; for
+// g << 0, e^-g overflows to inf and the reciprocal gives 0).
+__device__ inline float pf_silu_mul(float g, float u)
+{
+    const float e = __builtin_amdgcn_exp2f(-1.44269504088896341f * g);
+    return g * u * __builtin_amdgcn_rcpf(1.f + e);
+}
+
 struct PfItem {
     int ok, e, gp0, rows;
 };
@@ -587,7 +601,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
                 if (m < it.rows) {
                     const float g = acc[h2][mi][r];
                     const float u = acc[2 + h2][mi][r];
-                    const float h = g / (1.f + expf(-g)) * u;
+                    const float h = pf_silu_mul(g, u);
                     hperm[(size_t)(it.gp0 + m) * FF + col] = __float2half_rn(h);
                 }
             }
