@@ -40,7 +40,6 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int PF_THREADS = 256;
-constexpr int XA_STRIDE = 72;                  // halfs per staged row (144 B, conflict-free)
 
 __device__ inline uint32_t as_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ inline half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
@@ -70,43 +69,6 @@ __device__ inline void dequant_half(uint32_t w, uint32_t d2bits, uint32_t out[4]
         out[t] = as_u32(cm1 * d2);
     }
 }
-
-// All eight pairs of a code dword; dbits is the scale's fp16 bit pattern.
-__device__ inline void dequant_dword(uint32_t w, uint32_t dbits, uint32_t out[8])
-{
-    const uint32_t d2 = dbits | (dbits << 16);
-    dequant_half<0>(w, d2, out);
-    dequant_half<1>(w, d2, out + 4);
-}
-
-// K-order position of input column c (0..63) inside its block.
-__device__ inline int pf_pos_of_col(int c)
-{
-    const int q = c >> 4, r16 = c & 15;
-    const int p = r16 & 7, hb = r16 >> 3;
-    return 32 * (p >> 2) + 8 * q + 2 * (p & 3) + hb;
-}
-
-// Down: software pipeline of one (item, N-tile), fed by direct global->LDS
-// loads (global_load_lds: the data never passes through registers).
-//  - Activations (h): one block (64 rows x 64 halfs, 8 KB) per K-step in a
-//    ring of four LDS buffers, requested three blocks ahead.  Rows are packed
-//    at 128 bytes; the 16-byte chunk c of row m sits at position c ^ (m & 7),
-//    so the MFMA fragment reads of 16 rows hit distinct banks without padding.
-//  - Weights: the tile's down rows are contiguous in memory and all 10 blocks
-//    (46,080 bytes) arrive at once, 16 bytes a lane.
-// Every LDS read of a block and its wait are one asm statement, and the
-// vector-memory waits are explicit counts that follow from the fixed issue
-// order (derived at each wait below); one barrier per block.
-constexpr int PF_ROWS = 256;                            // weight rows per WG
-constexpr int PF_ABYTES = PF_M * QK * 2;                // 8,192 bytes per activation block
-constexpr int PF_NABUF = 4;                             // activation ring
-constexpr int PF_DB = PF_ROWS * ROW_D;                  // 46,080 bytes of down rows
-constexpr int PF_DCH = PF_DB / 16 / 4;                 // 720 16-byte chunks per wave
-constexpr int PF_DNB = (PF_DCH + 63) / 64;              // 12 dwordx4 loads per wave
-constexpr int PF_LDS_D = PF_NABUF * PF_ABYTES + PF_DB;           // 78,848
-static_assert(PF_DCH * 16 * 4 == PF_DB, "load split");
-static_assert(PF_THREADS == 256, "four waves");
 
 // Gate/up: K is walked in groups of four blocks (256 input columns).  In
 // group g the lanes of quarter q (= lane / 16) own block 4 g + q of their
@@ -142,126 +104,9 @@ __device__ inline uint32_t lds_addr(uint8_t *p)
     return (uint32_t)(uintptr_t)(lds_u8 *)p;
 }
 
-// Activation requests of block b for this wave: two 16-byte chunks per lane
-// (rows 16 w + 8 h + lane / 8, position lane % 8).
-struct PfAct {
-    const __half *row[2];   // this lane's two rows (valid memory for every lane)
-    int chunk;              // global 16-byte chunk for this lane's position
-    __device__ void request(uint8_t *abuf, int b) const
-    {
-        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            __builtin_amdgcn_global_load_lds(row[h] + QK * b + 8 * chunk,
-                                             abuf + (128 * w + 64 * h) * 16, 16, 0, 0);
-    }
-};
-
-// The LDS reads of one block: the 4 activation subtiles x 2 K-halves and, for
-// each of the 4 weight subtiles, its scale and this lane's code dword.
-// AOFF: activation buffer offset; BOFF: this block's offset in the weight
-// rows; NS1..NS3: offsets of weight subtiles 1..3 from subtile 0.
-struct PfVals {
-    half8 af[4][2];
-    uint32_t dbits[4], wc[4];
-};
-
-// Issues the reads without waiting for them: the values are not to be used
-// before pf_reads_done on the same PfVals (which is what orders them).  Only
-// the MS activation subtiles that hold item rows are read.
-template <int AOFF, int BOFF, int NS1, int NS2, int NS3, int MS>
-__device__ inline void pf_reads_issue(uint32_t a0, uint32_t a1, uint32_t bs, uint32_t bc, PfVals &v)
-{
-#define STRATA_PF_AREAD(MI)                                                                        \
-    asm volatile("ds_read_b128 %0, %2 offset:%4\n\t"                                             \
-                 "ds_read_b128 %1, %3 offset:%4"                                                   \
-                 : "=&v"(v.af[MI][0]), "=&v"(v.af[MI][1])                                          \
-                 : "v"(a0), "v"(a1), "i"(AOFF + 2048 * (MI))                                       \
-                 : "memory")
-    STRATA_PF_AREAD(0);
-    if constexpr (MS > 1)
-        STRATA_PF_AREAD(1);
-    if constexpr (MS > 2)
-        STRATA_PF_AREAD(2);
-    if constexpr (MS > 3)
-        STRATA_PF_AREAD(3);
-#undef STRATA_PF_AREAD
-    asm volatile("ds_read_u16 %0, %8 offset:%10\n\t"
-                 "ds_read_b32 %4, %9 offset:%10\n\t"
-                 "ds_read_u16 %1, %8 offset:%11\n\t"
-                 "ds_read_b32 %5, %9 offset:%11\n\t"
-                 "ds_read_u16 %2, %8 offset:%12\n\t"
-                 "ds_read_b32 %6, %9 offset:%12\n\t"
-                 "ds_read_u16 %3, %8 offset:%13\n\t"
-                 "ds_read_b32 %7, %9 offset:%13"
-                 : "=&v"(v.dbits[0]), "=&v"(v.dbits[1]), "=&v"(v.dbits[2]), "=&v"(v.dbits[3]),
-                   "=&v"(v.wc[0]), "=&v"(v.wc[1]), "=&v"(v.wc[2]), "=&v"(v.wc[3])
-                 : "v"(bs), "v"(bc), "i"(BOFF), "i"(BOFF + NS1), "i"(BOFF + NS2),
-                   "i"(BOFF + NS3)
-                 : "memory");
-}
-
-// Waits for the reads of v: from here on the compiler sees their values.
-__device__ inline void pf_reads_done(PfVals &v)
-{
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(v.af[0][0]), "+v"(v.af[0][1]), "+v"(v.af[1][0]), "+v"(v.af[1][1]),
-                   "+v"(v.af[2][0]), "+v"(v.af[2][1]), "+v"(v.af[3][0]), "+v"(v.af[3][1]),
-                   "+v"(v.dbits[0]), "+v"(v.dbits[1]), "+v"(v.dbits[2]), "+v"(v.dbits[3]),
-                   "+v"(v.wc[0]), "+v"(v.wc[1]), "+v"(v.wc[2]), "+v"(v.wc[3])
-                 :
-                 : "memory");
-}
-
-// acc[ns][mi] += A(64 x 64) W(64 x 64) from the values read for one block:
-// the four weight subtiles are dequantised first, then the 32 MFMAs run in
-// an order where one accumulator recurs only every 16 instructions.
-template <int MS>
-__device__ inline void pf_math(const PfVals &v, floatx4 acc[4][4])
-{
-    const auto &af = v.af;
-    const auto &dbits = v.dbits;
-    const auto &wc = v.wc;
-    half8 bf[4][2];
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-        uint32_t pr[8];
-        dequant_dword(wc[ns], dbits[ns], pr);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            bf[ns][j] = __builtin_bit_cast(
-                half8, make_uint4(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]));
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
-#pragma unroll
-            for (int mi = 0; mi < MS; ++mi)   // only the 16-row groups holding item rows
-                acc[ns][mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mi][j], bf[ns][j], acc[ns][mi],
-                                                                      0, 0, 0);
-#ifdef PF_INTERLEAVE
-    // scheduler hint: one MFMA, then up to three VALU, repeated
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-#endif
-}
-
 template <int N> __device__ inline void vm_wait()
 {
     asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
-}
-
-// Per-lane LDS read addresses of the activation fragments (K-halves j = 0, 1)
-// of row 16 mi + lane % 16, position (lane / 16 + 4 j) ^ (lane % 8).
-__device__ inline void pf_act_read_addrs(uint32_t abase, uint32_t &a0, uint32_t &a1)
-{
-    const int lane = threadIdx.x & 63, q = lane >> 4;
-    a0 = abase + (lane & 15) * 128 + 16 * (q ^ (lane & 7));
-    a1 = abase + (lane & 15) * 128 + 16 * ((q + 4) ^ (lane & 7));
 }
 
 // Activation requests of gate/up group g for this wave: 8 requests of 1 KB,
@@ -311,14 +156,14 @@ __device__ inline void pg_wload(const uint8_t *blob, const uint32_t woff[4], int
 }
 
 // LDS reads of the MS activation fragments of one MFMA step (without waiting);
-// 16-row group mi is two row groups, 8 KB, further on.
-template <int OFF, int MS>
+// 16-row group mi is two row groups, MSTR bytes, further on.
+template <int OFF, int MSTR, int MS>
 __device__ inline void pg_aread(uint32_t a, half8 af[4])
 {
 #define STRATA_PG_AREAD(MI)                                                                        \
     asm volatile("ds_read_b128 %0, %1 offset:%2"                                                   \
                  : "=&v"(af[MI])                                                                   \
-                 : "v"(a), "i"(OFF + 8192 * (MI))                                                  \
+                 : "v"(a), "i"(OFF + MSTR * (MI))                                                  \
                  : "memory")
     STRATA_PG_AREAD(0);
     if constexpr (MS > 1)
@@ -347,14 +192,16 @@ __device__ inline void pg_await(half8 af[4])
                      : "memory");
 }
 
-// MFMA step J of a group: issue the reads of step J + 1, dequantise this
-// step's four weight fragments, issue its 4 x MS MFMAs, wait for the reads.
-template <int BUF, int MS, int J>
+// MFMA step J of a group of NSTEP steps whose fragments start at LDS offset
+// AOFF (16-row groups MSTR bytes apart): issue the reads of step J + 1,
+// dequantise this step's four weight fragments, issue its 4 x MS MFMAs, wait
+// for the reads.
+template <int AOFF, int MSTR, int NSTEP, int MS, int J>
 __device__ inline void pg_step(uint32_t ae, uint32_t ao, const uint32_t d2[4], const uint32_t cw[4][4],
                                half8 af[2][4], floatx4 acc[4][4])
 {
-    if constexpr (J < 7)
-        pg_aread<BUF * PG_ABYTES + 128 * (J + 1), MS>(((J + 1) & 1) ? ao : ae, af[(J + 1) & 1]);
+    if constexpr (J + 1 < NSTEP)
+        pg_aread<AOFF + 128 * (J + 1), MSTR, MS>(((J + 1) & 1) ? ao : ae, af[(J + 1) & 1]);
     uint32_t pr[4][4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns)
@@ -366,8 +213,23 @@ __device__ inline void pg_step(uint32_t ae, uint32_t ao, const uint32_t d2[4], c
         for (int mi = 0; mi < MS; ++mi)   // only the 16-row groups holding item rows
             acc[ns][mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[J & 1][mi], bf, acc[ns][mi], 0, 0, 0);
     }
-    if constexpr (J < 7)
+    if constexpr (J + 1 < NSTEP)
         pg_await<MS>(af[(J + 1) & 1]);
+}
+
+// The scale pairs and code dwords of one group, picked out of its loaded
+// bytes (sel_d, sel_c: the byte selections for this lane's block offset).
+__device__ inline void pg_extract(const PgW &wr, uint32_t sel_c, uint32_t sel_d, uint32_t d2[4],
+                                  uint32_t cw[4][4])
+{
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+        const uint32_t L[5] = {wr.lo[ns].x, wr.lo[ns].y, wr.lo[ns].z, wr.lo[ns].w, wr.hi[ns]};
+        d2[ns] = __builtin_amdgcn_perm(L[0], L[0], sel_d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            cw[ns][i] = __builtin_amdgcn_perm(L[i + 1], L[i], sel_c);
+    }
 }
 
 // acc[ns][mi] += the products of one group: the scale pairs and code dwords
@@ -380,25 +242,19 @@ __device__ inline void pg_group(uint32_t ae, uint32_t ao, const PgW &wr, uint32_
                                 uint32_t sel_d, floatx4 acc[4][4])
 {
     uint32_t d2[4], cw[4][4];
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-        const uint32_t L[5] = {wr.lo[ns].x, wr.lo[ns].y, wr.lo[ns].z, wr.lo[ns].w, wr.hi[ns]};
-        d2[ns] = __builtin_amdgcn_perm(L[0], L[0], sel_d);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            cw[ns][i] = __builtin_amdgcn_perm(L[i + 1], L[i], sel_c);
-    }
+    pg_extract(wr, sel_c, sel_d, d2, cw);
+    constexpr int A0 = BUF * PG_ABYTES;
     half8 af[2][4];
-    pg_aread<BUF * PG_ABYTES, MS>(ae, af[0]);
+    pg_aread<A0, 8192, MS>(ae, af[0]);
     pg_await<MS>(af[0]);
-    pg_step<BUF, MS, 0>(ae, ao, d2, cw, af, acc);
-    pg_step<BUF, MS, 1>(ae, ao, d2, cw, af, acc);
-    pg_step<BUF, MS, 2>(ae, ao, d2, cw, af, acc);
-    pg_step<BUF, MS, 3>(ae, ao, d2, cw, af, acc);
-    pg_step<BUF, MS, 4>(ae, ao, d2, cw, af, acc);
-    pg_step<BUF, MS, 5>(ae, ao, d2, cw, af, acc);
-    pg_step<BUF, MS, 6>(ae, ao, d2, cw, af, acc);
-    pg_step<BUF, MS, 7>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 0>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 1>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 2>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 3>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 4>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 5>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 6>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 7>(ae, ao, d2, cw, af, acc);
 }
 
 // Gate/up K loop over the 10 groups: group g computes from LDS buffer g % 2
@@ -432,58 +288,59 @@ __device__ inline void pg_gateup_loop(const uint8_t *blob, const uint32_t woff[4
     }
 }
 
-// Down K loop: 10 blocks; all weights requested first, then A0 .. A3.
-// Iteration b: wait for A(b+1) (younger: A(b+2), A(b+3): 4), barrier, request
-// A(b+4) into block b's buffer, issue the reads of block b+1, compute block b.
-template <int MS>
-__device__ inline void pf_down_loop(const uint8_t *wsrc, const PfAct &act, uint8_t *lds,
-                                    uint32_t bs, uint32_t bc, floatx4 acc[4][4])
+// Down: K = 640.  Groups 0 and 1 are as in gate/up (lane quarter q owns
+// block 4 g + q); the last group holds blocks 8 and 9, quarter q owning half
+// q % 2 of block 8 + q / 2 for 4 MFMA steps (its 20 loaded bytes hold the
+// whole block; the half's two code dwords are picked by q % 2).  The item's
+// whole activation tile (64 rows x 1,280 bytes of h) sits in LDS at once:
+// groups 0 and 1 in the gate/up layout at 0 and 32 KB, the last group at
+// 64 KB (16 chunks per row, row groups of 2 KB, chunk c at position
+// c ^ (r & 1)).  Every request goes out at the start: one wait, one barrier.
+constexpr int PD_G2 = 2 * PG_ABYTES;                    // offset of the last group
+constexpr int PF_LDS_D = PD_G2 + PF_M * 256;            // 81,920
+static_assert(2 * PG_BLK + 2 == NB_D, "two whole groups and two blocks");
+static_assert(PD_G2 + 4096 * 3 + 2048 + 128 * 15 + 16 * 8 == PF_LDS_D, "last fragment read ends at the end");
+
+// Position of h column c (0..FF-1) in the down activation order: blocks 0..7
+// as in the gate/up order (chunk 8 q + j of 256-column group b / 4, q = b % 4);
+// blocks 8 and 9 in a last group of 128 positions, chunk 4 q + j for half
+// q % 2 of block 8 + q / 2.  Element s of the chunk of MFMA step j holds
+// column 16 (j / 2) + 4 (j % 2) + s / 2 + 8 (s % 2) of its block (or half).
+__device__ inline int pd_pos_of_col(int c)
 {
-    uint8_t *const wbuf = lds + PF_NABUF * PF_ABYTES;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    // the 46,080 contiguous bytes of the tile, 16 bytes a lane (the last
-    // request of a wave has 16 lanes)
-#pragma unroll
-    for (int h = 0; h < PF_DNB; ++h)
-        if (64 * h + lane < PF_DCH)
-            __builtin_amdgcn_global_load_lds(wsrc + 16 * (PF_DCH * w + 64 * h + lane),
-                                             wbuf + (PF_DCH * w + 64 * h) * 16, 16, 0, 0);
-    uint32_t a0, a1;
-    pf_act_read_addrs(lds_addr(lds), a0, a1);
-    act.request(lds, 0);
-    act.request(lds + PF_ABYTES, 1);
-    act.request(lds + 2 * PF_ABYTES, 2);
-    act.request(lds + 3 * PF_ABYTES, 3);
-    constexpr int NS1 = 16 * ROW_D, NS2 = 32 * ROW_D, NS3 = 48 * ROW_D;
-    vm_wait<6>();   // the weights and A0: younger A1, A2, A3
-    __builtin_amdgcn_s_barrier();
-    PfVals cur, nxt;
-    pf_reads_issue<0, 0, NS1, NS2, NS3, MS>(a0, a1, bs, bc, cur);
-    pf_reads_done(cur);
-#define STRATA_PF_DSTEP(B)                                                                         \
-    {                                                                                              \
-        vm_wait<4>();                                                                              \
-        __builtin_amdgcn_s_barrier();                                                              \
-        act.request(lds + ((B) & 3) * PF_ABYTES, (B) + 4 < NB_D ? (B) + 4 : NB_D - 1);             \
-        pf_reads_issue<(((B) + 1) & 3) * PF_ABYTES, BB * ((B) + 1 < NB_D ? (B) + 1 : NB_D - 1),    \
-                       NS1, NS2, NS3, MS>(a0, a1, bs, bc, nxt);                                        \
-        pf_math<MS>(cur, acc);                                                                     \
-        pf_reads_done(nxt);                                                                        \
-        cur = nxt;                                                                                 \
+    const int b = c >> 6, r = c & 15;
+    const int sj = (r >> 2) & 1, s = 2 * (r & 3) + (r >> 3);
+    if (b < 2 * PG_BLK) {
+        const int j = 2 * ((c >> 4) & 3) + sj;
+        return 256 * (b >> 2) + 64 * (b & 3) + 8 * j + s;
     }
-    STRATA_PF_DSTEP(0)
-    STRATA_PF_DSTEP(1)
-    STRATA_PF_DSTEP(2)
-    STRATA_PF_DSTEP(3)
-    STRATA_PF_DSTEP(4)
-    STRATA_PF_DSTEP(5)
-    STRATA_PF_DSTEP(6)
-    STRATA_PF_DSTEP(7)
-    STRATA_PF_DSTEP(8)
-    STRATA_PF_DSTEP(9)
-#undef STRATA_PF_DSTEP
-    vm_wait<0>();
+    const int q = 2 * (b - 2 * PG_BLK) + ((c >> 5) & 1);
+    const int j = 2 * ((c >> 4) & 1) + sj;
+    return 2 * (PG_GBYTES / 2) + 32 * q + 8 * j + s;   // after the 2 x 256 positions of groups 0, 1
+}
+
+// The down K loop, from registers and the resident activation tile.
+template <int MS>
+__device__ inline void pd_down_loop(const PgW w[3], uint32_t sel_c, uint32_t sel_d, uint32_t sel_c2,
+                                    uint32_t sel_d2, bool upper, uint32_t ae, uint32_t ao,
+                                    uint32_t ae2, uint32_t ao2, floatx4 acc[4][4])
+{
+    pg_group<0, MS>(ae, ao, w[0], sel_c, sel_d, acc);
+    pg_group<1, MS>(ae, ao, w[1], sel_c, sel_d, acc);
+    uint32_t d2[4], cw[4][4];
+    pg_extract(w[2], sel_c2, sel_d2, d2, cw);
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {   // code dwords 2 (q % 2), 2 (q % 2) + 1 of the block
+        cw[ns][0] = upper ? cw[ns][2] : cw[ns][0];
+        cw[ns][1] = upper ? cw[ns][3] : cw[ns][1];
+    }
+    half8 af[2][4];
+    pg_aread<0, 4096, MS>(ae2, af[0]);
+    pg_await<MS>(af[0]);
+    pg_step<0, 4096, 4, MS, 0>(ae2, ao2, d2, cw, af, acc);
+    pg_step<0, 4096, 4, MS, 1>(ae2, ao2, d2, cw, af, acc);
+    pg_step<0, 4096, 4, MS, 2>(ae2, ao2, d2, cw, af, acc);
+    pg_step<0, 4096, 4, MS, 3>(ae2, ao2, d2, cw, af, acc);
 }
 
 // silu(g) * u = g u / (1 + e^-g) with the hardware exp2 and reciprocal (each
@@ -592,7 +449,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
         const int j = jw + 16 * h2 + (lane & 15);
-        const int col = QK * (j >> 6) + pf_pos_of_col(j & 63);
+        const int col = pd_pos_of_col(j);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -624,16 +481,52 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rw = nt * PF_NT_D + 64 * wave;   // this wave's first output row
-    PfAct act;
+    // Activation rows (past the item's end: its first row, never stored).
+    PgAct act;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int r = 16 * wave + 8 * h + (lane >> 3);
-        act.row[h] = hperm + (size_t)(it.gp0 + (r < it.rows ? r : 0)) * FF;
+        const int r = 16 * wave + 8 * h + (lane & 7);
+        act.row[h] = reinterpret_cast<const uint8_t *>(hperm + (size_t)(it.gp0 + (r < it.rows ? r : 0)) * FF);
+        act.coff[h] = 16 * ((lane >> 3) ^ h);
     }
-    act.chunk = (lane & 7) ^ (lane >> 3);
-    const uint8_t *wsrc = blobs + (size_t)it.e * BLOB + 2 * MAT + (size_t)nt * PF_DB;
-    const uint32_t bs = lds_addr(lds + PF_NABUF * PF_ABYTES) + (64 * wave + (lane & 15)) * ROW_D;
-    const uint32_t bc = bs + 2 + 4 * (lane >> 4);
+    act.request(lds, 0);
+    act.request(lds + PG_ABYTES, 1);
+    {   // last group: request i fills row group 2 w + i / 2, chunk octet i % 2
+        const int w = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds(act.row[i >> 1] + 2 * PG_GBYTES + 128 * (i & 1) + act.coff[i >> 1],
+                                             lds + PD_G2 + (4 * w + i) * 1024, 16, 0, 0);
+    }
+    // Weight bytes of output rows rw + 16 ns + lane % 16: quarter q loads
+    // from the dword at or below its block's start (groups 0, 1: block
+    // 4 g + q; last group: block 8 + q / 2).
+    const int q = lane >> 4;
+    const uint8_t *wbase = blobs + (size_t)it.e * BLOB + 2 * MAT;
+    PgW wr[3];
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+        const uint32_t row = (uint32_t)(rw + 16 * ns + (lane & 15)) * ROW_D;
+#pragma unroll
+        for (int g = 0; g < 3; ++g) {
+            const uint32_t off = row + (g < 2 ? PG_BLK * BB * g + BB * q - 2 * (q & 1)
+                                              : 2 * PG_BLK * BB + (BB - 2) * (q >> 1));
+            wr[g].lo[ns] = *reinterpret_cast<const u32x4 *>(wbase + off);
+            wr[g].hi[ns] = *reinterpret_cast<const uint32_t *>(wbase + off + 16);
+        }
+    }
+    pg_wait_all(wr[0]);
+    pg_wait_all(wr[1]);
+    pg_wait_all(wr[2]);
+    __builtin_amdgcn_s_barrier();   // every wave's activations have landed
+    const int odd = q & 1, odd2 = q >> 1;
+    const uint32_t sel_c = odd ? 0x07060504u : 0x05040302u, sel_d = odd ? 0x03020302u : 0x01000100u;
+    const uint32_t sel_c2 = odd2 ? 0x07060504u : 0x05040302u, sel_d2 = odd2 ? 0x03020302u : 0x01000100u;
+    const int b = (lane >> 3) & 1;
+    const uint32_t abase = lds_addr(lds) + (32 * b + 8 * q) * 128 + 16 * (lane & 7);
+    const uint32_t ae = abase + 128 * b, ao = abase - 128 * b;
+    const uint32_t abase2 = lds_addr(lds) + PD_G2 + 2048 * b + 512 * q + 16 * (lane & 7);
+    const uint32_t ae2 = abase2 + 128 * b, ao2 = abase2 - 128 * b;
     floatx4 acc[4][4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns)
@@ -642,16 +535,16 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
             acc[ns][mi] = (floatx4){0.f, 0.f, 0.f, 0.f};
     switch ((it.rows + 15) >> 4) {
     case 1:
-        pf_down_loop<1>(wsrc, act, lds, bs, bc, acc);
+        pd_down_loop<1>(wr, sel_c, sel_d, sel_c2, sel_d2, odd, ae, ao, ae2, ao2, acc);
         break;
     case 2:
-        pf_down_loop<2>(wsrc, act, lds, bs, bc, acc);
+        pd_down_loop<2>(wr, sel_c, sel_d, sel_c2, sel_d2, odd, ae, ao, ae2, ao2, acc);
         break;
     case 3:
-        pf_down_loop<3>(wsrc, act, lds, bs, bc, acc);
+        pd_down_loop<3>(wr, sel_c, sel_d, sel_c2, sel_d2, odd, ae, ao, ae2, ao2, acc);
         break;
     default:
-        pf_down_loop<4>(wsrc, act, lds, bs, bc, acc);
+        pd_down_loop<4>(wr, sel_c, sel_d, sel_c2, sel_d2, odd, ae, ao, ae2, ao2, acc);
         break;
     }
 #pragma unroll
