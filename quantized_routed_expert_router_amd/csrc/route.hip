@@ -12,10 +12,12 @@
 //  gemm_kernel    bf16 MFMA over the exact three-term bf16 split of xhat
 //                 (fp32-accurate logits); identical router rows give
 //                 identical logits.
-//  topk_kernel    one wave per token: softmax in fp32, ten rounds of a
-//                 wave-wide max of p and min of the id among the maxima
-//                 (the order p desc, id asc), clamped renorm.
+//  topk_kernel    one wave per token (route_token, shared with the decode
+//                 top-k): softmax in fp32, each lane's 8 candidates sorted,
+//                 ten rounds of a wave-wide max over the lanes' heads (the
+//                 order p desc, id asc), clamped renorm.
 #include "common.hpp"
+#include "route_token.hpp"
 
 namespace strata {
 
@@ -262,55 +264,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     const int t = blockIdx.x * 4 + wave;
     if (t >= T)
         return;
-    const float *lt = logits + (size_t)t * E;
-    float l[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        l[i] = lt[lane + 64 * i];
-    float m = l[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i)
-        m = fmaxf(m, l[i]);
-    m = wave_max63(m);
-    float p[8];
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        p[i] = expf(l[i] - m);
-        s += p[i];
-    }
-    s = wave_sum63(s);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        p[i] = p[i] / s;
-    unsigned taken = 0;
-    int my_id = 0;
-    float my_p = 0.f;
-    float sel_sum = 0.f;
-    for (int k = 0; k < K; ++k) {
-        float bp = -1.f;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = lane + 64 * i;
-            const bool better = p[i] > bp || (p[i] == bp && e < be);
-            if (!((taken >> i) & 1) && better) {
-                bp = p[i];
-                be = e;
-            }
-        }
-        // the best candidate: the largest p, and among equal p the lowest id
-        const float pm = wave_max63(bp);
-        be = wave_min63(bp == pm ? be : 0x7fffffff);
-        bp = pm;
-        if ((be & 63) == lane)
-            taken |= 1u << ((be >> 6) & 7);
-        if (lane == k) {
-            my_id = be;
-            my_p = bp;
-        }
-        sel_sum += bp;
-    }
+    int my_id;
+    float my_p, sel_sum;
+    route_token(logits + (size_t)t * E, 1.f, nullptr, my_id, my_p, sel_sum);
     const float den = fmaxf(sel_sum, 6.103515625e-05f);   // clamp 2^-14
     if (lane < K) {
         ids[(size_t)t * K + lane] = my_id;
