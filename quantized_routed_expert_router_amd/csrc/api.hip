@@ -12,7 +12,8 @@ hipError_t launch_logits(const uint16_t *xsplit, int T, const uint16_t *R, const
                          float *logits, hipStream_t st);
 hipError_t launch_topk(const float *logits, int T, int32_t *ids, float *w, hipStream_t st);
 hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
-                        int32_t *active, int32_t *gcount, hipStream_t st);
+                        int32_t *active, int32_t *gcount, int max_items, int32_t *mlist,
+                        int32_t *nitems, hipStream_t st);
 hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_items,
                        int32_t *mlist, int32_t *nitems, hipStream_t st);
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
@@ -115,8 +116,11 @@ Carve carve(void *ws, int T)
     } while (0)
 
 // The experts for T tokens of a grouped layer (activation prep already done).
+// planned: the prefill work list is already in c.mlist / c.nitems (written
+// by the grouping of the layer call).
 int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
-                const int32_t *slots, const int32_t *active, float *out, int T, hipStream_t st)
+                const int32_t *slots, const int32_t *active, float *out, int T, hipStream_t st,
+                bool planned = false)
 {
     hipEvent_t e0, e1;
     take_events(e0, e1);
@@ -124,7 +128,8 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
         STRATA_TRY(launch_decode_experts(blobs, c.erec, slots, c.xq, c.hq, out, T, c.esync, nullptr,
                                          nullptr, nullptr, nullptr, nullptr, nullptr, e0, e1, st));
     } else {
-        STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
+        if (!planned)
+            STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
         STRATA_TRY(launch_prefill_experts(blobs, offsets, slots, active, c.mlist, c.nitems,
                                           c.L.max_items, c.xperm, c.hperm, out, T, e0, e1, st));
     }
@@ -181,7 +186,8 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
         STRATA_TRY(launch_prep(x, T, rms, c.xsplit, c.xperm, st));
         STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
         STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
-        STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, c.gcount, st));
+        STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, c.gcount, c.L.max_items,
+                                c.mlist, c.nitems, st));
     }
     const bool res = flags & STRATA_RESIDUAL;
     if (is_decode(T)) {   // the experts kernel finishes the combine
@@ -193,7 +199,7 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
                                          e0, e1, st));
         return STRATA_OK;
     }
-    if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st)))
+    if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st, true)))
         return rc;
     STRATA_TRY(launch_combine(c.out, w_o, T, y, res ? x : nullptr, 0, st));
     return STRATA_OK;
@@ -254,8 +260,8 @@ int strata_moe_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots
         return rc;
     if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(slots, 4) || !aligned(active, 4))
         return STRATA_E_ALIGN;
-    STRATA_TRY(launch_group(ids, T, offsets, slots, active, carve(ws, T).gcount,
-                            (hipStream_t)stream));
+    STRATA_TRY(launch_group(ids, T, offsets, slots, active, carve(ws, T).gcount, 0, nullptr,
+                            nullptr, (hipStream_t)stream));
     return STRATA_OK;
 }
 

@@ -177,9 +177,14 @@ __global__ __launch_bounds__(GB_SLOTS) void group_count_kernel(const int32_t *__
         gcount[(size_t)b * E + i] = hist[i];
 }
 
+// With mlist given it also writes the prefill work list (as plan_kernel
+// does from offsets and active): expert e's chunks sit at the exclusive scan
+// of the chunk counts, which in ascending e is the active order.
 __global__ __launch_bounds__(E) void group_scan_kernel(int nb, int32_t *__restrict__ gcount,
                                                        int32_t *__restrict__ offsets,
-                                                       int32_t *__restrict__ active)
+                                                       int32_t *__restrict__ active, int max_items,
+                                                       int32_t *__restrict__ mlist,
+                                                       int32_t *__restrict__ nitems)
 {
     __shared__ int tmp[8];
     __shared__ int tot;
@@ -207,6 +212,19 @@ __global__ __launch_bounds__(E) void group_scan_kernel(int nb, int32_t *__restri
         active[1 + pos] = e;
     if (e == 0)
         active[0] = tot;
+    if (!mlist)
+        return;
+    const int nch = (run + PF_M - 1) / PF_M;
+    const int base = block_exclusive_scan_512(nch, e, tmp, &tot);
+    for (int c = 0; c < nch; ++c) {
+        const int it = base + c;
+        if (it < max_items) {
+            mlist[2 * it] = pos;
+            mlist[2 * it + 1] = c * PF_M;
+        }
+    }
+    if (e == 0)
+        nitems[0] = min(tot, max_items);
 }
 
 __global__ __launch_bounds__(GB_SLOTS) void group_scatter_kernel(const int32_t *__restrict__ ids,
@@ -275,7 +293,8 @@ __global__ __launch_bounds__(512) void plan_kernel(const int32_t *__restrict__ o
 }
 
 hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
-                        int32_t *active, int32_t *gcount, hipStream_t st)
+                        int32_t *active, int32_t *gcount, int max_items, int32_t *mlist,
+                        int32_t *nitems, hipStream_t st)
 {
     if (is_decode(T) || !gcount) {
         hipLaunchKernelGGL(group_kernel, dim3(1), dim3(GR_THREADS), 0, st, ids, T, offsets, slots,
@@ -284,7 +303,8 @@ hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *sl
     }
     const int N = T * K, nb = (N + GB_SLOTS - 1) / GB_SLOTS;
     hipLaunchKernelGGL(group_count_kernel, dim3(nb), dim3(GB_SLOTS), 0, st, ids, N, gcount);
-    hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(E), 0, st, nb, gcount, offsets, active);
+    hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(E), 0, st, nb, gcount, offsets, active,
+                       max_items, mlist, nitems);
     hipLaunchKernelGGL(group_scatter_kernel, dim3(nb), dim3(GB_SLOTS), 0, st, ids, N,
                        (const int32_t *)gcount, (const int32_t *)offsets, slots);
     return hipGetLastError();
