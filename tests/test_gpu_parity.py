@@ -174,6 +174,53 @@ def test_timing_hook_records_and_leaves_results_alone(T):
         m.strata_moe_time_next_kernel(torch.cuda.Event(enable_timing=True), e1)
 
 
+def test_prefill_experts_row_boundaries():
+    """Experts entry point on a hand-made routing that gives experts exactly
+    1, 15, 16, 17, 48, 49, 64, 65 and 128 rows: every count of 16-row
+    subtiles an item can have, items that fill their 64-token chunk exactly,
+    and experts split over two and three chunks with ragged last chunks.  The
+    per-slot outputs are compared with the oracle's expert FFN."""
+    import torch
+    import oracle
+    m = hz.qm()
+    seed, T = 11, 200
+    rng = np.random.default_rng(seed)
+    counts = {0: 1, 1: 15, 2: 16, 3: 17, 4: 48, 5: 49, 6: 64, 7: 65, 8: 128}
+    rows = [[] for _ in range(T)]
+    for e, c in counts.items():
+        for t in rng.choice(T, c, replace=False):
+            rows[t].append(e)
+    for t in range(T):   # fill each token up to 10 distinct experts from 9..511
+        rest = rng.choice(np.arange(9, 512), 10 - len(rows[t]), replace=False)
+        rows[t] += list(rest)
+        rng.shuffle(rows[t])
+    ids = np.array(rows, dtype=np.int32)
+    cnt = np.bincount(ids.ravel(), minlength=512)
+    assert all(cnt[e] == c for e, c in counts.items())
+    x = rng.standard_normal((T, inputs.H)).astype(np.float32)
+    _say(f"case: prefill experts row boundaries T={T}, seed {seed}")
+    xd = hz.cuda(x)
+    ws = m.workspace(T)
+    offsets = torch.empty(513, dtype=torch.int32, device="cuda")
+    slots = torch.empty(T * 10, dtype=torch.int32, device="cuda")
+    active = torch.empty(513, dtype=torch.int32, device="cuda")
+    out = torch.empty((T * 10, inputs.H), dtype=torch.float32, device="cuda")
+    m.strata_moe_group(hz.cuda(ids), offsets, slots, active, ws)
+    m.strata_moe_experts(xd, hz.store(seed), offsets, slots, active, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    blobs = scr.BlobSource(seed).get_many(np.unique(ids))
+    ref = oracle.experts(x.astype(np.float64), ids, blobs, inputs.E, inputs.H, inputs.FF)
+    for e in counts:   # the boundary experts, slot by slot
+        sl = np.nonzero(ids.ravel() == e)[0]
+        rel = float(np.max(np.abs(got[sl] - ref[sl])) / np.max(np.abs(ref[sl])))
+        _say(f"  expert {e} ({counts[e]} rows): max|do|/max|o| = {rel:.3e}")
+        assert rel <= hz.Y_TOL, (e, rel)
+    rel = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    _say(f"  all slots: max|do|/max|o| = {rel:.3e}")
+    assert rel <= hz.Y_TOL
+
+
 def test_group_matches_cpu_counting_sort():
     import torch
     m = hz.qm()
