@@ -16,7 +16,7 @@ one token's), stack-decode (48-layer T = 1 stack on the full 34 GB store),
 prefill (T = 2048 layer), stack-prefill (one 2048-token chunk through 48
 Zipf-biased layers).
 
-Prints one JSON line.  With --gpus > 1 it exits: this build measures one GPU.
+Prints one JSON line.  With --gpus > 1 it exits: the measurement is of one GPU.
 """
 import argparse
 import json
@@ -34,13 +34,13 @@ MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
 FLOP_PER_SLOT = 3 * 2 * 2560 * 640
 
 WORKLOADS = {
-    "window": dict(cfg=1, T=4, layers=1, copies=48),
-    "window-corr": dict(cfg=5, T=4, layers=1, copies=48),
-    "token": dict(cfg=0, T=1, layers=1, copies=48),
-    "stack-decode": dict(cfg=2, T=1, layers=48, copies=1),
-    "stack-decode-lookahead": dict(cfg=2, T=1, layers=48, copies=1, lookahead=True),
-    "prefill": dict(cfg=3, T=2048, layers=1, copies=4),
-    "stack-prefill": dict(cfg=4, T=2048, layers=48, copies=1),
+    "window": dict(wl="layer-T4-window", T=4, layers=1, copies=48),
+    "window-corr": dict(wl="layer-T4-correlated-window", T=4, layers=1, copies=48),
+    "token": dict(wl="layer-T1", T=1, layers=1, copies=48),
+    "stack-decode": dict(wl="stack48-T1", T=1, layers=48, copies=1),
+    "stack-decode-lookahead": dict(wl="stack48-T1", T=1, layers=48, copies=1, lookahead=True),
+    "prefill": dict(wl="layer-T2048-prefill", T=2048, layers=1, copies=4),
+    "stack-prefill": dict(wl="stack48-T32768-zipf", T=2048, layers=48, copies=1),
 }
 
 
@@ -97,7 +97,8 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
-              "(the layer shards by tokens with no collective; see DESIGN.md)", file=sys.stderr)
+              "(the layer would shard by tokens: each GPU holds the whole store and runs its own "
+              "tokens, with no collective)", file=sys.stderr)
         sys.exit(2)
     import torch
     if a.calibrate_copy_mb:
@@ -113,7 +114,7 @@ def main():
     import quantized_routed_expert_router_amd as m
     m.lib()
     wl = WORKLOADS[a.workload]
-    cfg = inputs.CONFIGS[wl["cfg"]]
+    cfg = inputs.WORKLOADS[wl["wl"]]
     T, L, seed = wl["T"], wl["layers"], cfg["seed"]
     stack = L > 1
     flags = (m.RMSNORM | m.RESIDUAL) if stack else 0

@@ -141,19 +141,21 @@ def draw_zipf_bias(rng, e=E, s=1.1):
 
 
 # The five workload configurations: tokens, layers, seed, stack flags.
-CONFIGS = {
-    0: dict(name="layer-T1", T=1, layers=1, seed=0, stack=False, zipf=False, chunk=1),
-    1: dict(name="layer-T4-window", T=4, layers=1, seed=1, stack=False, zipf=False, chunk=4),
-    2: dict(name="stack48-T1", T=1, layers=48, seed=2, stack=True, zipf=False, chunk=1),
-    3: dict(name="layer-T2048-prefill", T=2048, layers=1, seed=3, stack=False, zipf=False,
-            chunk=2048),
-    4: dict(name="stack48-T32768-zipf", T=32768, layers=48, seed=4, stack=True, zipf=True,
-            chunk=2048),
-    # not one of the five above: a T = 4 verify window of correlated tokens
-    # (draw_window), for the window-dedup workload
-    5: dict(name="layer-T4-correlated-window", T=4, layers=1, seed=5, stack=False, zipf=False,
-            chunk=4, window=True),
-}
+_WORKLOAD_LIST = [
+    dict(name="layer-T1", T=1, layers=1, seed=0, stack=False, zipf=False, chunk=1),
+    dict(name="layer-T4-window", T=4, layers=1, seed=1, stack=False, zipf=False, chunk=4),
+    dict(name="stack48-T1", T=1, layers=48, seed=2, stack=True, zipf=False, chunk=1),
+    dict(name="layer-T2048-prefill", T=2048, layers=1, seed=3, stack=False, zipf=False,
+         chunk=2048),
+    dict(name="stack48-T32768-zipf", T=32768, layers=48, seed=4, stack=True, zipf=True,
+         chunk=2048),
+    # a T = 4 verify window of correlated tokens (draw_window), for the
+    # window-dedup workload
+    dict(name="layer-T4-correlated-window", T=4, layers=1, seed=5, stack=False, zipf=False,
+         chunk=4, window=True),
+]
+# The seeded synthetic workloads, by name.
+WORKLOADS = {w["name"]: w for w in _WORKLOAD_LIST}
 
 
 # ---------------------------------------------------------------- device side

@@ -7,7 +7,7 @@
  * never links or calls it.  No blocking, fusion or reordering beyond what the
  * definitions below state; OpenMP only splits independent rows.
  *
- * Readings of points the pages leave open (each also listed in the design doc):
+ * Readings of points the pages leave open:
  *  - block field order: fp16 scale in bytes 0-1, then 16 code bytes;
  *  - matrix order in a blob: gate, up, down; each blocked along its input
  *    dimension: gate/up are [FF][H], down is [H][FF], row-major;

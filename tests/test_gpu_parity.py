@@ -40,14 +40,14 @@ def test_device_fill_matches_host_generator():
     assert np.array_equal(one.cpu().numpy(), inputs.gen_blob(2, 47 * 512 + 5))
 
 
-@pytest.mark.parametrize("cfg", [0, 1])
-def test_decode_configs(cfg):
-    c = inputs.CONFIGS[cfg]
-    _say(f"case: config {cfg} ({c['name']}), T={c['T']}, seed {c['seed']}")
+@pytest.mark.parametrize("name", ["layer-T1", "layer-T4-window"])
+def test_decode_workloads(name):
+    c = inputs.WORKLOADS[name]
+    _say(f"case: {name}, T={c['T']}, seed {c['seed']}")
     x, R, _ = hz.single_layer_case(c["seed"], c["T"])
     ids, w, y, _ = hz.gpu_layer(x, R, hz.store(c["seed"]))
     oids, ow, oy = hz.oracle_rows(x, R, c["seed"], np.arange(c["T"]))
-    hz.check(f"config {cfg}", ids, w, y, oids, ow, oy)
+    hz.check(name, ids, w, y, oids, ow, oy)
 
 
 @pytest.mark.parametrize("T", [2, 3, 5, 8, 16])
@@ -87,8 +87,8 @@ def test_prefill_skewed_multi_chunk_experts():
 
 
 @pytest.mark.timeout(600)
-def test_config3_prefill_sampled():
-    c = inputs.CONFIGS[3]
+def test_layer_t2048_prefill_sampled():
+    c = inputs.WORKLOADS["layer-T2048-prefill"]
     _say(f"case: layer-T2048-prefill T={c['T']} seed {c['seed']}")
     x, R, redrawn = hz.single_layer_case(c["seed"], c["T"])
     ids, w, y, _ = hz.gpu_layer(x, R, hz.store(c["seed"]))

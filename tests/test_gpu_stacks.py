@@ -71,8 +71,8 @@ def _run_stack_gpu(x, routers, store, biases=None, rows=None):
 
 
 @pytest.mark.timeout(900)
-def test_config2_stack_t1():
-    c = inputs.CONFIGS[2]
+def test_stack48_t1():
+    c = inputs.WORKLOADS["stack48-T1"]
     seed = c["seed"]
     st = inputs.Streams(seed)
     x0 = inputs.draw_x(st.x, 1)
@@ -105,8 +105,8 @@ def test_config2_stack_t1():
 
 
 @pytest.mark.timeout(1200)
-def test_config4_stack_sampled():
-    c = inputs.CONFIGS[4]
+def test_stack48_t32768_zipf_sampled():
+    c = inputs.WORKLOADS["stack48-T32768-zipf"]
     seed, T, chunk = c["seed"], c["T"], c["chunk"]
     st = inputs.Streams(seed)
     x = inputs.draw_x(st.x, T)
