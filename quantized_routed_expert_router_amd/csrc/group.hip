@@ -159,6 +159,7 @@ __global__ __launch_bounds__(GR_THREADS) void group_kernel(const int32_t *__rest
 // waves' counts, plus the block's start and the expert's offset
 // (group_scatter_kernel).
 constexpr int GB_SLOTS = 256;   // slots per block
+constexpr int GS_BATCH = 40;    // per-block counts one scan thread loads at once (T = 2048: two rounds)
 
 __global__ __launch_bounds__(GB_SLOTS) void group_count_kernel(const int32_t *__restrict__ ids,
                                                                int N, int32_t *__restrict__ gcount)
@@ -190,13 +191,13 @@ __global__ __launch_bounds__(E) void group_scan_kernel(int nb, int32_t *__restri
     __shared__ int tot;
     const int e = threadIdx.x;
     int run = 0;   // expert e's slots in the blocks before b: block b's start
-    for (int b0 = 0; b0 < nb; b0 += 16) {   // 16 counts in flight, then their starts
-        int c[16];
+    for (int b0 = 0; b0 < nb; b0 += GS_BATCH) {   // GS_BATCH counts in flight, then their starts
+        int c[GS_BATCH];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < GS_BATCH; ++j)
             c[j] = b0 + j < nb ? gcount[(size_t)(b0 + j) * E + e] : 0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < GS_BATCH; ++j) {
             if (b0 + j < nb)
                 gcount[(size_t)(b0 + j) * E + e] = run;
             run += c[j];
