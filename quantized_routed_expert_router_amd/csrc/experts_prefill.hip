@@ -104,11 +104,6 @@ __device__ inline uint32_t lds_addr(uint8_t *p)
     return (uint32_t)(uintptr_t)(lds_u8 *)p;
 }
 
-template <int N> __device__ inline void vm_wait()
-{
-    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
-}
-
 // Activation requests of gate/up group g for this wave: 8 requests of 1 KB,
 // request i filling row group 2 w + i / 4, chunk octet i % 4.
 struct PgAct {
