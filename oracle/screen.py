@@ -42,14 +42,19 @@ def top11_gap(lg):
     return np.min(s[:, :-1] - s[:, 1:], axis=1)
 
 
-def screened_x(st, T, R_bits, bias=None, rmsnorm=False, margin=TIE_MARGIN, h=inputs.H):
+def screened_x(st, T, R_bits, bias=None, rmsnorm=False, margin=TIE_MARGIN, h=inputs.H,
+               extra=()):
     """x [T][H] from st.x; rows whose top-11 gap is within `margin` are redrawn
-    from st.x_redraw, in row order.  Returns (x, number of redrawn rows)."""
+    from st.x_redraw, in row order.  `extra` lists further (router, bias)
+    pairs the rows must also clear (a second router applied to the same
+    input).  Returns (x, number of redrawn rows)."""
     x = inputs.draw_x(st.x, T, h=h)
     redrawn = 0
+    pairs = [(R_bits, bias)] + list(extra)
     for _ in range(1000):
         xh = rms_np(x) if rmsnorm else x.astype(np.float64)
-        bad = np.nonzero(top11_gap(logits_np(xh, R_bits, bias)) <= margin)[0]
+        gap = np.min(np.stack([top11_gap(logits_np(xh, R, b)) for R, b in pairs]), axis=0)
+        bad = np.nonzero(gap <= margin)[0]
         if bad.size == 0:
             return x, redrawn
         for t in bad:

@@ -103,6 +103,55 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
+def _shape(name, t, shape):
+    """Raise ValueError unless tensor t (or None, when allowed by the caller)
+    has exactly `shape`: undersized buffers never reach the kernels."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _opt_shape(name, t, shape):
+    if t is not None:
+        _shape(name, t, shape)
+
+
+def _min_numel(name, t, n):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dim() != 1 or t.numel() < n:
+        raise ValueError(f"{name} must be 1-D with at least {n} elements, got {tuple(t.shape)}")
+
+
+def _tokens(x):
+    """T of an activation tensor x [T][H] (checked against the layer width)."""
+    if x is None or x.dim() != 2 or x.shape[1] != H:
+        raise ValueError(f"x must have shape (T, {H}), got "
+                         f"{None if x is None else tuple(x.shape)}")
+    T = int(x.shape[0])
+    if not 1 <= T <= T_MAX:
+        raise ValueError(f"T = {T} outside 1..{T_MAX}")
+    return T
+
+
+def _router_shape(name, R):
+    if R is None or R.numel() != E * H or R.dim() not in (1, 2) or (
+            R.dim() == 2 and tuple(R.shape) != (E, H)):
+        raise ValueError(f"{name} must hold {E} x {H} bf16 values, got "
+                         f"{None if R is None else tuple(R.shape)}")
+
+
+def _store_shape(name, blobs):
+    _min_numel(name, blobs, E * BLOB)
+
+
+def _ws_shape(ws, T):
+    need = strata_moe_workspace_bytes(T)
+    if ws is None or ws.dim() != 1 or _nbytes(ws) < need:
+        raise ValueError(f"workspace must be a 1-D tensor of at least {need} bytes for T = {T}")
+
+
 def _check(fn, rc):
     if rc != OK:
         raise StrataError(fn, rc)
@@ -131,7 +180,12 @@ def workspace(T, device="cuda"):
 
 def strata_moe_route(x, router, ids, w, ws, bias=None, flags=0, stream=None):
     import torch
-    T = x.shape[0]
+    T = _tokens(x)
+    _router_shape("router", router)
+    _opt_shape("bias", bias, (E,))
+    _shape("ids", ids, (T, K))
+    _shape("w", w, (T, K))
+    _ws_shape(ws, T)
     rc = lib().strata_moe_route(_p(x, torch.float32), T, _p_router(router),
                                 _p(bias, torch.float32), flags, _p(ids, torch.int32),
                                 _p(w, torch.float32), _p(ws), _nbytes(ws), _s(stream))
@@ -140,7 +194,13 @@ def strata_moe_route(x, router, ids, w, ws, bias=None, flags=0, stream=None):
 
 def strata_moe_group(ids, offsets, slots, active, ws, stream=None):
     import torch
-    T = ids.shape[0]
+    if ids is None or ids.dim() != 2 or ids.shape[1] != K or not 1 <= ids.shape[0] <= T_MAX:
+        raise ValueError(f"ids must have shape (T, {K}) with 1 <= T <= {T_MAX}")
+    T = int(ids.shape[0])
+    _shape("offsets", offsets, (E + 1,))
+    _shape("slots", slots, (T * K,))
+    _shape("active", active, (E + 1,))
+    _ws_shape(ws, T)
     rc = lib().strata_moe_group(_p(ids, torch.int32), T, _p(offsets, torch.int32),
                                 _p(slots, torch.int32), _p(active, torch.int32), _p(ws),
                                 _nbytes(ws), _s(stream))
@@ -149,7 +209,13 @@ def strata_moe_group(ids, offsets, slots, active, ws, stream=None):
 
 def strata_moe_experts(x, blobs, offsets, slots, active, out, ws, flags=0, stream=None):
     import torch
-    T = x.shape[0]
+    T = _tokens(x)
+    _store_shape("blobs", blobs)
+    _shape("offsets", offsets, (E + 1,))
+    _shape("slots", slots, (T * K,))
+    _shape("active", active, (E + 1,))
+    _shape("out", out, (T * K, H))
+    _ws_shape(ws, T)
     rc = lib().strata_moe_experts(_p(x, torch.float32), T, _p(blobs, torch.uint8),
                                   _p(offsets, torch.int32), _p(slots, torch.int32),
                                   _p(active, torch.int32), flags, _p(out, torch.float32), _p(ws),
@@ -159,7 +225,9 @@ def strata_moe_experts(x, blobs, offsets, slots, active, out, ws, flags=0, strea
 
 def strata_moe_combine(out, w, y, flags=0, stream=None):
     import torch
-    T = y.shape[0]
+    T = _tokens(y)
+    _shape("out", out, (T * K, H))
+    _shape("w", w, (T, K))
     rc = lib().strata_moe_combine(_p(out, torch.float32), _p(w, torch.float32), T, flags,
                                   _p(y, torch.float32), _s(stream))
     _check("strata_moe_combine", rc)
@@ -181,7 +249,14 @@ def strata_moe_time_next_kernel(start=None, stop=None):
 def strata_moe_layer(x, router, blobs, ws, bias=None, flags=0, y=None, ids=None, w=None,
                      stream=None):
     import torch
-    T = x.shape[0]
+    T = _tokens(x)
+    _router_shape("router", router)
+    _store_shape("blobs", blobs)
+    _opt_shape("bias", bias, (E,))
+    _opt_shape("y", y, (T, H))
+    _opt_shape("ids", ids, (T, K))
+    _opt_shape("w", w, (T, K))
+    _ws_shape(ws, T)
     rc = lib().strata_moe_layer(_p(x, torch.float32), T, _p_router(router),
                                 _p(bias, torch.float32), _p(blobs, torch.uint8), flags,
                                 _p(y, torch.float32), _p(ids, torch.int32), _p(w, torch.float32),
@@ -193,7 +268,18 @@ def strata_moe_layer_lookahead(x, router, blobs, ws, router_next, blobs_next, bi
                                bias_next=None, flags=0, y=None, ids=None, w=None, pred=None,
                                stream=None):
     import torch
-    T = x.shape[0]
+    T = _tokens(x)
+    _router_shape("router", router)
+    _router_shape("router_next", router_next)
+    _store_shape("blobs", blobs)
+    _store_shape("blobs_next", blobs_next)
+    _opt_shape("bias", bias, (E,))
+    _opt_shape("bias_next", bias_next, (E,))
+    _opt_shape("y", y, (T, H))
+    _opt_shape("ids", ids, (T, K))
+    _opt_shape("w", w, (T, K))
+    _opt_shape("pred", pred, (T, K))
+    _ws_shape(ws, T)
     rc = lib().strata_moe_layer_lookahead(
         _p(x, torch.float32), T, _p_router(router), _p(bias, torch.float32),
         _p(blobs, torch.uint8), flags, _p(y, torch.float32), _p(ids, torch.int32),

@@ -102,6 +102,15 @@ def single_layer_case(seed, T, bias=None, margin=scr.TIE_MARGIN):
     return x, R, redrawn
 
 
-def oracle_rows(x, R, seed, rows, bias=None, rmsnorm=False, layer=0):
-    src = scr.BlobSource(seed)
-    return scr.oracle_layer(x[rows], R, src, layer, bias=bias, rmsnorm=rmsnorm)
+def oracle_rows(x, R, seed, rows, bias=None, rmsnorm=False, layer=0, chunk=512, src=None):
+    """The oracle's layer on rows `rows` of x, run `chunk` rows at a time (the
+    per-slot expert outputs of a chunk are held in fp64).  Returns (ids, w, y)."""
+    src = scr.BlobSource(seed) if src is None else src
+    rows = np.asarray(rows)
+    parts = []
+    for i in range(0, rows.size, chunk):
+        parts.append(scr.oracle_layer(x[rows[i:i + chunk]], R, src, layer, bias=bias,
+                                      rmsnorm=rmsnorm))
+        if rows.size > chunk:
+            print(f"  oracle rows {min(i + chunk, rows.size)}/{rows.size}", flush=True)
+    return tuple(np.concatenate([p[j] for p in parts]) for j in range(3))

@@ -98,3 +98,51 @@ def test_binding_refuses_host_tensors(m):
     x = torch.zeros((1, 2560))
     with pytest.raises(ValueError):
         m.strata_moe_route(x, x, x, x, x)
+
+
+def test_binding_checks_sizes_before_the_call(m):
+    """Every wrapper checks shapes and sizes before it passes a pointer: an
+    undersized tensor raises ValueError naming it, on the host."""
+    import torch
+    T = 4
+    x = torch.zeros((T, 2560))
+    R = torch.zeros((512, 2560), dtype=torch.int16)
+    ids = torch.zeros((T, 10), dtype=torch.int32)
+    w = torch.zeros((T, 10))
+    ws = torch.zeros(m.strata_moe_workspace_bytes(T), dtype=torch.uint8)
+    store = torch.zeros(512 * 1382400, dtype=torch.uint8)
+    offsets = torch.zeros(513, dtype=torch.int32)
+    slots = torch.zeros(T * 10, dtype=torch.int32)
+    active = torch.zeros(513, dtype=torch.int32)
+    out = torch.zeros((T * 10, 2560))
+
+    def bad(fn, *a, what, **k):
+        with pytest.raises(ValueError, match=what):
+            fn(*a, **k)
+
+    bad(m.strata_moe_route, x[:, :2559], R, ids, w, ws, what="x must")
+    bad(m.strata_moe_route, torch.zeros((0, 2560)), R, ids, w, ws, what="T = 0")
+    bad(m.strata_moe_route, x, R[:511], ids, w, ws, what="router")
+    bad(m.strata_moe_route, x, R, ids[:3], w, ws, what="ids")
+    bad(m.strata_moe_route, x, R, ids, w[:, :9], ws, what="w must")
+    bad(m.strata_moe_route, x, R, ids, w, ws[:-1], what="workspace")
+    bad(m.strata_moe_route, x, R, ids, w, ws, bias=torch.zeros(511), what="bias")
+    bad(m.strata_moe_group, ids[:, :9], offsets, slots, active, ws, what="ids")
+    bad(m.strata_moe_group, ids, offsets[:512], slots, active, ws, what="offsets")
+    bad(m.strata_moe_group, ids, offsets, slots[:-1], active, ws, what="slots")
+    bad(m.strata_moe_group, ids, offsets, slots, active[:1], ws, what="active")
+    bad(m.strata_moe_experts, x, store[:-1], offsets, slots, active, out, ws, what="blobs")
+    bad(m.strata_moe_experts, x, store, offsets, slots, active, out[:-1], ws, what="out")
+    bad(m.strata_moe_combine, out[:-10], w, x, what="out")
+    bad(m.strata_moe_combine, out, w[:2], x, what="w must")
+    bad(m.strata_moe_layer, x, R, store[:100], ws, y=x, what="blobs")
+    bad(m.strata_moe_layer, x, R, store, ws, y=x[:2], what="y must")
+    bad(m.strata_moe_layer, x, R, store, ws, y=x, ids=ids[:1], what="ids")
+    bad(m.strata_moe_layer, x, R, store, ws[:10], y=x, what="workspace")
+    bad(m.strata_moe_layer_lookahead, x, R, store, ws, R[:1], store, y=x, what="router_next")
+    bad(m.strata_moe_layer_lookahead, x, R, store, ws, R, store[:5], y=x, what="blobs_next")
+    bad(m.strata_moe_layer_lookahead, x, R, store, ws, R, store, y=x, pred=ids[:2],
+        what="pred")
+    # right sizes, host memory: refused for not being on the GPU
+    bad(m.strata_moe_route, x, R, ids, w, ws, what="GPU")
+    bad(m.strata_moe_layer, x, R, store, ws, y=x, ids=ids, w=w, what="GPU")

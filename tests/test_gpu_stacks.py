@@ -10,11 +10,13 @@ Two checks per stack:
    decode stack (routers screened with a wide margin) ids must match the
    oracle trajectory at every layer and y, x stay within 2e-3 of max|.|; w
    inherits the fp32 residual drift, so it only gets W_TOL_STACK.  For the
-   prefill stack the residual stream grows to |x| ~ 1e2 within a few layers
-   and a token's experts can change with that drift, so the end-to-end part
-   there checks properties of the GPU's own results (row weights sum to 1,
-   distinct ids, final x = x0 + the layers' y), the first layer against the
-   oracle, and reports the drift from the oracle trajectory.
+   prefill stack (32,768 Zipf-routed tokens; the per-layer check runs on 4
+   seeded layers x 64 seeded tokens) the residual stream grows to |x| ~ 1e2
+   within a few layers and a token's experts can change with that drift, so
+   the end-to-end part checks properties of the GPU's own results (row
+   weights sum to 1, distinct ids, final x = x0 + the layers' y), the first
+   layer against the oracle at the full bar, and bounds the drift from the
+   oracle trajectories on the rows still on the oracle's experts.
 """
 import numpy as np
 import pytest
@@ -28,8 +30,11 @@ pytestmark = pytest.mark.gpu
 # The GPU's fp32 residual stream drifts from the fp64 one by rounding over 48
 # layers, so stacked runs keep a wider router margin than single layers.
 STACK_MARGIN_T1 = 1e-3
-STACK_MARGIN_PREFILL = 3e-4
+# End-to-end drift bounds (about twice the drift measured on MI355X; the
+# per-layer checks on identical inputs hold the full bar).
 W_TOL_STACK = 2e-2
+ZIPF_E2E_DY = 0.1
+ZIPF_E2E_DW = 2e-2
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -85,13 +90,15 @@ def test_stack48_t1():
     store = inputs.layer_store(seed, 0, n_layers=48)
     print("case: stack48-T1 GPU stack (48 layers, 34 GB store)", flush=True)
     got = _run_stack_gpu(x0, routers, store)
-    worst = 0.0
+    worst, worst_dw = 0.0, 0.0
     for l in range(48):
         worst = max(worst, hz.check(f"stack48-T1 e2e layer {l}", got["ids"][l], got["w"][l],
                                     got["y"][l], traj["ids"][l], traj["w"][l], traj["y"][l],
                                     w_tol=W_TOL_STACK))
+        worst_dw = max(worst_dw, float(np.max(np.abs(got["w"][l] - traj["w"][l]))))
     dx = np.max(np.abs(got["x"] - traj["x_out"])) / np.max(np.abs(traj["x_out"]))
-    print(f"stack48-T1: worst end-to-end layer {worst:.3e}, final x {dx:.3e}", flush=True)
+    print(f"stack48-T1: worst end-to-end layer max|dy|/max|y| {worst:.3e}, max|dw| "
+          f"{worst_dw:.2e}, final x {dx:.3e}", flush=True)
     assert dx <= hz.Y_TOL
     # the byte budget: 48 x 10 distinct blobs were read for the token
     assert sum(len(set(i.ravel())) for i in got["ids"]) == 480
@@ -104,74 +111,109 @@ def test_stack48_t1():
                  traj["y"][l])
 
 
-@pytest.mark.timeout(1200)
+N_SAMPLED_LAYERS = 4
+N_SAMPLED_TOKENS = 64
+
+
+@pytest.mark.timeout(1800)
 def test_stack48_t32768_zipf_sampled():
+    """The 32,768-token Zipf stack (16 chunks of 2048 through 48 layers).
+
+    Sample: 4 seeded layers and 64 seeded tokens.  Candidate tokens are taken
+    in a seeded order; the oracle runs each candidate's whole trajectory, and a
+    candidate is kept if its router input clears the 1e-4 near-tie margin at
+    all 4 sampled layers, else it is excluded (and reported) and the next
+    candidate is taken, until 64 are kept.  Per sampled layer, the GPU layer
+    runs on the oracle's own layer input of the 64 tokens, placed inside a
+    full 2048-token chunk, and must meet the single-layer bar on those rows.
+    End to end, the GPU stack runs on its own residual stream; its drift from
+    the oracle trajectories is measured and bounded."""
     c = inputs.WORKLOADS["stack48-T32768-zipf"]
     seed, T, chunk = c["seed"], c["T"], c["chunk"]
     st = inputs.Streams(seed)
     x = inputs.draw_x(st.x, T)
     routers = [inputs.draw_router(st.router) for _ in range(48)]
     biases = [inputs.draw_zipf_bias(st.bias) for _ in range(48)]
-    cand = np.sort(np.random.default_rng(44).choice(T, 24, replace=False))
+    pick = np.random.default_rng(44)
+    layers = np.sort(pick.choice(48, N_SAMPLED_LAYERS, replace=False))
+    order = pick.permutation(T)
+    src = scr.BlobSource(seed, cache=30000)
+    print(f"case: stack48-T32768-zipf sampled layers {list(layers)}; oracle trajectories",
+          flush=True)
+    kept, excluded, trajs = [], [], []
+    pos = 0
+    while len(kept) < N_SAMPLED_TOKENS:
+        need = N_SAMPLED_TOKENS - len(kept)
+        cand = order[pos:pos + need + max(4, need // 8)]
+        pos += cand.size
+        tr = scr.stack_trajectory(x[cand], routers, src, biases)
+        gaps = np.min(np.stack([tr["gap"][l] for l in layers]), axis=0)
+        for i, tok in enumerate(cand):
+            if gaps[i] > scr.TIE_MARGIN and len(kept) < N_SAMPLED_TOKENS:
+                kept.append(int(tok))
+                trajs.append((tr, i))
+            elif gaps[i] <= scr.TIE_MARGIN:
+                excluded.append(int(tok))
+    print(f"stack48-T32768-zipf: {len(kept)} tokens kept, {len(excluded)} excluded for a near-tie "
+          f"at a sampled layer: {excluded}", flush=True)
+
+    def traj(key, l):
+        return np.stack([tr[key][l][i] for tr, i in trajs])
+
     store = inputs.layer_store(seed, 0, n_layers=48)
-    print("case: stack48-T32768-zipf GPU, 16 chunks x 48 layers", flush=True)
-    got = {k: [[] for _ in range(48)] for k in ("ids", "w", "y")}
-    gx = []
-    for ch in range(T // chunk):
-        lo, hi = ch * chunk, (ch + 1) * chunk
-        rows = cand[(cand >= lo) & (cand < hi)] - lo
-        r = _run_stack_gpu(x[lo:hi], routers, store, biases, rows=rows)
-        for k in ("ids", "w", "y"):
-            for l in range(48):
-                got[k][l].append(r[k][l])
-        gx.append(r["x"])
-    for k in ("ids", "w", "y"):
-        got[k] = [np.concatenate(v) for v in got[k]]
-    gx = np.concatenate(gx)
-    print("case: stack48-T32768-zipf oracle trajectories of 24 sampled tokens", flush=True)
-    src = scr.BlobSource(seed, cache=20000)
-    traj = scr.stack_trajectory(x[cand], routers, src, biases)
-    gaps = np.min(np.stack(traj["gap"]), axis=0)
-    keep = np.nonzero(gaps > STACK_MARGIN_PREFILL)[0]
-    print(f"stack48-T32768-zipf: {keep.size}/24 tokens clear the {STACK_MARGIN_PREFILL} margin at all 48 "
-          f"layers", flush=True)
-    assert keep.size >= 6
-    # per layer on the oracle's own inputs, inside a full 2048-token chunk (so
-    # the prefill kernels run as in the stack); the other rows are chunk 0's
-    # generator rows
     per = 512 * inputs.blob_bytes()
-    k = keep.size
-    for l in range(48):
+    # per sampled layer, on the oracle's own inputs inside a full chunk
+    for l in layers:
         xin = x[:chunk].copy()
-        xin[:k] = traj["x_in"][l][keep]
+        xin[:N_SAMPLED_TOKENS] = traj("x_in", l)
         ids, w, y, _ = hz.gpu_layer(xin, routers[l], store[l * per:(l + 1) * per],
                                     bias=biases[l], flags=3)
-        hz.check(f"stack48-T32768-zipf forced layer {l}", ids[:k], w[:k], y[:k], traj["ids"][l][keep],
-                 traj["w"][l][keep], traj["y"][l][keep])
-    # end to end on the GPU's own residual stream.  The fp32 stream drifts from
-    # the fp64 trajectory (this stack's residual grows to |x| ~ 1e2), so after
-    # some layers a token may legitimately take other experts; the strict bar
-    # is the per-layer check above.  Here: properties of the GPU's own results
-    # (weights of a row sum to 1, ids distinct and in range, the final x is x0
-    # plus the layers' y in fp32), the first layer equal to the oracle's, and
-    # the drift from the oracle trajectory reported (bounded grossly while a
-    # token is still on the oracle's experts).
-    xs = x[cand].astype(np.float32)
+        n = N_SAMPLED_TOKENS
+        hz.check(f"stack48-T32768-zipf sampled layer {l}", ids[:n], w[:n], y[:n],
+                 traj("ids", l), traj("w", l), traj("y", l))
+
+    # end to end on the GPU's own residual stream
+    print("case: stack48-T32768-zipf GPU, 16 chunks x 48 layers", flush=True)
+    kept_a = np.array(kept)
+    got = {k: [[None] * len(kept) for _ in range(48)] for k in ("ids", "w", "y")}
+    gx = [None] * len(kept)
+    for ch in range(T // chunk):
+        lo, hi = ch * chunk, (ch + 1) * chunk
+        sel = np.nonzero((kept_a >= lo) & (kept_a < hi))[0]
+        if sel.size == 0:
+            continue
+        r = _run_stack_gpu(x[lo:hi], routers, store, biases, rows=kept_a[sel] - lo)
+        for j, i in enumerate(sel):
+            for k in ("ids", "w", "y"):
+                for l in range(48):
+                    got[k][l][i] = r[k][l][j]
+            gx[i] = r["x"][j]
+    got = {k: [np.stack(v) for v in got[k]] for k in got}
+    gx = np.stack(gx)
+    xs = x[kept_a].astype(np.float32)
+    worst_dy, worst_dw, rows_off = 0.0, 0.0, 0
     for l in range(48):
         gi, gw, gy = got["ids"][l], got["w"][l], got["y"][l]
         assert np.all((gi >= 0) & (gi < 512)), l
         assert all(len(set(r)) == 10 for r in gi), l
         assert np.max(np.abs(gw.astype(np.float64).sum(axis=1) - 1.0)) <= hz.W_TOL, l
         assert np.all(np.isfinite(gy)), l
-        same = np.all(gi == traj["ids"][l], axis=1)
-        if l == 0:
-            hz.check("stack48-T32768-zipf e2e layer 0", gi[keep], gw[keep], gy[keep], traj["ids"][0][keep],
-                     traj["w"][0][keep], traj["y"][0][keep])
-        on = keep[same[keep]]
-        dy = (float(np.max(np.abs(gy[on] - traj["y"][l][on])) / np.max(np.abs(traj["y"][l][on])))
-              if on.size else 0.0)
+        oi, ow, oy = traj("ids", l), traj("w", l), traj("y", l)
+        if l == 0:   # the first layer sees identical inputs: the full bar
+            hz.check("stack48-T32768-zipf e2e layer 0", gi, gw, gy, oi, ow, oy)
+        same = np.all(gi == oi, axis=1)
+        rows_off = max(rows_off, int((~same).sum()))
+        on = np.nonzero(same)[0]
+        if on.size:
+            dy = float(np.max(np.abs(gy[on] - oy[on])) / np.max(np.abs(oy[on])))
+            dw = float(np.max(np.abs(gw[on] - ow[on])))
+            worst_dy, worst_dw = max(worst_dy, dy), max(worst_dw, dw)
         print(f"[stack48-T32768-zipf e2e layer {l}] rows on the oracle trajectory's experts "
-              f"{int(same.sum())}/{len(cand)}, drift max|dy|/max|y| on them {dy:.3e}", flush=True)
-        assert dy <= 0.1, (l, dy)
+              f"{int(same.sum())}/{len(kept)}, drift on them max|dy|/max|y| "
+              f"{dy if on.size else 0.0:.3e} max|dw| {dw if on.size else 0.0:.2e}", flush=True)
         xs = (xs + gy.astype(np.float32)).astype(np.float32)
+    print(f"stack48-T32768-zipf e2e: worst drift max|dy|/max|y| {worst_dy:.3e}, max|dw| "
+          f"{worst_dw:.2e}, most rows off the oracle's experts at one layer {rows_off}",
+          flush=True)
+    assert worst_dy <= ZIPF_E2E_DY and worst_dw <= ZIPF_E2E_DW, (worst_dy, worst_dw)
     assert np.array_equal(xs, gx)   # the residual stream is x0 plus the layers' y
