@@ -1,20 +1,28 @@
 """Benchmark of the routed-expert MoE layer on one MI355X.
 
-Default workload: one MoE layer, T = 4 verify-window tokens (1 committed +
+Headline workload: one MoE layer, T = 4 verify-window tokens (1 committed +
 3 drafts), 512 Q2_0 experts, top-10 -- the decode-window configuration the
 headline metric (routed-expert GB/s and tok/s per MoE layer) is quoted on.
-A step is one whole layer call: RMSNorm-free router GEMV, softmax/top-10,
-grouping, the experts (each distinct expert's 1,382,400-byte blob read once)
-and the combine.  The working set of one layer (~54 MB) would sit in the
-256 MB Infinity Cache on repeats, so the timed steps cycle over 48 copies of
-the layer's store (and router) at distinct HBM addresses; every step reads
-cold memory and computes the same result.
+A step is one whole layer call: router GEMV, softmax/top-10, grouping, the
+experts (each distinct expert's 1,382,400-byte blob read once) and the
+combine.  One layer's working set (~54 MB) would sit in the 256 MB memory-side
+cache on repeats, so consecutive steps use 48 copies of the layer's store
+(and router) at distinct HBM addresses in turn; every step reads cold memory
+and computes the same result.
 
-Other workloads (--workload): token (T = 1 layer), window-corr (a T = 4
-verify window of correlated tokens whose distinct experts average 3.05 times
-one token's), stack-decode (48-layer T = 1 stack on the full 34 GB store),
-prefill (T = 2048 layer), stack-prefill (one 2048-token chunk through 48
-Zipf-biased layers).
+The same run also measures the metric's other configurations, each in its
+own object under "workloads" (same --steps / --warmup): the T = 1 layer, the
+T = 2048 prefill layer, and the two 48-layer stacks (a step is one token
+through 48 layers, or one 2048-token chunk through 48 Zipf-biased layers).
+Inputs are the workloads' screened inputs (inputs.workload_inputs).
+
+Timing: --warmup steps, then exactly --steps steps, each as a HIP graph
+replayed on one stream (single layers: one graph of exactly that many steps;
+stacks: one graph per step, replayed step by step), bracketed by device
+synchronisation; ms_per_step = the steps' event-timed total / steps.  The
+dominant kernel of a workload is timed live with HIP events attached to its
+own dispatch (strata_moe_time_next_kernel) over eager calls of the same
+steps: its mean duration prices the roofline object.
 
 Prints one JSON line.  With --gpus > 1 it exits: the measurement is of one GPU.
 """
@@ -31,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
-FLOP_PER_SLOT = 3 * 2 * 2560 * 640
+GATEUP_FLOP_PER_SLOT = 2 * 2 * 2560 * 640
 
 WORKLOADS = {
     "window": dict(wl="layer-T4-window", T=4, layers=1, copies=48),
@@ -42,6 +50,8 @@ WORKLOADS = {
     "prefill": dict(wl="layer-T2048-prefill", T=2048, layers=1, copies=4),
     "stack-prefill": dict(wl="stack48-T32768-zipf", T=2048, layers=48, copies=1),
 }
+# measured beside the headline in a default run
+ALSO = ("token", "prefill", "stack-decode", "stack-prefill")
 
 
 # HBM traffic of the dominant kernel from committed rocprofv3 counter
@@ -79,11 +89,16 @@ def traffic_from_profile(kernel, workload):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", default="window", choices=sorted(WORKLOADS))
+    ap.add_argument("--only", action="store_true",
+                    help="measure the chosen workload alone (no 'workloads' objects)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time of the headline workload's cpu_baseline")
+    ap.add_argument("--cpu-seconds-also", type=float, default=6.0,
+                    help="oracle time of each other workload's cpu_baseline")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graphs")
     ap.add_argument("--copies", type=int, default=0,
                     help="store copies cycled by single-layer workloads (default: the workload's; "
@@ -93,35 +108,19 @@ def parse():
     return ap.parse_args()
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
-              "(the layer would shard by tokens: each GPU holds the whole store and runs its own "
-              "tokens, with no collective)", file=sys.stderr)
-        sys.exit(2)
+def measure(name, a, cpu_seconds):
+    """One workload: returns its result object."""
     import torch
-    if a.calibrate_copy_mb:
-        n = a.calibrate_copy_mb << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
-        return
     import inputs
     import quantized_routed_expert_router_amd as m
-    m.lib()
-    wl = WORKLOADS[a.workload]
+    wl = WORKLOADS[name]
     cfg = inputs.WORKLOADS[wl["wl"]]
     T, L, seed = wl["T"], wl["layers"], cfg["seed"]
     stack = L > 1
+    prefill = T > 16
     flags = (m.RMSNORM | m.RESIDUAL) if stack else 0
-    st = inputs.Streams(seed)
-    x = inputs.draw_window(st.x, T) if cfg.get("window") else inputs.draw_x(st.x, T)
-    routers = [inputs.draw_router(st.router) for _ in range(L)]
-    biases = [inputs.draw_zipf_bias(st.bias) for _ in range(L)] if cfg["zipf"] else None
+    x, routers, biases = inputs.workload_inputs(wl["wl"], T=T)
+    x = np.ascontiguousarray(x[:T])
     blob = inputs.blob_bytes()
     per_layer = 512 * blob
 
@@ -151,75 +150,89 @@ def main():
     def layer_call(l, i, ids_o, stream):
         """Layer l (store copy i for single layers); with the lookahead, layers
         0 .. L-2 also predict layer l+1's experts and warm its blobs."""
+        sto = store[i * per_layer:(i + 1) * per_layer]
         if lookahead and l + 1 < L:
             m.strata_moe_layer_lookahead(
-                xd, Rd[i], store[i * per_layer:(i + 1) * per_layer], ws, Rd[i + 1],
-                store[(i + 1) * per_layer:(i + 2) * per_layer],
+                xd, Rd[i], sto, ws, Rd[i + 1], store[(i + 1) * per_layer:(i + 2) * per_layer],
                 bias=None if bd is None else bd[l], bias_next=None if bd is None else bd[l + 1],
                 flags=flags, y=y, ids=ids_o, w=w, pred=pred_t[l], stream=stream)
         else:
-            m.strata_moe_layer(xd, Rd[i], store[i * per_layer:(i + 1) * per_layer], ws,
-                               bias=None if bd is None else bd[l], flags=flags, y=y, ids=ids_o,
-                               w=w, stream=stream)
+            m.strata_moe_layer(xd, Rd[i], sto, ws, bias=None if bd is None else bd[l],
+                               flags=flags, y=y, ids=ids_o, w=w, stream=stream)
 
-    def one_step(i, stream=None):
+    def one_step(i, stream=None, ids_o=None):
+        ids_o = ids if ids_o is None else ids_o
         if stack:
             for l in range(L):
-                layer_call(l, l, ids, stream)
+                layer_call(l, l, ids_o[l] if isinstance(ids_o, list) else ids_o, stream)
         else:
-            c = i % copies
-            m.strata_moe_layer(xd, Rd[c], store[c * per_layer:(c + 1) * per_layer], ws,
-                               bias=None, flags=flags, y=y, ids=ids, w=w, stream=stream)
+            layer_call(0, i % copies, ids_o, stream)
 
     # Routing facts of the workload (from the GPU's own ids).
     one_step(0)
     torch.cuda.synchronize()
-    ids_h = ids.cpu().numpy()
-    distinct = int(np.unique(ids_h).size)
+    distinct = int(np.unique(ids.cpu().numpy()).size)
     if stack:
         xd.copy_(x0)
 
-    # Timed region: graphs of `chunk` steps replayed, or eager calls.
+    # Timed region: exactly a.warmup, then exactly a.steps steps.  Single
+    # layers: one graph per count holding that many consecutive steps; stacks:
+    # one graph of one step (48 layers), replayed step by step.  A stack's
+    # residual stream keeps moving from step to step (its inputs are the
+    # previous step's outputs); the work per step is the same.
     stream = torch.cuda.Stream()
-    chunk = copies if not stack else 1
-    graph = None
-    if not a.eager:
-        graph = torch.cuda.CUDAGraph()
+
+    def capture(n, first):
+        g = torch.cuda.CUDAGraph()
         stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(stream):
-            with torch.cuda.graph(graph, stream=stream):
-                for i in range(chunk):
-                    one_step(i, stream=stream)
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    one_step(first + i, stream=stream)
         torch.cuda.current_stream().wait_stream(stream)
         torch.cuda.synchronize()
-    steps = max(chunk, (a.steps // chunk) * chunk)
-    warm = max(chunk, (a.warmup // chunk) * chunk) if a.warmup > 0 else 0
+        return g
 
-    def run(n):
+    # The timed steps continue the warmup's walk over the store copies, so
+    # none of them finds its copy still in the memory-side cache.
+    graphs = {}
+    if not a.eager:
+        if stack:
+            graphs["step"] = capture(1, 0)
+        else:
+            if a.warmup:
+                graphs["warmup"] = capture(a.warmup, 0)
+            graphs["steps"] = capture(a.steps, a.warmup)
+
+    def run(n, key, first):
+        if n == 0:
+            return
         with torch.cuda.stream(stream):
-            if graph is not None:
-                for _ in range(n // chunk):
-                    graph.replay()
-            else:
+            if a.eager:
                 for i in range(n):
-                    one_step(i, stream=stream)
+                    one_step(first + i, stream=stream)
+            elif stack:
+                for _ in range(n):
+                    graphs["step"].replay()
+            else:
+                graphs[key].replay()
 
-    run(warm)
+    run(a.warmup, "warmup", 0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
-    run(steps)
+    run(a.steps, "steps", a.warmup)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / steps
+    ms = e0.elapsed_time(e1) / a.steps
+    del graphs
 
     # The dominant kernel, timed live with HIP events that the library records
     # on its stream just around it (strata_moe_time_next_kernel): the fused
     # decode experts kernel, or the prefill gate/up GEMM.  Eager layer calls
     # on the same stores; a stack re-runs its 48 layers from x0.
-    prefill = T > 16
     n_pass = 2 if stack else max(2, (max(copies * 4, 48) + copies - 1) // copies)
     ids_t = [torch.empty((T, 10), dtype=torch.int32, device="cuda") for _ in range(L)]
     evs = []
@@ -228,38 +241,27 @@ def main():
             if stack:
                 xd.copy_(x0)
             for i in range(L if stack else copies):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                e1.record(stream)
-                m.strata_moe_time_next_kernel(e0, e1)
+                ev0 = torch.cuda.Event(enable_timing=True)
+                ev1 = torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+                ev1.record(stream)
+                m.strata_moe_time_next_kernel(ev0, ev1)
                 l = i if stack else 0                  # layer (store copy i otherwise)
                 layer_call(l, i, ids_t[l], stream)
                 if p > 0:
-                    evs.append((e0, e1, l))
+                    evs.append((ev0, ev1, l))
     torch.cuda.synchronize()
-    if stack:
-        xd.copy_(x0)
-        torch.cuda.synchronize()
     per_l = [int(np.unique(t.cpu().numpy()).size) for t in ids_t]
-    k_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in evs]))
+    k_ms = float(np.mean([ev0.elapsed_time(ev1) for ev0, ev1, _ in evs]))
     if prefill:
         units = [T * 10 for _ in evs]              # (token, expert) slots per launch
-        per_unit = 2 * 2 * 2560 * 640              # gate and up flops per slot
+        per_unit = GATEUP_FLOP_PER_SLOT            # gate and up flops per slot
     else:
         units = [per_l[l] for _, _, l in evs]      # distinct experts per launch
         per_unit = blob                            # weight bytes per distinct expert
     k_work = float(np.mean(units)) * per_unit
 
-    # Throughput of the whole step.
-    if stack:
-        step_bytes = None
-        tok_s = T / (ms / 1e3)
-        layer_ms = ms / L
-    else:
-        step_bytes = distinct * blob
-        tok_s = T / (ms / 1e3)
-        layer_ms = ms
+    tok_s = T / (ms / 1e3)
     if prefill:
         roof = {"bound": "mfma", "achieved": k_work / (k_ms / 1e3) / 1e12,
                 "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
@@ -269,7 +271,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = "pf_gateup" if prefill else "dec_experts"
     # HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or null
-    roof["traffic"] = traffic_from_profile(roof["kernel"], a.workload)
+    roof["traffic"] = traffic_from_profile(roof["kernel"], name)
     if roof["traffic"] is not None and not prefill:
         roof["traffic_per_algorithmic_byte"] = roof["traffic"] / k_work
     roof["traffic_unit"] = "bytes per launch"
@@ -279,27 +281,33 @@ def main():
                                else f"{float(np.mean(units)):.2f} distinct experts x {per_unit} B")
 
     if stack:
-        value, unit, metric = tok_s, "tok/s", "routed-expert tok/s, 48-layer stack"
+        value, unit = tok_s, "tok/s"
+        metric = "routed-expert tok/s, 48-layer stack"
+        step_bytes = sum(per_l) * blob if not prefill else None
     elif prefill:
-        value, unit, metric = tok_s, "tok/s", "routed-expert tok/s per MoE layer (prefill)"
+        value, unit = tok_s, "tok/s"
+        metric = "routed-expert tok/s per MoE layer (prefill)"
+        step_bytes = distinct * blob
     else:
+        step_bytes = distinct * blob
         value = step_bytes / (ms / 1e3) / 1e9
         unit, metric = "GB/s", "routed-expert GB/s per MoE layer (decode)"
 
     res = {
-        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
-        "warmup": warm, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16-mfma/f32-acc" if prefill else "i4dot-16bit/f32-acc",
-        "data": "synthetic (seeded generator; no trained weights)",
-        "config": {"workload": f"{a.workload}: {cfg['name']}, T={T}, "
-                               f"layers={L}, 512 Q2_0 experts, top-10",
-                   "global_batch": T, "seq_len": 1 if not prefill else T,
-                   "parallelism": "single GPU", "timing": "eager" if a.eager else "hipGraph replay",
+        "metric": metric, "value": value, "unit": unit, "ms_per_step": ms,
+        "steps": a.steps, "warmup": a.warmup,
+        "dtype": "f16-mfma/f32-acc" if prefill else "i4dot-16bit/f32-acc",
+        "config": {"workload": f"{name}: {cfg['name']}, T={T}, layers={L}, "
+                               f"512 Q2_0 experts, top-10",
+                   "global_batch": T, "seq_len": T if prefill else 1,
+                   "timing": "eager" if a.eager else "hipGraph replay",
                    "store_copies": copies},
-        "tok_per_s": tok_s, "layer_ms": layer_ms, "distinct_experts": distinct,
+        "tok_per_s": tok_s, "layer_ms": ms / L, "distinct_experts": distinct,
         "expert_bytes_per_step": step_bytes, "wall_s": wall,
         "roofline": roof,
     }
+    if stack and not prefill:
+        res["expert_gbs"] = step_bytes / (ms / 1e3) / 1e9
     if lookahead:
         # How often a routed expert of layer l+1 was among those predicted
         # (and warmed) while layer l ran, over the eager pass's tokens.
@@ -313,18 +321,22 @@ def main():
                             "prefetched_bytes_per_step": pbytes,
                             "note": "prefetched bytes are read in addition to the routed "
                                     "experts' own; tok/s counts the whole 48-layer step"}
+    del store, Rd, ws, xd, x0, y, ids, w, pred_t, ids_t
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(a, x, routers, biases, seed, stack, T, blob)
-    print(json.dumps(res))
+        res["cpu_baseline"] = cpu_baseline(cpu_seconds, x, routers, biases, seed, stack, prefill,
+                                           T, blob)
+    return res
 
 
-def cpu_baseline(a, x, routers, biases, seed, stack, T, blob):
+def cpu_baseline(seconds, x, routers, biases, seed, stack, prefill, T, blob):
     """The oracle timed on the host cores on a bounded sample of the same
     workload: whole layers (route, experts, combine) for the workload's first
-    layer, repeated until --cpu-seconds have passed (at most 64 tokens)."""
+    layer, repeated until `seconds` have passed (at most 64 tokens)."""
     import oracle
     import oracle.screen as scr
-    n = min(T, 64 if T > 16 else T)
+    n = min(T, 64)
     xs = x[:n]
     R = routers[0]
     b = None if biases is None else biases[0]
@@ -336,17 +348,61 @@ def cpu_baseline(a, x, routers, biases, seed, stack, T, blob):
         ids, w, y = scr.oracle_layer(xs, R, src, 0, bias=b, rmsnorm=stack)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= a.cpu_seconds or reps >= 1000:
+        if el >= seconds or reps >= 1000:
             break
     distinct = int(np.unique(ids).size)
     per_rep = el / reps
-    if T <= 16 and not stack:
+    if not prefill and not stack:
         value, unit = distinct * blob / per_rep / 1e9, "GB/s"
     else:
-        value, unit = n / per_rep, "tok/s (one layer)"
+        value, unit = n / per_rep, "token-layers/s"
     return {"value": value, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{reps} x one layer on {n} token(s) of the workload ({distinct} distinct "
                       f"experts), {el:.1f} s", "seconds_per_layer": per_rep}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the layer would shard by tokens: each GPU holds the whole store and runs its own "
+              "tokens, with no collective)", file=sys.stderr)
+        sys.exit(2)
+    if a.steps < 1 or a.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if a.calibrate_copy_mb:
+        n = a.calibrate_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
+        return
+    import quantized_routed_expert_router_amd as m
+    m.lib()
+    head = measure(a.workload, a, a.cpu_seconds)
+    res = {
+        "metric": head["metric"], "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head["dtype"], "data": "synthetic (seeded generator; no trained weights)",
+        "config": dict(head["config"], parallelism="single GPU"),
+    }
+    for k in ("tok_per_s", "layer_ms", "distinct_experts", "expert_bytes_per_step", "wall_s",
+              "roofline", "lookahead", "cpu_baseline"):
+        if k in head:
+            res[k] = head[k]
+    if not a.only:
+        res["workloads"] = {}
+        for name in ALSO:
+            if name == a.workload:
+                continue
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            res["workloads"][name] = measure(name, a, a.cpu_seconds_also)
+    print(json.dumps(res))
 
 
 if __name__ == "__main__":

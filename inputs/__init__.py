@@ -204,3 +204,51 @@ def layer_store(seed, layer, device="cuda", n_layers=1, e=E):
     store = torch.empty(n_layers * e * blob_bytes(), dtype=torch.uint8, device=device)
     fill_blobs_device(store, seed, layer * e, n_layers * e)
     return store
+
+
+# ---------------------------------------------------------------- screened workloads
+def apply_row_redraws(st, x, rows, h=H):
+    """Replace rows of x, in the listed order, by fresh draws from st.x_redraw
+    (the replay of a near-tie screen's decisions)."""
+    for t in rows:
+        x[t] = draw_x(st.x_redraw, 1, h=h)[0]
+    return x
+
+
+def _screens():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "screens.json")
+    with open(path) as f:
+        return json.load(f)
+
+
+def workload_inputs(name, T=None):
+    """x, the routers and the biases of a workload configuration, with the
+    stored near-tie screen decisions replayed (screens.json, written by
+    oracle/write_screens.py): the inputs the parity tests check.  T overrides
+    the token count of the unscreened Zipf stack only (one chunk of it)."""
+    c = WORKLOADS[name]
+    st = Streams(c["seed"])
+    scr = _screens().get(name, {})
+    routers, biases = [], None
+    if c.get("window"):
+        x = draw_window(st.x, c["T"])
+        routers = [draw_router(st.router)]
+        for _ in range(scr.get("window_redraws", 0)):
+            x = draw_window(st.x_redraw, c["T"])
+    elif name == "stack48-T1":
+        x = draw_x(st.x, 1)
+        for n in scr["router_redraws"]:
+            R = draw_router(st.router)
+            for _ in range(n):
+                R = draw_router(st.router_redraw)
+            routers.append(R)
+    elif name == "stack48-T32768-zipf":
+        x = draw_x(st.x, c["T"] if T is None else T)
+        routers = [draw_router(st.router) for _ in range(c["layers"])]
+        biases = [draw_zipf_bias(st.bias) for _ in range(c["layers"])]
+    else:
+        routers = [draw_router(st.router)]
+        x = apply_row_redraws(st, draw_x(st.x, c["T"]), scr["x_redraw_rows"])
+    return x, routers, biases

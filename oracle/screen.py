@@ -48,18 +48,26 @@ def screened_x(st, T, R_bits, bias=None, rmsnorm=False, margin=TIE_MARGIN, h=inp
     from st.x_redraw, in row order.  `extra` lists further (router, bias)
     pairs the rows must also clear (a second router applied to the same
     input).  Returns (x, number of redrawn rows)."""
+    x, rows = screened_x_rows(st, T, R_bits, bias, rmsnorm, margin, h, extra)
+    return x, len(rows)
+
+
+def screened_x_rows(st, T, R_bits, bias=None, rmsnorm=False, margin=TIE_MARGIN, h=inputs.H,
+                    extra=()):
+    """screened_x, returning the redrawn row indices in the order of their
+    redraws (inputs.apply_row_redraws replays them)."""
     x = inputs.draw_x(st.x, T, h=h)
-    redrawn = 0
+    rows = []
     pairs = [(R_bits, bias)] + list(extra)
     for _ in range(1000):
         xh = rms_np(x) if rmsnorm else x.astype(np.float64)
         gap = np.min(np.stack([top11_gap(logits_np(xh, R, b)) for R, b in pairs]), axis=0)
         bad = np.nonzero(gap <= margin)[0]
         if bad.size == 0:
-            return x, redrawn
+            return x, rows
         for t in bad:
             x[t] = inputs.draw_x(st.x_redraw, 1, h=h)[0]
-            redrawn += 1
+            rows.append(int(t))
     raise RuntimeError("near-tie screen did not converge")
 
 
@@ -128,17 +136,22 @@ def stack_trajectory(x0, routers, src, biases=None, margin=TIE_MARGIN, verbose=T
     return out
 
 
-def screened_stack_routers(st, x0, src, n_layers, margin):
+def screened_stack_routers(st, x0, src, n_layers, margin, per_layer=None):
     """Routers for a T=1 stack drawn layer by layer on the oracle trajectory;
-    router l is redrawn (st.router_redraw) until the row clears the margin."""
+    router l is redrawn (st.router_redraw) until the row clears the margin.
+    per_layer, if a list, receives the number of redraws of each layer."""
     x = np.asarray(x0, dtype=np.float64)
     routers, redraws = [], 0
     for l in range(n_layers):
         R = inputs.draw_router(st.router)
         xf = x.astype(np.float32)
+        n = 0
         while top11_gap(logits_np(rms_np(xf), R))[0] <= margin:
             R = inputs.draw_router(st.router_redraw)
             redraws += 1
+            n += 1
+        if per_layer is not None:
+            per_layer.append(n)
         routers.append(R)
         _, _, y = oracle_layer(xf, R, src, l, rmsnorm=True)
         x = x + y

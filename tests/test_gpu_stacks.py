@@ -28,13 +28,18 @@ import oracle.screen as scr
 pytestmark = pytest.mark.gpu
 
 # The GPU's fp32 residual stream drifts from the fp64 one by rounding over 48
-# layers, so stacked runs keep a wider router margin than single layers.
-STACK_MARGIN_T1 = 1e-3
-# End-to-end drift bounds (about twice the drift measured on MI355X; the
-# per-layer checks on identical inputs hold the full bar).
-W_TOL_STACK = 2e-2
-ZIPF_E2E_DY = 0.1
-ZIPF_E2E_DW = 2e-2
+# layers, so the T=1 stack keeps a wider router margin than single layers
+# (the margin is also the one of the stored screen decisions that bench.py
+# replays).
+from oracle.write_screens import STACK_MARGIN_T1  # noqa: E402
+
+# End-to-end drift bounds, about twice the drift measured on MI355X (T=1
+# stack: max|dw| 5.4e-6 over 48 layers; Zipf stack: max|dy|/max|y| 2.6e-2 and
+# max|dw| 2.5e-2 on the rows still on the oracle's experts).  The per-layer
+# checks on identical inputs hold the full single-layer bar.
+W_TOL_STACK = 1.1e-5
+ZIPF_E2E_DY = 5e-2
+ZIPF_E2E_DW = 5e-2
 
 
 @pytest.fixture(scope="module", autouse=True)
