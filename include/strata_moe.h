@@ -64,6 +64,9 @@ extern "C" {
 #define STRATA_E_HIP (-4)       /* the HIP runtime reported a launch error */
 #define STRATA_E_ALIGN (-5)     /* a pointer breaks the alignment rule above */
 
+/* Bits of a workspace's status word (see strata_moe_read_status). */
+#define STRATA_STATUS_WAIT_TIMEOUT 1 /* a decode experts wait gave up: outputs of that call are NaN */
+
 /* Flags. */
 #define STRATA_RMSNORM 1  /* normalise x first: x / sqrt(mean(x^2) + 1e-6), unit gain */
 #define STRATA_RESIDUAL 2 /* combine adds into its output (x += y) instead of storing */
@@ -107,7 +110,11 @@ STRATA_API int strata_moe_route(const float *x, int T, const uint16_t *router, c
 STRATA_API int strata_moe_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
                      int32_t *active, void *ws, size_t ws_bytes, void *stream);
 
-/* Expert FFNs (SwiGLU): for every grouped slot s = t*K+k of expert e,
+/* Expert FFNs ([SRC] "The byte budget, in code": each expert is a gate, an up
+ * and a down matrix of 2,560 x 640 Q2_0 weights; [MY] 提示词处理: a chunk's
+ * tokens are grouped per expert and each expert's weights are dequantised and
+ * multiplied once for all of its tokens).  The expert function is SwiGLU:
+ * for every grouped slot s = t*K+k of expert e,
  *   out[s] = W_d (silu(W_g xhat_t) * (W_u xhat_t)),  silu(z) = z / (1 + e^-z),
  * reading each active expert's blob once for all of its tokens.
  *   x       [T][H] fp32; xhat as in strata_moe_route (STRATA_RMSNORM).
@@ -130,7 +137,9 @@ STRATA_API int strata_moe_experts(const float *x, int T, const uint8_t *blobs, c
 STRATA_API int strata_moe_combine(const float *out, const float *w, int T, int flags, float *y,
                        void *stream);
 
-/* The whole layer in one call: route -> group -> experts -> combine.
+/* The whole layer in one call ([ZW], the passage that follows one token
+ * through a layer: logits, top-10, the experts, then one weighted Combine):
+ * route -> group -> experts -> combine.
  *   x      [T][H] fp32 in; with STRATA_RESIDUAL also out (x += layer output).
  *   y      [T][H] fp32 out (layer output without residual), or NULL; must not
  *          be NULL unless STRATA_RESIDUAL is set.
@@ -172,6 +181,34 @@ STRATA_API int strata_moe_layer_lookahead(float *x, int T, const uint16_t *route
  * disarm.  Returns STRATA_E_ARG if only one is NULL.  Not for use under graph
  * capture. */
 STRATA_API int strata_moe_time_next_kernel(void *start, void *stop);
+
+/* Status word.  The first 4 bytes of every workspace hold a status word that
+ * the kernels OR STRATA_STATUS_* bits into and never clear.  The decode-sized
+ * experts kernel (T <= 16) has one wait: a unit's down part waits for the
+ * gate/up results of its expert's other units, which the dispatch order
+ * guarantees to come (workgroups start in index order on each XCD).  The wait
+ * is bounded; if it gives up, the outputs that depended on it are set to NaN
+ * and STRATA_STATUS_WAIT_TIMEOUT is set, so such a failure never passes as a
+ * result.  A fresh workspace must have its status word zeroed once (the
+ * Python binding's workspace() does; or call strata_moe_clear_status).
+ *
+ * strata_moe_read_status: synchronises `stream`, then copies the status word
+ * of `ws` (at least 256 bytes, 256-byte aligned) to *bits (host memory).  A
+ * diagnostic: not for use under graph capture.  Returns STRATA_OK,
+ * STRATA_E_ARG, STRATA_E_WORKSPACE, STRATA_E_ALIGN or STRATA_E_HIP. */
+STRATA_API int strata_moe_read_status(const void *ws, size_t ws_bytes, int32_t *bits,
+                                      void *stream);
+
+/* Enqueues on `stream` a kernel that sets the status word of `ws` to 0
+ * (capturable: no memset). */
+STRATA_API int strata_moe_clear_status(void *ws, size_t ws_bytes, void *stream);
+
+/* Bound of the decode experts kernel's wait, in polls of the expert's counter
+ * (each about 0.2-1 us); 0 restores the default of 2^18, negative values
+ * return STRATA_E_ARG.  Applies to launches made after the call, from any
+ * thread.  Meant for tests of the failure path (a bound of 1 makes most waits
+ * give up at once, so every kernel still ends). */
+STRATA_API int strata_moe_set_wait_limit(int polls);
 
 /* Human-readable text of a status code (static storage). */
 STRATA_API const char *strata_moe_status_string(int status);

@@ -43,20 +43,23 @@ def top11_gap(lg):
 
 
 def screened_x(st, T, R_bits, bias=None, rmsnorm=False, margin=TIE_MARGIN, h=inputs.H,
-               extra=()):
-    """x [T][H] from st.x; rows whose top-11 gap is within `margin` are redrawn
-    from st.x_redraw, in row order.  `extra` lists further (router, bias)
-    pairs the rows must also clear (a second router applied to the same
-    input).  Returns (x, number of redrawn rows)."""
-    x, rows = screened_x_rows(st, T, R_bits, bias, rmsnorm, margin, h, extra)
+               extra=(), x_scale=1.0):
+    """x [T][H] from st.x (times x_scale, in fp32); rows whose top-11 gap is
+    within `margin` are redrawn from st.x_redraw, in row order.  `extra` lists
+    further (router, bias) pairs the rows must also clear (a second router
+    applied to the same input).  Returns (x, number of redrawn rows)."""
+    x, rows = screened_x_rows(st, T, R_bits, bias, rmsnorm, margin, h, extra, x_scale)
     return x, len(rows)
 
 
 def screened_x_rows(st, T, R_bits, bias=None, rmsnorm=False, margin=TIE_MARGIN, h=inputs.H,
-                    extra=()):
+                    extra=(), x_scale=1.0):
     """screened_x, returning the redrawn row indices in the order of their
     redraws (inputs.apply_row_redraws replays them)."""
-    x = inputs.draw_x(st.x, T, h=h)
+    def draw(n, rng):
+        v = inputs.draw_x(rng, n, h=h)
+        return v if x_scale == 1.0 else (v * np.float32(x_scale)).astype(np.float32)
+    x = draw(T, st.x)
     rows = []
     pairs = [(R_bits, bias)] + list(extra)
     for _ in range(1000):
@@ -66,7 +69,7 @@ def screened_x_rows(st, T, R_bits, bias=None, rmsnorm=False, margin=TIE_MARGIN, 
         if bad.size == 0:
             return x, rows
         for t in bad:
-            x[t] = inputs.draw_x(st.x_redraw, 1, h=h)[0]
+            x[t] = draw(1, st.x_redraw)[0]
             rows.append(int(t))
     raise RuntimeError("near-tie screen did not converge")
 

@@ -23,7 +23,9 @@ OK, E_ARG, E_SHAPE, E_WORKSPACE, E_HIP, E_ALIGN = 0, -1, -2, -3, -4, -5
 EXPORTS = ("strata_moe_blob_bytes", "strata_moe_workspace_bytes", "strata_moe_route",
            "strata_moe_group", "strata_moe_experts", "strata_moe_combine", "strata_moe_layer",
            "strata_moe_layer_lookahead", "strata_moe_time_next_kernel",
+           "strata_moe_read_status", "strata_moe_clear_status", "strata_moe_set_wait_limit",
            "strata_moe_status_string")
+STATUS_WAIT_TIMEOUT = 1
 
 _lib = None
 
@@ -62,6 +64,12 @@ def lib():
                                                  vp, vp, sz, vp]
         L.strata_moe_time_next_kernel.restype = i32
         L.strata_moe_time_next_kernel.argtypes = [vp, vp]
+        L.strata_moe_read_status.restype = i32
+        L.strata_moe_read_status.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_int32), vp]
+        L.strata_moe_clear_status.restype = i32
+        L.strata_moe_clear_status.argtypes = [vp, sz, vp]
+        L.strata_moe_set_wait_limit.restype = i32
+        L.strata_moe_set_wait_limit.argtypes = [i32]
         L.strata_moe_status_string.restype = ctypes.c_char_p
         L.strata_moe_status_string.argtypes = [i32]
         _lib = L
@@ -170,12 +178,31 @@ def strata_moe_workspace_bytes(T):
 
 
 def workspace(T, device="cuda"):
-    """A workspace tensor sized for T tokens (torch allocations are 256-aligned)."""
+    """A workspace tensor sized for T tokens (torch allocations are 256-aligned),
+    zero-filled so that its status word starts clear."""
     import torch
     n = strata_moe_workspace_bytes(T)
     if n == 0:
         raise StrataError("strata_moe_workspace_bytes", E_SHAPE)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def strata_moe_read_status(ws, stream=None):
+    """Synchronise the stream and return the workspace's status word (bits
+    STATUS_*; 0 when every call since the last clear completed normally)."""
+    v = ctypes.c_int32(0)
+    rc = lib().strata_moe_read_status(_p(ws), _nbytes(ws), ctypes.byref(v), _s(stream))
+    _check("strata_moe_read_status", rc)
+    return int(v.value)
+
+
+def strata_moe_clear_status(ws, stream=None):
+    _check("strata_moe_clear_status", lib().strata_moe_clear_status(_p(ws), _nbytes(ws), _s(stream)))
+
+
+def strata_moe_set_wait_limit(polls):
+    """Bound of the decode experts kernel's wait (0 restores the default)."""
+    _check("strata_moe_set_wait_limit", lib().strata_moe_set_wait_limit(int(polls)))
 
 
 def strata_moe_route(x, router, ids, w, ws, bias=None, flags=0, stream=None):

@@ -4,10 +4,11 @@
 #include "common.hpp"
 #include "quant.hpp"
 #include "workspace.hpp"
+#include <atomic>
 
 namespace strata {
 hipError_t launch_prep(const float *x, int T, int rmsnorm, uint16_t *xsplit, __half *xperm,
-                       hipStream_t st);
+                       int32_t *xexp, hipStream_t st);
 hipError_t launch_logits(const uint16_t *xsplit, int T, const uint16_t *R, const float *bias,
                          float *logits, hipStream_t st);
 hipError_t launch_topk(const float *logits, int T, int32_t *ids, float *w, hipStream_t st);
@@ -27,17 +28,29 @@ hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const i
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
                                  XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
                                  const float *w, float *y, float *res, const int32_t *pred,
-                                 const uint8_t *blobs_next, hipEvent_t ev0, hipEvent_t ev1,
-                                 hipStream_t st);
+                                 const uint8_t *blobs_next, int32_t *status, int wait_limit,
+                                 hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
 hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
-                                  const __half *xperm, __half *hperm, float *out, int T,
-                                  hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
+                                  const __half *xperm, const int32_t *xexp, __half *hperm,
+                                  float *out, int T, hipEvent_t ev0, hipEvent_t ev1,
+                                  hipStream_t st);
 hipError_t launch_combine(const float *out, const float *w, int T, float *y, float *res,
                           int accumulate_y, hipStream_t st);
 
+// Sets a workspace's status word to zero (graph-capturable, unlike a memset).
+__global__ void status_clear_kernel(int32_t *status)
+{
+    if (threadIdx.x == 0)
+        *status = 0;
+}
+
 namespace {
+
+// Bound on the decode experts kernel's wait, in polls (about 0.3 s by default).
+constexpr int WAIT_LIMIT_DEFAULT = 1 << 18;
+std::atomic<int> g_wait_limit{WAIT_LIMIT_DEFAULT};
 
 // The measurement hook's events (per host thread, used by one call).
 thread_local hipEvent_t t_ev0 = nullptr, t_ev1 = nullptr;
@@ -77,6 +90,7 @@ struct Carve {
     int32_t *cdone, *esync;
     float *lraw2;
     int32_t *pred, *gcount;
+    int32_t *status, *xexp;
 };
 
 Carve carve(void *ws, int T)
@@ -100,6 +114,8 @@ Carve carve(void *ws, int T)
     c.lraw2 = at<float>(ws, L.lraw2);
     c.pred = at<int32_t>(ws, L.pred);
     c.gcount = at<int32_t>(ws, L.gcount);
+    c.status = at<int32_t>(ws, L.status);
+    c.xexp = at<int32_t>(ws, L.xexp);
     c.ids = at<int32_t>(ws, L.ids);
     c.w = at<float>(ws, L.w);
     c.mlist = at<int32_t>(ws, L.mlist);
@@ -126,12 +142,14 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
     take_events(e0, e1);
     if (is_decode(T)) {
         STRATA_TRY(launch_decode_experts(blobs, c.erec, slots, c.xq, c.hq, out, T, c.esync, nullptr,
-                                         nullptr, nullptr, nullptr, nullptr, nullptr, e0, e1, st));
+                                         nullptr, nullptr, nullptr, nullptr, nullptr, c.status,
+                                         g_wait_limit.load(), e0, e1, st));
     } else {
         if (!planned)
             STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
         STRATA_TRY(launch_prefill_experts(blobs, offsets, slots, active, c.mlist, c.nitems,
-                                          c.L.max_items, c.xperm, c.hperm, out, T, e0, e1, st));
+                                          c.L.max_items, c.xperm, c.xexp, c.hperm, out, T, e0,
+                                          e1, st));
     }
     return STRATA_OK;
 }
@@ -145,7 +163,7 @@ int run_prep(const Carve &c, const float *x, int T, int rms, const int32_t *offs
     if (is_decode(T))
         STRATA_TRY(launch_prep_decode(x, T, rms, c.xq, offsets, slots, active, c.erec, c.esync, st));
     else
-        STRATA_TRY(launch_prep(x, T, rms, nullptr, c.xperm, st));
+        STRATA_TRY(launch_prep(x, T, rms, nullptr, c.xperm, c.xexp, st));
     return STRATA_OK;
 }
 
@@ -183,7 +201,7 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
                                        c.slots, c.erec, c.cdone, c.esync, router2, bias2, c.lraw2,
                                        pred_o, st));
     } else {
-        STRATA_TRY(launch_prep(x, T, rms, c.xsplit, c.xperm, st));
+        STRATA_TRY(launch_prep(x, T, rms, c.xsplit, c.xperm, c.xexp, st));
         STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
         STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
         STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, c.gcount, c.L.max_items,
@@ -196,7 +214,7 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
         STRATA_TRY(launch_decode_experts(blobs, c.erec, c.slots, c.xq, c.hq, c.out, T, c.esync,
                                          c.cdone, w_o, y, res ? x : nullptr,
                                          router2 ? pred_o : nullptr, router2 ? blobs2 : nullptr,
-                                         e0, e1, st));
+                                         c.status, g_wait_limit.load(), e0, e1, st));
         return STRATA_OK;
     }
     if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st, true)))
@@ -241,7 +259,7 @@ int strata_moe_route(const float *x, int T, const uint16_t *router, const float 
                                        nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                        nullptr, st));
     } else {
-        STRATA_TRY(launch_prep(x, T, rms, c.xsplit, nullptr, st));
+        STRATA_TRY(launch_prep(x, T, rms, c.xsplit, nullptr, nullptr, st));
         STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
         STRATA_TRY(launch_topk(c.logits, T, ids, w, st));
     }
@@ -333,6 +351,44 @@ int strata_moe_time_next_kernel(void *start, void *stop)
         return STRATA_E_ARG;
     t_ev0 = (hipEvent_t)start;
     t_ev1 = (hipEvent_t)stop;
+    return STRATA_OK;
+}
+
+int strata_moe_read_status(const void *ws, size_t ws_bytes, int32_t *bits, void *stream)
+{
+    if (!ws || !bits)
+        return STRATA_E_ARG;
+    if (ws_bytes < WS_STATUS_BYTES)
+        return STRATA_E_WORKSPACE;
+    if (!aligned(ws, 256))
+        return STRATA_E_ALIGN;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+        return STRATA_E_HIP;
+    int32_t v = 0;
+    if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
+        return STRATA_E_HIP;
+    *bits = v;
+    return STRATA_OK;
+}
+
+int strata_moe_clear_status(void *ws, size_t ws_bytes, void *stream)
+{
+    if (!ws)
+        return STRATA_E_ARG;
+    if (ws_bytes < WS_STATUS_BYTES)
+        return STRATA_E_WORKSPACE;
+    if (!aligned(ws, 256))
+        return STRATA_E_ALIGN;
+    hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                       static_cast<int32_t *>(ws));
+    return hipGetLastError() == hipSuccess ? STRATA_OK : STRATA_E_HIP;
+}
+
+int strata_moe_set_wait_limit(int polls)
+{
+    if (polls < 0)
+        return STRATA_E_ARG;
+    g_wait_limit.store(polls == 0 ? WAIT_LIMIT_DEFAULT : polls);
     return STRATA_OK;
 }
 

@@ -117,7 +117,8 @@ __device__ inline float2 block_dot2(const uint32_t *p, uint32_t sel, uint32_t sh
 
 // Per-call counters of the fused kernel (zeroed by the router / prep kernel):
 // sync[1 + SYNC_STRIDE * a] counts the finished gate/up items of active expert a.
-constexpr int EX_WAIT_LIMIT = 1 << 18;   // bounded wait (~0.2 s), never reached in a correct call
+// Status bits the kernel ORs into the caller's status word.
+constexpr int ST_WAIT_GAVE_UP = STRATA_STATUS_WAIT_TIMEOUT;
 
 // h values are stored and read at agent scope (coherent across the XCDs'
 // L2 caches): the down part of the same launch reads them.
@@ -481,7 +482,8 @@ __device__ inline void finish_slot(int slot, float acc, int ch, float *__restric
 __device__ void down_group(int grp, const uint8_t *__restrict__ blobs,
                            const int4 *__restrict__ erec, const int32_t *__restrict__ slots,
                            const HQ &hq, float *__restrict__ out, int T, const Combine &cb,
-                           uint32_t *wl, const int32_t *gdone)
+                           uint32_t *wl, const int32_t *gdone, int32_t *status, int wait_limit,
+                           int *ok_flag)
 {
     const int nslot = T * K;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -511,15 +513,22 @@ __device__ void down_group(int grp, const uint8_t *__restrict__ blobs,
     // wait (bounded) until the expert's DG_SEGS gate/up items have stored h;
     // h itself is read with agent-scope loads, so the poll needs no cache
     // invalidation, only to stay ahead of those loads in program order.  One
-    // lane of the workgroup polls, sparsely.
+    // lane of the workgroup polls, sparsely.  If the wait gives up, the
+    // group's outputs are NaN and the status word records it.
     if (threadIdx.x == 0) {
         int n = 0;
         while (__hip_atomic_load(gdone + SYNC_STRIDE * a, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT) < DG_SEGS &&
-               ++n < EX_WAIT_LIMIT)
+               ++n < wait_limit)
             __builtin_amdgcn_s_sleep(32);
+        const int ok = n < wait_limit;
+        *ok_flag = ok;
+        if (!ok)
+            __hip_atomic_fetch_or(status, ST_WAIT_GAVE_UP, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
+    const bool gave_up = *ok_flag == 0;
     HOps ho = load_hops(hq, slot >= 0 && slot < nslot ? slot : 0, c0, l);
     // the wave reads back what its own lanes wrote: LDS keeps a wave's order
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -546,6 +555,10 @@ __device__ void down_group(int grp, const uint8_t *__restrict__ blobs,
             acc = down_row(row, c0, ho);
         }
         acc += __shfl_xor(acc, 32, 64);
+        if (gave_up) {
+            acc = __builtin_nanf("");
+            acc2 = __builtin_nanf("");
+        }
         finish_slot(slot, acc, ch, out, T, cb);
         if (two)
             finish_slot(slot2, acc2, ch, out, T, cb);
@@ -558,7 +571,8 @@ static_assert(DD_ITEMS_PER_E % DD_WAVES == 0, "a down group stays within one exp
 constexpr int EX_DN_PER_E = DD_ITEMS_PER_E / DD_WAVES;   // 20 down groups per expert
 constexpr size_t EX_LDS_GU = (size_t)DG_ROWS * DG_RS * 4 + (size_t)2 * DG_WAVES * DG_ROWS * 4;
 constexpr size_t EX_LDS_DN = (size_t)DD_WAVES * DD_ROWS * DD_RS * 4;
-constexpr size_t EX_LDS = EX_LDS_GU > EX_LDS_DN ? EX_LDS_GU : EX_LDS_DN;
+constexpr size_t EX_LDS_MAX = EX_LDS_GU > EX_LDS_DN ? EX_LDS_GU : EX_LDS_DN;
+constexpr size_t EX_LDS = EX_LDS_MAX + 16;   // + the down group's wait flag
 
 // Lookahead: workgroups past the down groups read the blobs of the experts
 // predicted for the next layer, one request per 128-byte line, so that the
@@ -599,12 +613,15 @@ __device__ void touch_next(int b, int nslot, const int32_t *__restrict__ pred,
 // dispatches its workgroups in index order, so every gate/up workgroup of an
 // XCD holds a slot before any down workgroup of that XCD can take one: gate/up
 // workgroups never wait behind the down ones, and the waits end.  The wait is
-// bounded all the same.
+// bounded all the same; a wait that gives up leaves NaN outputs and sets
+// ST_WAIT_GAVE_UP in the caller's status word.
 __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restrict__ blobs,
                                                           const int4 *__restrict__ erec,
                                                           const int32_t *__restrict__ slots, XQ xq,
                                                           HQ hq, float *__restrict__ out, int T,
                                                           Combine cb, int32_t *__restrict__ gdone,
+                                                          int32_t *__restrict__ status,
+                                                          int wait_limit,
                                                           const int32_t *__restrict__ pred,
                                                           const uint8_t *__restrict__ blobs_next)
 {
@@ -625,7 +642,8 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
             return;
         uint32_t *wl = reinterpret_cast<uint32_t *>(lds) +
                        (size_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DD_ROWS * DD_RS;
-        down_group(g, blobs, erec, slots, hq, out, T, cb, wl, gdone);
+        down_group(g, blobs, erec, slots, hq, out, T, cb, wl, gdone, status, wait_limit,
+                   reinterpret_cast<int *>(lds + EX_LDS_MAX));
     } else {
         touch_next(b - amax * (DG_SEGS + EX_DN_PER_E), T * K, pred, blobs_next);
     }
@@ -634,8 +652,8 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
                                  XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
                                  const float *w, float *y, float *res, const int32_t *pred,
-                                 const uint8_t *blobs_next, hipEvent_t ev0, hipEvent_t ev1,
-                                 hipStream_t st)
+                                 const uint8_t *blobs_next, int32_t *status, int wait_limit,
+                                 hipEvent_t ev0, hipEvent_t ev1, hipStream_t st)
 {
     Combine cb{cdone, w, y, res};
     const int amax = T * K < E ? T * K : E;
@@ -645,12 +663,13 @@ hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const i
     const dim3 grid(amax * (DG_SEGS + EX_DN_PER_E) + (pred ? T * K * XT_PER_SLOT : 0));
     const dim3 block(EX_THREADS);
     if (ev0) {   // timed launch: the events carry the dispatch's own start and end
-        void *args[] = {&blobs, &erec, &slots, &xq, &hq, &out, &T, &cb, &gdone, &pred, &blobs_next};
+        void *args[] = {&blobs, &erec,  &slots,  &xq,         &hq,   &out,       &T,
+                        &cb,    &gdone, &status, &wait_limit, &pred, &blobs_next};
         return hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_experts), grid, block, args,
                                   0, st, ev0, ev1, 0);
     }
     hipLaunchKernelGGL(dec_experts, grid, block, 0, st, blobs, erec, slots, xq, hq, out, T, cb,
-                       gdone, pred, blobs_next);
+                       gdone, status, wait_limit, pred, blobs_next);
     return hipGetLastError();
 }
 

@@ -351,6 +351,31 @@ struct PfItem {
     int ok, e, gp0, rows;
 };
 
+// The activations carry a per-token power-of-two scale 2^k (k = xexp of the
+// row's token, see the prep kernel): gate and up come out of the MFMAs times
+// 2^k; h is stored as silu(g) u times 2^(2k - 14), which keeps it inside
+// fp16's range for any input magnitude (about 2^6 times the row's largest
+// |xhat|^2 fits), and down's sums are divided by that again.  Every scaling
+// is an exact power of two.
+constexpr int H_EXP_SHIFT = 14;
+
+// Threads 0..PF_M-1 put the exponent of item row tid (0 past the item's end)
+// into kx; the caller's next barrier publishes it.
+__device__ inline void pf_row_exps(const PfItem &it, const int32_t *__restrict__ slots,
+                                   const int32_t *__restrict__ xexp, int T, int *kx)
+{
+    const int tid = threadIdx.x;
+    if (tid < PF_M) {
+        int k = 0;
+        if (tid < it.rows) {
+            const int sl = slots[it.gp0 + tid];
+            if (sl >= 0 && sl < T * K)
+                k = xexp[sl / K];
+        }
+        kx[tid] = k;
+    }
+}
+
 __device__ inline PfItem pf_item(int item, const int32_t *mlist, const int32_t *nitems,
                                  const int32_t *offsets, const int32_t *active, int T)
 {
@@ -380,9 +405,11 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
     const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ slots, const int32_t *__restrict__ active,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
-    const __half *__restrict__ xperm, __half *__restrict__ hperm, int T)
+    const __half *__restrict__ xperm, const int32_t *__restrict__ xexp, __half *__restrict__ hperm,
+    int T)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[PF_LDS_G];
+    __shared__ int kx[PF_M];
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int item = 8 * (idx / PF_NTILES_G) + xcd;
     const int nt = idx % PF_NTILES_G;
@@ -391,6 +418,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int jw = nt * PF_NT_G + 32 * wave;   // this wave's first FF row
+    pf_row_exps(it, slots, xexp, T, kx);
     const uint8_t *blob = blobs + (size_t)it.e * BLOB;
     // Activation rows this lane requests (rows past the item's end read its
     // first row; their results are never stored): rows 16 w + 8 h + lane % 8,
@@ -440,7 +468,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
         pg_gateup_loop<4>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
         break;
     }
-    // Epilogue: h = silu(g) * u for FF rows jw + 16 h2 + lane%16.
+    __syncthreads();   // kx
+    // Epilogue: h = silu(g) * u for FF rows jw + 16 h2 + lane%16, stored
+    // times 2^(2k - 14): g = acc 2^-k, and silu(g) acc_u = silu(g) u 2^k.
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
         const int j = jw + 16 * h2 + (lane & 15);
@@ -451,9 +481,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
             for (int r = 0; r < 4; ++r) {
                 const int m = 16 * mi + 4 * (lane >> 4) + r;
                 if (m < it.rows) {
-                    const float g = acc[h2][mi][r];
-                    const float u = acc[2 + h2][mi][r];
-                    const float h = pf_silu_mul(g, u);
+                    const int k = kx[m];
+                    const float g = ldexpf(acc[h2][mi][r], -k);
+                    const float h = ldexpf(pf_silu_mul(g, acc[2 + h2][mi][r]), k - H_EXP_SHIFT);
                     hperm[(size_t)(it.gp0 + m) * FF + col] = __float2half_rn(h);
                 }
             }
@@ -465,7 +495,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
     const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ slots, const int32_t *__restrict__ active,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
-    const __half *__restrict__ hperm, float *__restrict__ out, int T)
+    const int32_t *__restrict__ xexp, const __half *__restrict__ hperm, float *__restrict__ out,
+    int T)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[PF_LDS_D];
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
@@ -476,6 +507,14 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rw = nt * PF_NT_D + 64 * wave;   // this wave's first output row
+    // the exponent of item row tid (threads 0..PF_M-1), requested now, put in
+    // LDS once the activation tile there is no longer needed
+    int kmine = 0;
+    if (tid < it.rows) {
+        const int sl = slots[it.gp0 + tid];
+        if (sl >= 0 && sl < T * K)
+            kmine = xexp[sl / K];
+    }
     // Activation rows (past the item's end: its first row, never stored).
     PgAct act;
 #pragma unroll
@@ -542,6 +581,11 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
         pd_down_loop<4>(wr, sel_c, sel_d, sel_c2, sel_d2, odd, ae, ao, ae2, ao2, acc);
         break;
     }
+    int *kx = reinterpret_cast<int *>(lds);
+    __syncthreads();   // every wave is done with the activation tile
+    if (tid < PF_M)
+        kx[tid] = kmine;
+    __syncthreads();
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -549,10 +593,11 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
             const int m = 16 * mi + 4 * (lane >> 4) + r;
             if (m < it.rows) {
                 const int s = slots[it.gp0 + m];
+                const int sh = H_EXP_SHIFT - 2 * kx[m];   // h was stored times 2^(2k - 14)
                 if (s >= 0 && s < T * K) {
 #pragma unroll
                     for (int ns = 0; ns < 4; ++ns)
-                        out[(size_t)s * H + rw + 16 * ns + (lane & 15)] = acc[ns][mi][r];
+                        out[(size_t)s * H + rw + 16 * ns + (lane & 15)] = ldexpf(acc[ns][mi][r], sh);
                 }
             }
         }
@@ -562,23 +607,25 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
 hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
-                                  const __half *xperm, __half *hperm, float *out, int T,
-                                  hipEvent_t ev0, hipEvent_t ev1, hipStream_t st)
+                                  const __half *xperm, const int32_t *xexp, __half *hperm,
+                                  float *out, int T, hipEvent_t ev0, hipEvent_t ev1,
+                                  hipStream_t st)
 {
     const int groups = (max_items + 7) / 8;
     const dim3 grid_g(8 * PF_NTILES_G * groups), block(PF_THREADS);
     if (ev0) {   // timed launch: the events carry the dispatch's own start and end
-        void *args[] = {&blobs, &offsets, &slots, &active, &mlist, &nitems, &xperm, &hperm, &T};
+        void *args[] = {&blobs, &offsets, &slots, &active, &mlist, &nitems, &xperm, &xexp, &hperm,
+                        &T};
         const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&pf_gateup), grid_g,
                                                 block, args, 0, st, ev0, ev1, 0);
         if (e != hipSuccess)
             return e;
     } else {
         hipLaunchKernelGGL(pf_gateup, grid_g, block, 0, st, blobs, offsets, slots, active, mlist,
-                           nitems, xperm, hperm, T);
+                           nitems, xperm, xexp, hperm, T);
     }
     hipLaunchKernelGGL(pf_down, dim3(8 * PF_NTILES_D * groups), dim3(PF_THREADS), 0, st, blobs,
-                       offsets, slots, active, mlist, nitems, hperm, out, T);
+                       offsets, slots, active, mlist, nitems, xexp, hperm, out, T);
     return hipGetLastError();
 }
 

@@ -40,12 +40,23 @@ __device__ inline uint16_t bf16_rn_bits(float v)
     return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
+// The fp16 activations of the prefill GEMMs carry a per-token power-of-two
+// scale 2^k: k is chosen so that max |xhat_t| 2^k lies in [2^12, 2^13)
+// (k = 0 for an all-zero row, |k| <= 100), which keeps any input magnitude
+// inside fp16's normal range; xexp[t] = k lets the GEMM epilogues undo it
+// exactly.  For inputs whose rows peak in [4, 8) this is 2^10, and the
+// products and sums of the GEMMs are the unscaled ones times an exact power
+// of two.
+constexpr int XEXP_TARGET = 13;
+constexpr int XEXP_MAX = 100;
+
 __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     const float *__restrict__ x, int rmsnorm, uint16_t *__restrict__ xsplit,
-    __half *__restrict__ xperm)
+    __half *__restrict__ xperm, int32_t *__restrict__ xexp)
 {
     __shared__ float xs[H];
     __shared__ float wsum[PREP_THREADS / 64];
+    __shared__ float wmax[PREP_THREADS / 64];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const float *xt = x + (size_t)t * H;
@@ -65,9 +76,11 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
         const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
         inv = 1.f / sqrtf(tot / (float)H + 1e-6f);
     }
+    float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < H / PREP_THREADS; ++i) {
         const float h = v[i] * inv;
+        mx = fmaxf(mx, fabsf(h));
         const int c = tid + PREP_THREADS * i;
         xs[c] = h;
         // the router's exact three-term bf16 split of xhat
@@ -82,10 +95,19 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
             xo[2 * H] = bf16_rn_bits(r2);
         }
     }
+    mx = wave_max63(mx);
+    if ((tid & 63) == 0)
+        wmax[tid >> 6] = mx;
     __syncthreads();
     if (xperm) {
+        mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        int ex = 0;
+        (void)frexpf(mx, &ex);   // mx in [2^(ex-1), 2^ex)
+        const int k = mx > 0.f ? min(max(XEXP_TARGET - ex, -XEXP_MAX), XEXP_MAX) : 0;
+        if (tid == 0)
+            xexp[t] = k;
         for (int pos = tid; pos < H; pos += PREP_THREADS)
-            xperm[(size_t)t * H + pos] = __float2half_rn(xs[pg_col_of_pos(pos)]);
+            xperm[(size_t)t * H + pos] = __float2half_rn(ldexpf(xs[pg_col_of_pos(pos)], k));
     }
 }
 
@@ -275,9 +297,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 }
 
 hipError_t launch_prep(const float *x, int T, int rmsnorm, uint16_t *xsplit, __half *xperm,
-                       hipStream_t st)
+                       int32_t *xexp, hipStream_t st)
 {
-    hipLaunchKernelGGL(prep_kernel, dim3(T), dim3(PREP_THREADS), 0, st, x, rmsnorm, xsplit, xperm);
+    hipLaunchKernelGGL(prep_kernel, dim3(T), dim3(PREP_THREADS), 0, st, x, rmsnorm, xsplit, xperm,
+                       xexp);
     return hipGetLastError();
 }
 

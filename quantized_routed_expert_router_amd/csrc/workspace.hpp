@@ -8,8 +8,10 @@ namespace strata {
 // Workspace regions (byte offsets, 256-aligned) for a call with T tokens;
 // Td = T on the decode path (T <= DECODE_T_MAX) else 0, Tp the converse.
 struct Ws {
+    size_t status;     // i32 [1] (256 bytes reserved) status word, always at offset 0
     size_t xsplit;     // bf16 [Tp][3][H]    router input (prefill): x = x1 + x2 + x3 exactly
-    size_t xperm;      // f16 [Tp][H]        MFMA-ordered activations (prefill)
+    size_t xperm;      // f16 [Tp][H]        MFMA-ordered activations (prefill), times 2^xexp
+    size_t xexp;       // i32 [Tp]           per-token power-of-two exponent of xperm
     size_t logits;     // f32 [T][E]         logits (prefill) / raw logits (decode)
     size_t inv_rms;    // f32 [Td]
     size_t xq_dig;     // u32 [Td][40][32]   16-bit x, one 64-block per block column
@@ -39,6 +41,9 @@ struct Ws {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Bytes at the start of every workspace that hold the status word.
+constexpr size_t WS_STATUS_BYTES = 256;
+
 inline Ws ws_layout(int T)
 {
     Ws L{};
@@ -51,8 +56,10 @@ inline Ws ws_layout(int T)
         return at;
     };
     const size_t nb = H / QK, ns = FF / 16;
+    L.status = take(4);
     L.xsplit = take(Tp * 3 * H * 2);
     L.xperm = take(Tp * H * 2);
+    L.xexp = take(Tp * 4);
     L.logits = take((size_t)T * E * 4);
     L.inv_rms = take(Td * 4);
     L.xq_dig = take(Td * nb * 32 * 4);

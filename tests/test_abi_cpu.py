@@ -31,7 +31,7 @@ def m():
 
 def test_exports_every_declared_symbol(m):
     names = declared()
-    assert len(names) == 10, names
+    assert len(names) == 13, names
     assert set(names) == set(m.EXPORTS)
     for n in names:
         assert hasattr(m.lib(), n), n
@@ -88,6 +88,13 @@ def test_host_validation_rejects_before_launch(m):
     assert L.strata_moe_time_next_kernel(fake, None) == m.E_ARG
     assert L.strata_moe_time_next_kernel(None, fake) == m.E_ARG
     assert L.strata_moe_time_next_kernel(None, None) == m.OK
+    # status entry points: argument checks need no device
+    assert L.strata_moe_read_status(None, 256, None, None) == m.E_ARG
+    assert L.strata_moe_clear_status(None, 256, None) == m.E_ARG
+    assert L.strata_moe_clear_status(fake, 255, None) == m.E_WORKSPACE
+    assert L.strata_moe_clear_status(fake + 4, 256, None) == m.E_ALIGN
+    assert L.strata_moe_set_wait_limit(-1) == m.E_ARG
+    assert L.strata_moe_set_wait_limit(0) == m.OK
     for rc in (0, -1, -2, -3, -4, -5):
         assert m.strata_moe_status_string(rc) != "unknown status"
     assert m.strata_moe_status_string(-99) == "unknown status"

@@ -128,6 +128,23 @@ def test_decode_with_router_bias(T, flags):
     hz.check(f"decode T={T} flags={flags} biased", ids, w, y, oids, ow, oy)
 
 
+@pytest.mark.parametrize("T,scale", [(64, 1e5), (64, 1e-5), (300, 3e4), (4, 1e5), (4, 1e-5)])
+def test_input_magnitude(T, scale):
+    """Activations far from unit size, with the router scaled by the inverse
+    so that routing stays as for unit-size inputs: without RMSNorm the
+    experts see |x| up to ~4e5 (prefill: beyond fp16's range unless scaled)
+    or ~4e-5 (fp16's subnormal range), and the outputs scale as x^2."""
+    seed = 1500 + T
+    st = inputs.Streams(seed)
+    R = inputs.f32_to_bf16_bits(scr.bf16_values(inputs.draw_router(st.router)) / np.float32(scale))
+    x, _ = scr.screened_x(st, T, R, x_scale=scale)
+    _say(f"case: T={T} with |x| scaled by {scale:g}, seed {seed}")
+    ids, w, y, _ = hz.gpu_layer(x, R, hz.store(seed))
+    oids, ow, oy = hz.oracle_rows(x, R, seed, np.arange(T))
+    assert np.all(np.isfinite(y))
+    hz.check(f"T={T} |x| x {scale:g}", ids, w, y, oids, ow, oy)
+
+
 @pytest.mark.parametrize("T", [4, 100])
 def test_layer_equals_composition_and_is_deterministic(T):
     seed = 4000 + T
