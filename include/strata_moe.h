@@ -55,6 +55,7 @@ extern "C" {
 #define STRATA_MOE_BLOB 1382400 /* bytes per expert blob: gate, up, down */
 #define STRATA_MOE_T_MAX 8192  /* largest token count per call (one prefill chunk) */
 #define STRATA_LOOKAHEAD_T_MAX 8 /* largest token count of strata_moe_layer_lookahead */
+#define STRATA_STATIC_T_MAX 64   /* largest token count of strata_moe_layer_static */
 
 /* Status codes. */
 #define STRATA_OK 0
@@ -169,6 +170,26 @@ STRATA_API int strata_moe_layer_lookahead(float *x, int T, const uint16_t *route
                                int32_t *ids, float *w, const uint16_t *router_next,
                                const float *bias_next, const uint8_t *blobs_next,
                                int32_t *pred_ids, void *ws, size_t ws_bytes, void *stream);
+
+/* strata_moe_layer for callers that cannot allocate (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the same
+ * arguments without `ws` / `ws_bytes`, and bitwise the same results.  Its
+ * workspace is a static device array of 9 MiB per GPU, part of the library's
+ * code object (it stays allocated until the process ends); its address is
+ * looked up once per device on the first call made with that device
+ * current.  No call allocates or frees anything.
+ *  - T must be 1..STRATA_STATIC_T_MAX (64); larger T return STRATA_E_SHAPE
+ *    and enqueue nothing.
+ *  - Every call on one GPU uses the same array, which keeps the last call's
+ *    contents: calls that overlap on one GPU (other streams, other threads)
+ *    race and must be serialised by the caller.  Each call clears what it
+ *    needs cleared itself.
+ *  - The array's first 4 bytes are its status word (see below); it is zero
+ *    when the library is loaded and is never cleared by the library.
+ *  - STRATA_E_HIP if the array's address cannot be obtained. */
+STRATA_API int strata_moe_layer_static(float *x, int T, const uint16_t *router, const float *bias,
+                                       const uint8_t *blobs, int flags, float *y, int32_t *ids,
+                                       float *w, void *stream);
 
 /* Measurement hook (not part of the layer's math): arms the next
  * strata_moe_experts or strata_moe_layer call made by this host thread to

@@ -24,7 +24,8 @@ EXPORTS = ("strata_moe_blob_bytes", "strata_moe_workspace_bytes", "strata_moe_ro
            "strata_moe_group", "strata_moe_experts", "strata_moe_combine", "strata_moe_layer",
            "strata_moe_layer_lookahead", "strata_moe_time_next_kernel",
            "strata_moe_read_status", "strata_moe_clear_status", "strata_moe_set_wait_limit",
-           "strata_moe_status_string")
+           "strata_moe_layer_static", "strata_moe_status_string")
+STATIC_T_MAX = 64
 STATUS_WAIT_TIMEOUT = 1
 
 _lib = None
@@ -64,6 +65,8 @@ def lib():
                                                  vp, vp, sz, vp]
         L.strata_moe_time_next_kernel.restype = i32
         L.strata_moe_time_next_kernel.argtypes = [vp, vp]
+        L.strata_moe_layer_static.restype = i32
+        L.strata_moe_layer_static.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp]
         L.strata_moe_read_status.restype = i32
         L.strata_moe_read_status.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_int32), vp]
         L.strata_moe_clear_status.restype = i32
@@ -289,6 +292,28 @@ def strata_moe_layer(x, router, blobs, ws, bias=None, flags=0, y=None, ids=None,
                                 _p(y, torch.float32), _p(ids, torch.int32), _p(w, torch.float32),
                                 _p(ws), _nbytes(ws), _s(stream))
     _check("strata_moe_layer", rc)
+
+
+def strata_moe_layer_static(x, router, blobs, bias=None, flags=0, y=None, ids=None, w=None,
+                            stream=None):
+    """strata_moe_layer on the library's static per-GPU workspace (no
+    workspace argument, nothing allocated; T <= STATIC_T_MAX; calls on one GPU
+    must not overlap)."""
+    import torch
+    T = _tokens(x)
+    if T > STATIC_T_MAX:
+        raise ValueError(f"T = {T} exceeds the static workspace's {STATIC_T_MAX} tokens")
+    _router_shape("router", router)
+    _store_shape("blobs", blobs)
+    _opt_shape("bias", bias, (E,))
+    _opt_shape("y", y, (T, H))
+    _opt_shape("ids", ids, (T, K))
+    _opt_shape("w", w, (T, K))
+    rc = lib().strata_moe_layer_static(_p(x, torch.float32), T, _p_router(router),
+                                       _p(bias, torch.float32), _p(blobs, torch.uint8), flags,
+                                       _p(y, torch.float32), _p(ids, torch.int32),
+                                       _p(w, torch.float32), _s(stream))
+    _check("strata_moe_layer_static", rc)
 
 
 def strata_moe_layer_lookahead(x, router, blobs, ws, router_next, blobs_next, bias=None,

@@ -5,6 +5,7 @@
 #include "quant.hpp"
 #include "workspace.hpp"
 #include <atomic>
+#include <mutex>
 
 namespace strata {
 hipError_t launch_prep(const float *x, int T, int rmsnorm, uint16_t *xsplit, __half *xperm,
@@ -38,6 +39,14 @@ hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   hipStream_t st);
 hipError_t launch_combine(const float *out, const float *w, int T, float *y, float *res,
                           int accumulate_y, hipStream_t st);
+
+// The workspace of strata_moe_layer_static: one array per GPU, in the code
+// object's device memory (zero at load), shared by every call on that GPU.
+// Host code never uses `scratch` itself (on the host it is only a stand-in
+// for the symbol): the device address comes from hipGetSymbolAddress, once
+// per device, and only that address is handed to kernels.
+constexpr size_t STATIC_WS_BYTES = 9u << 20;   // 9 MiB: ws_layout(T) for any T <= 64
+static __device__ __align__(256) uint8_t scratch[STATIC_WS_BYTES];
 
 // Sets a workspace's status word to zero (graph-capturable, unlike a memset).
 __global__ void status_clear_kernel(int32_t *status)
@@ -225,6 +234,31 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
 } // namespace
 } // namespace strata
 
+namespace strata {
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device (looked up once per
+// device, with that device current), or NULL on failure.
+void *static_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return nullptr;
+        g_scratch[dev] = ptr;
+    }
+    return g_scratch[dev];
+}
+} // namespace
+} // namespace strata
+
 using namespace strata;
 
 extern "C" {
@@ -390,6 +424,23 @@ int strata_moe_set_wait_limit(int polls)
         return STRATA_E_ARG;
     g_wait_limit.store(polls == 0 ? WAIT_LIMIT_DEFAULT : polls);
     return STRATA_OK;
+}
+
+
+int strata_moe_layer_static(float *x, int T, const uint16_t *router, const float *bias,
+                            const uint8_t *blobs, int flags, float *y, int32_t *ids, float *w,
+                            void *stream)
+{
+    if (T < 1 || T > STRATA_STATIC_T_MAX)
+        return STRATA_E_SHAPE;
+    const size_t need = strata::ws_layout(T).total;
+    if (need > STATIC_WS_BYTES)   // cannot happen for T <= STRATA_STATIC_T_MAX
+        return STRATA_E_WORKSPACE;
+    void *ws = strata::static_scratch();
+    if (!ws)
+        return STRATA_E_HIP;
+    return strata::layer_impl(x, T, router, bias, blobs, flags, y, ids, w, nullptr, nullptr,
+                              nullptr, nullptr, ws, STATIC_WS_BYTES, stream);
 }
 
 const char *strata_moe_status_string(int status)

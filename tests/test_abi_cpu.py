@@ -31,7 +31,7 @@ def m():
 
 def test_exports_every_declared_symbol(m):
     names = declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(m.EXPORTS)
     for n in names:
         assert hasattr(m.lib(), n), n
@@ -88,6 +88,10 @@ def test_host_validation_rejects_before_launch(m):
     assert L.strata_moe_time_next_kernel(fake, None) == m.E_ARG
     assert L.strata_moe_time_next_kernel(None, fake) == m.E_ARG
     assert L.strata_moe_time_next_kernel(None, None) == m.OK
+    # the static-workspace layer: T beyond its limit is refused before any
+    # device call
+    assert L.strata_moe_layer_static(fake, 65, fake, None, fake, 2, None, None, None, None) == m.E_SHAPE
+    assert L.strata_moe_layer_static(fake, 0, fake, None, fake, 2, None, None, None, None) == m.E_SHAPE
     # status entry points: argument checks need no device
     assert L.strata_moe_read_status(None, 256, None, None) == m.E_ARG
     assert L.strata_moe_clear_status(None, 256, None) == m.E_ARG
