@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
+MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, TOP/s
 GATEUP_FLOP_PER_SLOT = 2 * 2 * 2560 * 640
 
 WORKLOADS = {
@@ -48,6 +49,8 @@ WORKLOADS = {
     "stack-decode": dict(wl="stack48-T1", T=1, layers=48, copies=1),
     "stack-decode-lookahead": dict(wl="stack48-T1", T=1, layers=48, copies=1, lookahead=True),
     "prefill": dict(wl="layer-T2048-prefill", T=2048, layers=1, copies=4),
+    # the integer variant (STRATA_INT8: int8 activations on the int8 matrix cores)
+    "prefill-i8": dict(wl="layer-T2048-prefill", T=2048, layers=1, copies=4, int8=True),
     "stack-prefill": dict(wl="stack48-T32768-zipf", T=2048, layers=48, copies=1),
 }
 # measured beside the headline in a default run
@@ -119,6 +122,9 @@ def measure(name, a, cpu_seconds):
     stack = L > 1
     prefill = T > 16
     flags = (m.RMSNORM | m.RESIDUAL) if stack else 0
+    int8 = bool(wl.get("int8"))
+    if int8:
+        flags |= m.INT8
     x, routers, biases = inputs.workload_inputs(wl["wl"], T=T)
     x = np.ascontiguousarray(x[:T])
     blob = inputs.blob_bytes()
@@ -262,14 +268,17 @@ def measure(name, a, cpu_seconds):
     k_work = float(np.mean(units)) * per_unit
 
     tok_s = T / (ms / 1e3)
-    if prefill:
+    if prefill and int8:
+        roof = {"bound": "mfma", "achieved": k_work / (k_ms / 1e3) / 1e12,
+                "peak": MFMA_I8_PEAK_TOPS, "unit": "TOP/s"}
+    elif prefill:
         roof = {"bound": "mfma", "achieved": k_work / (k_ms / 1e3) / 1e12,
                 "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": k_work / (k_ms / 1e3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "pf_gateup" if prefill else "dec_experts"
+    roof["kernel"] = ("pq_gateup" if int8 else "pf_gateup") if prefill else "dec_experts"
     # HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or null
     roof["traffic"] = traffic_from_profile(roof["kernel"], name)
     if roof["traffic"] is not None and not prefill:
@@ -296,7 +305,8 @@ def measure(name, a, cpu_seconds):
     res = {
         "metric": metric, "value": value, "unit": unit, "ms_per_step": ms,
         "steps": a.steps, "warmup": a.warmup,
-        "dtype": "f16-mfma/f32-acc" if prefill else "i4dot-16bit/f32-acc",
+        "dtype": ("i8-mfma/f32-acc" if int8 else "f16-mfma/f32-acc") if prefill
+                 else "i4dot-16bit/f32-acc",
         "config": {"workload": f"{name}: {cfg['name']}, T={T}, layers={L}, "
                                f"512 Q2_0 experts, top-10",
                    "global_batch": T, "seq_len": T if prefill else 1,

@@ -71,6 +71,7 @@ extern "C" {
 /* Flags. */
 #define STRATA_RMSNORM 1  /* normalise x first: x / sqrt(mean(x^2) + 1e-6), unit gain */
 #define STRATA_RESIDUAL 2 /* combine adds into its output (x += y) instead of storing */
+#define STRATA_INT8 4     /* experts and layer calls with T > 16: the integer variant (below) */
 
 /* Bytes of one Q2_0 expert blob (1,382,400): the gate [FF][H], up [FF][H] and
  * down [H][FF] matrices in that order, each row a run of 18-byte blocks along
@@ -126,7 +127,18 @@ STRATA_API int strata_moe_group(const int32_t *ids, int T, int32_t *offsets, int
  * products: x as 16-bit integers per 64-value block and h per 16-value
  * segment, against the exact 2-bit codes, with exact int32 block sums and
  * fp32 across blocks; larger T uses fp16 MFMA grouped GEMMs with exactly
- * dequantised weights and fp32 accumulation. */
+ * dequantised weights and fp32 accumulation.  For T > 16 the fp16
+ * activations carry an exact per-token power-of-two scale (the token's
+ * largest |xhat| maps into [2^12, 2^13)), and h one that follows the square
+ * of the input's magnitude outside [1, 8), so inputs of any magnitude stay
+ * in fp16's range; an h value whose magnitude exceeds 65504 times that
+ * scale would overflow to inf.
+ * With STRATA_INT8 and T > 16, the integer variant of [SRC] "The CPU
+ * kernels" runs instead: xhat and h as int8 per 64-value block (scale
+ * max|v| / 127), the raw codes on int8 MFMA with the code offset removed by
+ * the block's -(sum q), fp32 across blocks.  Its results differ from the
+ * exact layer by the int8 rounding of the activations (about 1e-2 of max|y|;
+ * see the parity tests), which the fp16 path does not have. */
 STRATA_API int strata_moe_experts(const float *x, int T, const uint8_t *blobs, const int32_t *offsets,
                        const int32_t *slots, const int32_t *active, int flags, float *out,
                        void *ws, size_t ws_bytes, void *stream);
@@ -145,7 +157,8 @@ STRATA_API int strata_moe_combine(const float *out, const float *w, int T, int f
  *   y      [T][H] fp32 out (layer output without residual), or NULL; must not
  *          be NULL unless STRATA_RESIDUAL is set.
  *   ids, w [T][K] out, or NULL to keep them in the workspace.
- * Other arguments as above.  Results equal the four-call composition. */
+ * Other arguments as above (flags: STRATA_RMSNORM, STRATA_RESIDUAL,
+ * STRATA_INT8).  Results equal the four-call composition. */
 STRATA_API int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
                      const uint8_t *blobs, int flags, float *y, int32_t *ids, float *w,
                      void *ws, size_t ws_bytes, void *stream);

@@ -17,7 +17,7 @@ H, FF, E, K, QK, BB = 2560, 640, 512, 10, 64, 18
 BLOB = 1382400
 T_MAX = 8192
 LOOKAHEAD_T_MAX = 8
-RMSNORM, RESIDUAL = 1, 2
+RMSNORM, RESIDUAL, INT8 = 1, 2, 4
 OK, E_ARG, E_SHAPE, E_WORKSPACE, E_HIP, E_ALIGN = 0, -1, -2, -3, -4, -5
 
 EXPORTS = ("strata_moe_blob_bytes", "strata_moe_workspace_bytes", "strata_moe_route",

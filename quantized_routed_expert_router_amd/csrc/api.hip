@@ -39,6 +39,16 @@ hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   hipStream_t st);
 hipError_t launch_combine(const float *out, const float *w, int T, float *y, float *res,
                           int accumulate_y, hipStream_t st);
+hipError_t launch_prep_i8(const float *x, int T, int rmsnorm, int8_t *x8, float *xs, int32_t *xn,
+                          hipStream_t st);
+hipError_t launch_prefill_experts_i8(const uint8_t *blobs, const int32_t *offsets,
+                                     const int32_t *slots, const int32_t *active,
+                                     const int32_t *mlist, const int32_t *nitems, int max_items,
+                                     const int8_t *x8, const float *xs8, const int32_t *xn8,
+                                     int8_t *h8, float *hs8, int32_t *hn8, float *out, int T,
+                                     hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
+
+constexpr int ALL_FLAGS = STRATA_RMSNORM | STRATA_RESIDUAL | STRATA_INT8;
 
 // The workspace of strata_moe_layer_static: one array per GPU, in the code
 // object's device memory (zero at load), shared by every call on that GPU.
@@ -100,6 +110,9 @@ struct Carve {
     float *lraw2;
     int32_t *pred, *gcount;
     int32_t *status, *xexp;
+    int8_t *x8, *h8;
+    float *xs8, *hs8;
+    int32_t *xn8, *hn8;
 };
 
 Carve carve(void *ws, int T)
@@ -125,6 +138,12 @@ Carve carve(void *ws, int T)
     c.gcount = at<int32_t>(ws, L.gcount);
     c.status = at<int32_t>(ws, L.status);
     c.xexp = at<int32_t>(ws, L.xexp);
+    c.x8 = at<int8_t>(ws, L.x8);
+    c.h8 = at<int8_t>(ws, L.h8);
+    c.xs8 = at<float>(ws, L.xs8);
+    c.hs8 = at<float>(ws, L.hs8);
+    c.xn8 = at<int32_t>(ws, L.xn8);
+    c.hn8 = at<int32_t>(ws, L.hn8);
     c.ids = at<int32_t>(ws, L.ids);
     c.w = at<float>(ws, L.w);
     c.mlist = at<int32_t>(ws, L.mlist);
@@ -145,7 +164,7 @@ Carve carve(void *ws, int T)
 // by the grouping of the layer call).
 int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
                 const int32_t *slots, const int32_t *active, float *out, int T, hipStream_t st,
-                bool planned = false)
+                bool planned = false, bool int8 = false)
 {
     hipEvent_t e0, e1;
     take_events(e0, e1);
@@ -156,6 +175,12 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
     } else {
         if (!planned)
             STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
+        if (int8) {
+            STRATA_TRY(launch_prefill_experts_i8(blobs, offsets, slots, active, c.mlist, c.nitems,
+                                                 c.L.max_items, c.x8, c.xs8, c.xn8, c.h8, c.hs8,
+                                                 c.hn8, out, T, e0, e1, st));
+            return STRATA_OK;
+        }
         STRATA_TRY(launch_prefill_experts(blobs, offsets, slots, active, c.mlist, c.nitems,
                                           c.L.max_items, c.xperm, c.xexp, c.hperm, out, T, e0,
                                           e1, st));
@@ -167,9 +192,11 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
 // work records of the caller's grouping; prefill: normalised fp32 and
 // K-ordered fp16 copies).
 int run_prep(const Carve &c, const float *x, int T, int rms, const int32_t *offsets,
-             const int32_t *slots, const int32_t *active, hipStream_t st)
+             const int32_t *slots, const int32_t *active, hipStream_t st, bool int8 = false)
 {
-    if (is_decode(T))
+    if (!is_decode(T) && int8)
+        STRATA_TRY(launch_prep_i8(x, T, rms, c.x8, c.xs8, c.xn8, st));
+    else if (is_decode(T))
         STRATA_TRY(launch_prep_decode(x, T, rms, c.xq, offsets, slots, active, c.erec, c.esync, st));
     else
         STRATA_TRY(launch_prep(x, T, rms, nullptr, c.xperm, c.xexp, st));
@@ -187,7 +214,7 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
     int rc = check_T(T);
     if (rc)
         return rc;
-    if (!x || !router || !blobs || (flags & ~(STRATA_RMSNORM | STRATA_RESIDUAL)))
+    if (!x || !router || !blobs || (flags & ~ALL_FLAGS))
         return STRATA_E_ARG;
     if (!y && !(flags & STRATA_RESIDUAL))
         return STRATA_E_ARG;
@@ -210,11 +237,14 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
                                        c.slots, c.erec, c.cdone, c.esync, router2, bias2, c.lraw2,
                                        pred_o, st));
     } else {
-        STRATA_TRY(launch_prep(x, T, rms, c.xsplit, c.xperm, c.xexp, st));
+        const bool int8 = flags & STRATA_INT8;
+        STRATA_TRY(launch_prep(x, T, rms, c.xsplit, int8 ? nullptr : c.xperm, c.xexp, st));
         STRATA_TRY(launch_logits(c.xsplit, T, router, bias, c.logits, st));
         STRATA_TRY(launch_topk(c.logits, T, ids_o, w_o, st));
         STRATA_TRY(launch_group(ids_o, T, c.offsets, c.slots, c.active, c.gcount, c.L.max_items,
                                 c.mlist, c.nitems, st));
+        if (int8)
+            STRATA_TRY(launch_prep_i8(x, T, rms, c.x8, c.xs8, c.xn8, st));
     }
     const bool res = flags & STRATA_RESIDUAL;
     if (is_decode(T)) {   // the experts kernel finishes the combine
@@ -226,7 +256,8 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
                                          c.status, g_wait_limit.load(), e0, e1, st));
         return STRATA_OK;
     }
-    if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st, true)))
+    if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st, true,
+                          flags & STRATA_INT8)))
         return rc;
     STRATA_TRY(launch_combine(c.out, w_o, T, y, res ? x : nullptr, 0, st));
     return STRATA_OK;
@@ -324,8 +355,7 @@ int strata_moe_experts(const float *x, int T, const uint8_t *blobs, const int32_
     int rc = check_T(T);
     if (rc)
         return rc;
-    if (!x || !blobs || !offsets || !slots || !active || !out ||
-        (flags & ~(STRATA_RMSNORM | STRATA_RESIDUAL)))
+    if (!x || !blobs || !offsets || !slots || !active || !out || (flags & ~ALL_FLAGS))
         return STRATA_E_ARG;
     if ((rc = check_ws(ws, ws_bytes, T)))
         return rc;
@@ -334,9 +364,10 @@ int strata_moe_experts(const float *x, int T, const uint8_t *blobs, const int32_
         return STRATA_E_ALIGN;
     hipStream_t st = (hipStream_t)stream;
     Carve c = carve(ws, T);
-    if ((rc = run_prep(c, x, T, flags & STRATA_RMSNORM, offsets, slots, active, st)))
+    const bool int8 = flags & STRATA_INT8;
+    if ((rc = run_prep(c, x, T, flags & STRATA_RMSNORM, offsets, slots, active, st, int8)))
         return rc;
-    return run_experts(c, blobs, offsets, slots, active, out, T, st);
+    return run_experts(c, blobs, offsets, slots, active, out, T, st, false, int8);
 }
 
 int strata_moe_combine(const float *out, const float *w, int T, int flags, float *y,

@@ -353,11 +353,16 @@ struct PfItem {
 
 // The activations carry a per-token power-of-two scale 2^k (k = xexp of the
 // row's token, see the prep kernel): gate and up come out of the MFMAs times
-// 2^k; h is stored as silu(g) u times 2^(2k - 14), which keeps it inside
-// fp16's range for any input magnitude (about 2^6 times the row's largest
-// |xhat|^2 fits), and down's sums are divided by that again.  Every scaling
-// is an exact power of two.
-constexpr int H_EXP_SHIFT = 14;
+// 2^k and are divided by it before SiLU.  h is stored times 2^hs(k): rows
+// whose largest |xhat| lies in [1, 8) (k = 10, 11, 12; every RMSNorm'd row
+// without a large outlier) keep h unscaled, larger inputs scale it down and
+// smaller ones up, twice as fast as k (h grows as x^2), so that it stays
+// inside fp16's range at any input magnitude; down's sums are divided by
+// 2^hs(k) again.  Every scaling is an exact power of two.
+__device__ inline int h_shift(int k)
+{
+    return 2 * min(k - 10, 0) + 2 * max(k - 12, 0);
+}
 
 // Threads 0..PF_M-1 put the exponent of item row tid (0 past the item's end)
 // into kx; the caller's next barrier publishes it.
@@ -470,7 +475,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
     }
     __syncthreads();   // kx
     // Epilogue: h = silu(g) * u for FF rows jw + 16 h2 + lane%16, stored
-    // times 2^(2k - 14): g = acc 2^-k, and silu(g) acc_u = silu(g) u 2^k.
+    // times 2^hs(k): g = acc 2^-k, and silu(g) acc_u = silu(g) u 2^k.
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
         const int j = jw + 16 * h2 + (lane & 15);
@@ -483,7 +488,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
                 if (m < it.rows) {
                     const int k = kx[m];
                     const float g = ldexpf(acc[h2][mi][r], -k);
-                    const float h = ldexpf(pf_silu_mul(g, acc[2 + h2][mi][r]), k - H_EXP_SHIFT);
+                    const float h = ldexpf(pf_silu_mul(g, acc[2 + h2][mi][r]), h_shift(k) - k);
                     hperm[(size_t)(it.gp0 + m) * FF + col] = __float2half_rn(h);
                 }
             }
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
             const int m = 16 * mi + 4 * (lane >> 4) + r;
             if (m < it.rows) {
                 const int s = slots[it.gp0 + m];
-                const int sh = H_EXP_SHIFT - 2 * kx[m];   // h was stored times 2^(2k - 14)
+                const int sh = -h_shift(kx[m]);   // h was stored times 2^hs(k)
                 if (s >= 0 && s < T * K) {
 #pragma unroll
                     for (int ns = 0; ns < 4; ++ns)

@@ -35,6 +35,12 @@ struct Ws {
     size_t gcount;     // i32 [ceil(Tp*K/256)][E] prefill grouping: per-block expert counts / starts
     size_t lraw2;      // f32 [Td][E]        lookahead: the next layer's raw logits
     size_t pred;       // i32 [Td*K]         lookahead: the next layer's predicted ids
+    size_t x8;         // i8 [Tp][H]         int8 variant: activations per 64-block
+    size_t xs8;        // f32 [Tp][40]       their scales
+    size_t xn8;        // i32 [Tp][40]       -(sum q) per block
+    size_t h8;         // i8 [Tp*K][FF]      int8 variant: h per 64-block (grouped order)
+    size_t hs8;        // f32 [Tp*K][10]
+    size_t hn8;        // i32 [Tp*K][10]
     size_t total;
     int max_items;
 };
@@ -84,6 +90,12 @@ inline Ws ws_layout(int T)
     L.gcount = take((Tp * K + 255) / 256 * E * 4);
     L.lraw2 = take(Td * E * 4);
     L.pred = take(Td * K * 4);
+    L.x8 = take(Tp * H);
+    L.xs8 = take(Tp * nb * 4);
+    L.xn8 = take(Tp * nb * 4);
+    L.h8 = take(Tp * K * FF);
+    L.hs8 = take(Tp * K * (FF / QK) * 4);
+    L.hn8 = take(Tp * K * (FF / QK) * 4);
     L.total = o;
     return L;
 }
