@@ -54,7 +54,7 @@ WORKLOADS = {
     "stack-prefill": dict(wl="stack48-T32768-zipf", T=2048, layers=48, copies=1),
 }
 # measured beside the headline in a default run
-ALSO = ("token", "prefill", "stack-decode", "stack-prefill")
+ALSO = ("token", "prefill", "prefill-i8", "stack-decode", "stack-prefill")
 
 
 # HBM traffic of the dominant kernel from committed rocprofv3 counter

@@ -187,7 +187,7 @@ STRATA_API int strata_moe_layer_lookahead(float *x, int T, const uint16_t *route
 /* strata_moe_layer for callers that cannot allocate (code under HIP graph
  * capture, serving loops or harnesses that forbid hipMalloc): the same
  * arguments without `ws` / `ws_bytes`, and bitwise the same results.  Its
- * workspace is a static device array of 9 MiB per GPU, part of the library's
+ * workspace is a static device array of 10 MiB per GPU, part of the library's
  * code object (it stays allocated until the process ends); its address is
  * looked up once per device on the first call made with that device
  * current.  No call allocates or frees anything.

@@ -55,7 +55,9 @@ constexpr int ALL_FLAGS = STRATA_RMSNORM | STRATA_RESIDUAL | STRATA_INT8;
 // Host code never uses `scratch` itself (on the host it is only a stand-in
 // for the symbol): the device address comes from hipGetSymbolAddress, once
 // per device, and only that address is handed to kernels.
-constexpr size_t STATIC_WS_BYTES = 9u << 20;   // 9 MiB: ws_layout(T) for any T <= 64
+constexpr size_t STATIC_WS_BYTES = 10u << 20;   // 10 MiB: ws_layout(T) for any T <= 64
+static_assert(strata::ws_max_bytes(STRATA_STATIC_T_MAX) <= STATIC_WS_BYTES,
+              "the static workspace holds every T up to STRATA_STATIC_T_MAX");
 static __device__ __align__(256) uint8_t scratch[STATIC_WS_BYTES];
 
 // Sets a workspace's status word to zero (graph-capturable, unlike a memset).

@@ -40,9 +40,9 @@ constexpr int PF_NT_D = 256;                   // output rows per down work item
 constexpr int PF_NTILES_G = FF / PF_NT_G;      // 5
 constexpr int PF_NTILES_D = H / PF_NT_D;       // 10
 
-inline bool is_decode(int T) { return T <= DECODE_T_MAX; }
+constexpr bool is_decode(int T) { return T <= DECODE_T_MAX; }
 
-inline int pf_max_items(int T) { return E + (T * K + PF_M - 1) / PF_M; }
+constexpr int pf_max_items(int T) { return E + (T * K + PF_M - 1) / PF_M; }
 
 // ---------------------------------------------------------------- device helpers
 __device__ inline float half_bits_to_float(uint32_t bits)

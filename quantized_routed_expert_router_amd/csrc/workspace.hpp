@@ -45,12 +45,12 @@ struct Ws {
     int max_items;
 };
 
-inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Bytes at the start of every workspace that hold the status word.
 constexpr size_t WS_STATUS_BYTES = 256;
 
-inline Ws ws_layout(int T)
+constexpr Ws ws_layout(int T)
 {
     Ws L{};
     size_t o = 0;
@@ -98,6 +98,15 @@ inline Ws ws_layout(int T)
     L.hn8 = take(Tp * K * (FF / QK) * 4);
     L.total = o;
     return L;
+}
+
+// The largest workspace any T in 1..tmax needs.
+constexpr size_t ws_max_bytes(int tmax)
+{
+    size_t m = 0;
+    for (int T = 1; T <= tmax; ++T)
+        m = ws_layout(T).total > m ? ws_layout(T).total : m;
+    return m;
 }
 
 } // namespace strata
