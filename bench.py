@@ -63,6 +63,7 @@ ALSO = ("token", "prefill", "prefill-i8", "stack-decode", "stack-prefill")
 TRAFFIC = {
     ("dec_experts", "window"): ("T4_window", ["experts_decode.hip", "quant.hpp", "common.hpp"]),
     ("pf_gateup", "prefill"): ("T2048_prefill", ["experts_prefill.hip", "common.hpp"]),
+    ("pq_gateup", "prefill-i8"): ("T2048_prefill_int8", ["experts_prefill_i8.hip", "common.hpp"]),
 }
 
 
