@@ -35,7 +35,7 @@ hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
                                   const __half *xperm, const int32_t *xexp, __half *hperm,
-                                  float *out, int T, hipEvent_t ev0, hipEvent_t ev1,
+                                  int32_t *hexp, float *out, int T, hipEvent_t ev0, hipEvent_t ev1,
                                   hipStream_t st);
 hipError_t launch_combine(const float *out, const float *w, int T, float *y, float *res,
                           int accumulate_y, hipStream_t st);
@@ -111,7 +111,7 @@ struct Carve {
     int32_t *cdone, *esync;
     float *lraw2;
     int32_t *pred, *gcount;
-    int32_t *status, *xexp;
+    int32_t *status, *xexp, *hexp;
     int8_t *x8, *h8;
     float *xs8, *hs8;
     int32_t *xn8, *hn8;
@@ -140,6 +140,7 @@ Carve carve(void *ws, int T)
     c.gcount = at<int32_t>(ws, L.gcount);
     c.status = at<int32_t>(ws, L.status);
     c.xexp = at<int32_t>(ws, L.xexp);
+    c.hexp = at<int32_t>(ws, L.hexp);
     c.x8 = at<int8_t>(ws, L.x8);
     c.h8 = at<int8_t>(ws, L.h8);
     c.xs8 = at<float>(ws, L.xs8);
@@ -184,8 +185,8 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
             return STRATA_OK;
         }
         STRATA_TRY(launch_prefill_experts(blobs, offsets, slots, active, c.mlist, c.nitems,
-                                          c.L.max_items, c.xperm, c.xexp, c.hperm, out, T, e0,
-                                          e1, st));
+                                          c.L.max_items, c.xperm, c.xexp, c.hperm, c.hexp, out, T,
+                                          e0, e1, st));
     }
     return STRATA_OK;
 }

@@ -34,6 +34,7 @@ constexpr int DECODE_T_MAX = 16;
 constexpr int SYNC_STRIDE = 32;
 
 // Prefill path tiles.
+constexpr int GB_SLOTS = 1024;                 // slots per block of the prefill grouping
 constexpr int PF_M = 64;                       // tokens per M-chunk
 constexpr int PF_NT_G = 128;                   // FF rows per gate/up work item
 constexpr int PF_NT_D = 256;                   // output rows per down work item

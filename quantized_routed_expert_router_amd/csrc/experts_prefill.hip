@@ -351,33 +351,38 @@ struct PfItem {
     int ok, e, gp0, rows;
 };
 
-// The activations carry a per-token power-of-two scale 2^k (k = xexp of the
-// row's token, see the prep kernel): gate and up come out of the MFMAs times
-// 2^k and are divided by it before SiLU.  h is stored times 2^hs(k): rows
-// whose largest |xhat| lies in [1, 8) (k = 10, 11, 12; every RMSNorm'd row
-// without a large outlier) keep h unscaled, larger inputs scale it down and
-// smaller ones up, twice as fast as k (h grows as x^2), so that it stays
-// inside fp16's range at any input magnitude; down's sums are divided by
-// 2^hs(k) again.  Every scaling is an exact power of two.
-__device__ inline int h_shift(int k)
-{
-    return 2 * min(k - 10, 0) + 2 * max(k - 12, 0);
-}
+// The activations carry a per-token power-of-two scale 2^k and h a second
+// one, 2^hs (both 0 for rows whose largest |xhat| lies in [1, 8); see the prep
+// kernel): gate and up come out of the MFMAs times 2^k and are divided by it
+// before SiLU, h is stored times 2^hs so that it stays inside fp16's range at
+// any input magnitude, and down's sums are divided by 2^hs again.  Every
+// scaling is an exact power of two.  xexp[t] holds k in its low 16 bits and
+// hs in its high 16 bits, both signed.
+__device__ inline int pf_k(int v) { return (int)(int16_t)(v & 0xffff); }
+__device__ inline int pf_hs(int v) { return v >> 16; }
 
-// Threads 0..PF_M-1 put the exponent of item row tid (0 past the item's end)
-// into kx; the caller's next barrier publishes it.
-__device__ inline void pf_row_exps(const PfItem &it, const int32_t *__restrict__ slots,
-                                   const int32_t *__restrict__ xexp, int T, int *kx)
+// Threads 0..PF_M-1 (wave 0) put the packed exponents of item row tid (0 past
+// the item's end) into kx and whether any is nonzero into kx[PF_M]; the
+// caller's next barrier publishes them.  N-tile 0 also records each row's hs
+// for the down kernel (hexp, in grouped order).
+__device__ inline void pf_row_exps(const PfItem &it, int nt, const int32_t *__restrict__ slots,
+                                   const int32_t *__restrict__ xexp, int32_t *__restrict__ hexp,
+                                   int T, int *kx)
 {
     const int tid = threadIdx.x;
     if (tid < PF_M) {
-        int k = 0;
+        int v = 0;
         if (tid < it.rows) {
             const int sl = slots[it.gp0 + tid];
             if (sl >= 0 && sl < T * K)
-                k = xexp[sl / K];
+                v = xexp[sl / K];
+            if (nt == 0)
+                hexp[it.gp0 + tid] = pf_hs(v);
         }
-        kx[tid] = k;
+        kx[tid] = v;
+        const bool any = __ballot(v != 0) != 0;
+        if (tid == 0)
+            kx[PF_M] = any;
     }
 }
 
@@ -411,10 +416,10 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
     const int32_t *__restrict__ slots, const int32_t *__restrict__ active,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
     const __half *__restrict__ xperm, const int32_t *__restrict__ xexp, __half *__restrict__ hperm,
-    int T)
+    int32_t *__restrict__ hexp, int T)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[PF_LDS_G];
-    __shared__ int kx[PF_M];
+    __shared__ int kx[PF_M + 1];
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int item = 8 * (idx / PF_NTILES_G) + xcd;
     const int nt = idx % PF_NTILES_G;
@@ -423,7 +428,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int jw = nt * PF_NT_G + 32 * wave;   // this wave's first FF row
-    pf_row_exps(it, slots, xexp, T, kx);
+    pf_row_exps(it, nt, slots, xexp, hexp, T, kx);
     const uint8_t *blob = blobs + (size_t)it.e * BLOB;
     // Activation rows this lane requests (rows past the item's end read its
     // first row; their results are never stored): rows 16 w + 8 h + lane % 8,
@@ -475,7 +480,9 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
     }
     __syncthreads();   // kx
     // Epilogue: h = silu(g) * u for FF rows jw + 16 h2 + lane%16, stored
-    // times 2^hs(k): g = acc 2^-k, and silu(g) acc_u = silu(g) u 2^k.
+    // times 2^hs: g = acc 2^-k, and silu(g) acc_u = silu(g) u 2^k.  Items whose
+    // rows are all unscaled skip the exponents.
+    const bool scaled = kx[PF_M] != 0;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
         const int j = jw + 16 * h2 + (lane & 15);
@@ -486,9 +493,14 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
             for (int r = 0; r < 4; ++r) {
                 const int m = 16 * mi + 4 * (lane >> 4) + r;
                 if (m < it.rows) {
-                    const int k = kx[m];
-                    const float g = ldexpf(acc[h2][mi][r], -k);
-                    const float h = ldexpf(pf_silu_mul(g, acc[2 + h2][mi][r]), h_shift(k) - k);
+                    float h;
+                    if (scaled) {
+                        const int v = kx[m], k = pf_k(v);
+                        const float g = ldexpf(acc[h2][mi][r], -k);
+                        h = ldexpf(pf_silu_mul(g, acc[2 + h2][mi][r]), pf_hs(v) - k);
+                    } else {
+                        h = pf_silu_mul(acc[h2][mi][r], acc[2 + h2][mi][r]);
+                    }
                     hperm[(size_t)(it.gp0 + m) * FF + col] = __float2half_rn(h);
                 }
             }
@@ -500,7 +512,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
     const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ slots, const int32_t *__restrict__ active,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
-    const int32_t *__restrict__ xexp, const __half *__restrict__ hperm, float *__restrict__ out,
+    const int32_t *__restrict__ hexp, const __half *__restrict__ hperm, float *__restrict__ out,
     int T)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[PF_LDS_D];
@@ -512,13 +524,19 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rw = nt * PF_NT_D + 64 * wave;   // this wave's first output row
-    // the exponent of item row tid (threads 0..PF_M-1), requested now, put in
-    // LDS once the activation tile there is no longer needed
-    int kmine = 0;
-    if (tid < it.rows) {
-        const int sl = slots[it.gp0 + tid];
-        if (sl >= 0 && sl < T * K)
-            kmine = xexp[sl / K];
+    // The slot and the h exponent of this lane's 16 output rows, loaded now so
+    // the epilogue does not wait for them (rows past the item's end read its
+    // first row and are never stored).
+    int osl[4][4], ohs[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 16 * mi + 4 * (lane >> 4) + r;
+            const int gp = it.gp0 + (m < it.rows ? m : 0);
+            osl[mi][r] = slots[gp];
+            ohs[mi][r] = hexp[gp];
+        }
     }
     // Activation rows (past the item's end: its first row, never stored).
     PgAct act;
@@ -586,19 +604,14 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
         pd_down_loop<4>(wr, sel_c, sel_d, sel_c2, sel_d2, odd, ae, ao, ae2, ao2, acc);
         break;
     }
-    int *kx = reinterpret_cast<int *>(lds);
-    __syncthreads();   // every wave is done with the activation tile
-    if (tid < PF_M)
-        kx[tid] = kmine;
-    __syncthreads();
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 16 * mi + 4 * (lane >> 4) + r;
             if (m < it.rows) {
-                const int s = slots[it.gp0 + m];
-                const int sh = -h_shift(kx[m]);   // h was stored times 2^hs(k)
+                const int s = osl[mi][r];
+                const int sh = -ohs[mi][r];   // h was stored times 2^hs
                 if (s >= 0 && s < T * K) {
 #pragma unroll
                     for (int ns = 0; ns < 4; ++ns)
@@ -613,24 +626,24 @@ hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
                                   const __half *xperm, const int32_t *xexp, __half *hperm,
-                                  float *out, int T, hipEvent_t ev0, hipEvent_t ev1,
+                                  int32_t *hexp, float *out, int T, hipEvent_t ev0, hipEvent_t ev1,
                                   hipStream_t st)
 {
     const int groups = (max_items + 7) / 8;
     const dim3 grid_g(8 * PF_NTILES_G * groups), block(PF_THREADS);
     if (ev0) {   // timed launch: the events carry the dispatch's own start and end
         void *args[] = {&blobs, &offsets, &slots, &active, &mlist, &nitems, &xperm, &xexp, &hperm,
-                        &T};
+                        &hexp, &T};
         const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&pf_gateup), grid_g,
                                                 block, args, 0, st, ev0, ev1, 0);
         if (e != hipSuccess)
             return e;
     } else {
         hipLaunchKernelGGL(pf_gateup, grid_g, block, 0, st, blobs, offsets, slots, active, mlist,
-                           nitems, xperm, xexp, hperm, T);
+                           nitems, xperm, xexp, hperm, hexp, T);
     }
     hipLaunchKernelGGL(pf_down, dim3(8 * PF_NTILES_D * groups), dim3(PF_THREADS), 0, st, blobs,
-                       offsets, slots, active, mlist, nitems, xexp, hperm, out, T);
+                       offsets, slots, active, mlist, nitems, hexp, hperm, out, T);
     return hipGetLastError();
 }
 

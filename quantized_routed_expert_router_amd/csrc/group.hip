@@ -151,15 +151,14 @@ __global__ __launch_bounds__(GR_THREADS) void group_kernel(const int32_t *__rest
 }
 
 // The same grouping over many workgroups, for prefill-sized T (bitwise the
-// same outputs): 256-slot blocks count their experts in LDS
+// same outputs): 1024-slot blocks count their experts in LDS
 // (group_count_kernel); one workgroup turns the per-block counts into each
 // block's start inside every expert, the offsets and the active list
 // (group_scan_kernel); the blocks then place their slots stably -- rank among
 // equal experts inside a wave by ballots over the id bits, plus the earlier
 // waves' counts, plus the block's start and the expert's offset
 // (group_scatter_kernel).
-constexpr int GB_SLOTS = 256;   // slots per block
-constexpr int GS_BATCH = 40;    // per-block counts one scan thread loads at once (T = 2048: two rounds)
+constexpr int GS_BATCH = 40;    // per-block counts one scan thread loads at once (T = 2048: one round)
 
 __global__ __launch_bounds__(GB_SLOTS) void group_count_kernel(const int32_t *__restrict__ ids,
                                                                int N, int32_t *__restrict__ gcount)

@@ -41,12 +41,14 @@ __device__ inline uint16_t bf16_rn_bits(float v)
 }
 
 // The fp16 activations of the prefill GEMMs carry a per-token power-of-two
-// scale 2^k: k is chosen so that max |xhat_t| 2^k lies in [2^12, 2^13)
-// (k = 0 for an all-zero row, |k| <= 100), which keeps any input magnitude
-// inside fp16's normal range; xexp[t] = k lets the GEMM epilogues undo it
-// exactly.  For inputs whose rows peak in [4, 8) this is 2^10, and the
-// products and sums of the GEMMs are the unscaled ones times an exact power
-// of two.
+// scale 2^k, and the h the gate/up GEMM writes a second one, 2^hs.  A row
+// whose max |xhat_t| lies in [1, 8) (every RMSNorm'd row without a large
+// outlier, and unnormalised rows of unit-scale values) is stored unscaled:
+// k = hs = 0.  Any other row gets k with max |xhat_t| 2^k in [2^12, 2^13)
+// (|k| <= 100) and hs = 2 min(k - 10, 0) + 2 max(k - 12, 0), h growing as
+// x^2 (an all-zero row: k = hs = 0).  That keeps every input magnitude inside
+// fp16's normal range; xexp[t] = k in the low 16 bits, hs in the high 16
+// (both signed), lets the GEMM epilogues undo both exactly.
 constexpr int XEXP_TARGET = 13;
 constexpr int XEXP_MAX = 100;
 
@@ -103,9 +105,12 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
         mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
         int ex = 0;
         (void)frexpf(mx, &ex);   // mx in [2^(ex-1), 2^ex)
-        const int k = mx > 0.f ? min(max(XEXP_TARGET - ex, -XEXP_MAX), XEXP_MAX) : 0;
+        int k = mx > 0.f ? min(max(XEXP_TARGET - ex, -XEXP_MAX), XEXP_MAX) : 0;
+        int hs = 2 * min(k - 10, 0) + 2 * max(k - 12, 0);
+        if (mx == 0.f || (k >= 10 && k <= 12))
+            k = hs = 0;
         if (tid == 0)
-            xexp[t] = k;
+            xexp[t] = (int32_t)(((uint32_t)hs << 16) | ((uint32_t)k & 0xffffu));
         for (int pos = tid; pos < H; pos += PREP_THREADS)
             xperm[(size_t)t * H + pos] = __float2half_rn(ldexpf(xs[pg_col_of_pos(pos)], k));
     }

@@ -11,7 +11,7 @@ struct Ws {
     size_t status;     // i32 [1] (256 bytes reserved) status word, always at offset 0
     size_t xsplit;     // bf16 [Tp][3][H]    router input (prefill): x = x1 + x2 + x3 exactly
     size_t xperm;      // f16 [Tp][H]        MFMA-ordered activations (prefill), times 2^xexp
-    size_t xexp;       // i32 [Tp]           per-token power-of-two exponent of xperm
+    size_t xexp;       // i32 [Tp]           per-token power-of-two exponents of xperm (low 16 bits) and h (high)
     size_t logits;     // f32 [T][E]         logits (prefill) / raw logits (decode)
     size_t inv_rms;    // f32 [Td]
     size_t xq_dig;     // u32 [Td][40][32]   16-bit x, one 64-block per block column
@@ -29,10 +29,11 @@ struct Ws {
     size_t hq_scale;   // f32 [Td*K][40]
     size_t hq_sum;     // i32 [Td*K][40]
     size_t hperm;      // f16 [Tp*K][FF]     (grouped order)
+    size_t hexp;       // i32 [Tp*K]         the exponent h of each grouped row carries
     size_t out;        // f32 [T*K][H]
     size_t cdone;      // i32 [Td][H/32]      decode layer: finished slots per (token, 32 rows)
     size_t esync;      // i32 [1+32E]        decode experts: finished gate/up items per active expert (128-B apart)
-    size_t gcount;     // i32 [ceil(Tp*K/256)][E] prefill grouping: per-block expert counts / starts
+    size_t gcount;     // i32 [ceil(Tp*K/1024)][E] prefill grouping: per-block expert counts / starts
     size_t lraw2;      // f32 [Td][E]        lookahead: the next layer's raw logits
     size_t pred;       // i32 [Td*K]         lookahead: the next layer's predicted ids
     size_t x8;         // i8 [Tp][H]         int8 variant: activations per 64-block
@@ -84,10 +85,11 @@ constexpr Ws ws_layout(int T)
     L.hq_scale = take(Td * K * ns * 4);
     L.hq_sum = take(Td * K * ns * 4);
     L.hperm = take(Tp * K * FF * 2);
+    L.hexp = take(Tp * K * 4);
     L.out = take((size_t)T * K * H * 4);
     L.cdone = take(Td * (H / 32) * 4);
     L.esync = take(Td ? (size_t)(1 + 32 * E) * 4 : 0);
-    L.gcount = take((Tp * K + 255) / 256 * E * 4);
+    L.gcount = take((Tp * K + GB_SLOTS - 1) / GB_SLOTS * E * 4);
     L.lraw2 = take(Td * E * 4);
     L.pred = take(Td * K * 4);
     L.x8 = take(Tp * H);
