@@ -145,6 +145,40 @@ def test_input_magnitude(T, scale):
     hz.check(f"T={T} |x| x {scale:g}", ids, w, y, oids, ow, oy)
 
 
+def test_mixed_row_magnitudes_share_experts():
+    """Prefill rows of different magnitudes in one call, so that the items of
+    an expert hold rows with different exponents: token t is scaled by
+    (0.2, 1, 3, 0.5)[t % 4] (max |x| ~0.8, ~4, ~12, ~2: rows inside [1, 8)
+    stored unscaled, the others with their own power-of-two scales), no
+    RMSNorm.  Rows are redrawn until the scaled logits clear the near-tie
+    margin, and the test checks that the ten largest probabilities stay
+    far from fp32's subnormal range."""
+    T, seed = 256, 1777
+    st = inputs.Streams(seed)
+    R = inputs.draw_router(st.router)
+    scale = np.array([0.2, 1.0, 3.0, 0.5], np.float32)[np.arange(T) % 4][:, None]
+    x = (inputs.draw_x(st.x, T) * scale).astype(np.float32)
+    for _ in range(100):
+        gap = scr.top11_gap(scr.logits_np(x.astype(np.float64), R, None))
+        bad = np.nonzero(gap <= scr.TIE_MARGIN)[0]
+        if bad.size == 0:
+            break
+        for t in bad:
+            x[t] = (inputs.draw_x(st.x_redraw, 1)[0] * scale[t]).astype(np.float32)
+    else:
+        raise RuntimeError("near-tie screen did not converge")
+    lg = scr.logits_np(x.astype(np.float64), R, None)
+    top = np.sort(lg, axis=1)[:, -10:]
+    assert np.all(top[:, -1] - top[:, 0] < 60.0), "softmax tail near fp32 underflow"
+    mx = np.abs(x).max(axis=1)
+    assert mx[0::4].max() < 1.0 and mx[2::4].min() >= 8.0 and 1.0 <= mx[1::4].min()
+    _say(f"case: T={T} mixed row magnitudes, seed {seed}")
+    ids, w, y, _ = hz.gpu_layer(x, R, hz.store(seed))
+    oids, ow, oy = hz.oracle_rows(x, R, seed, np.arange(T))
+    assert np.all(np.isfinite(y))
+    hz.check(f"T={T} mixed row magnitudes", ids, w, y, oids, ow, oy)
+
+
 @pytest.mark.parametrize("T", [4, 100])
 def test_layer_equals_composition_and_is_deterministic(T):
     seed = 4000 + T
