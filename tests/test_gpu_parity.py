@@ -60,6 +60,27 @@ def test_decode_sizes(T):
     hz.check(f"decode T={T}", ids, w, y, oids, ow, oy)
 
 
+def test_decode_prefill_boundary_agree():
+    """The same 16 tokens through the decode arithmetic (T = 16: 16-bit
+    integer dot products) and the prefill arithmetic (T = 17, the 16 plus one
+    more token: fp16 MFMA).  Ids are identical, w agree to the w bar, and both
+    meet the oracle's bar, so their outputs agree within twice the y bar."""
+    seed = 1616
+    _say(f"case: decode T=16 vs prefill T=17 on the same tokens, seed {seed}")
+    x, R, _ = hz.single_layer_case(seed, 17)
+    blobs = hz.store(seed)
+    ids16, w16, y16, _ = hz.gpu_layer(x[:16].copy(), R, blobs)
+    ids17, w17, y17, _ = hz.gpu_layer(x, R, blobs)
+    oids, ow, oy = hz.oracle_rows(x, R, seed, np.arange(17))
+    hz.check("boundary T=16 (decode)", ids16, w16, y16, oids[:16], ow[:16], oy[:16])
+    hz.check("boundary T=17 (prefill)", ids17, w17, y17, oids, ow, oy)
+    assert np.array_equal(ids16, ids17[:16])
+    assert np.max(np.abs(w16 - w17[:16])) <= hz.W_TOL
+    d = np.max(np.abs(y16 - y17[:16])) / np.max(np.abs(oy[:16]))
+    _say(f"  decode vs prefill max|dy|/max|y| = {d:.2e}")
+    assert d <= 2 * hz.Y_TOL
+
+
 @pytest.mark.parametrize("T", [17, 64, 100, 257])
 def test_prefill_sizes(T):
     seed = 2000 + T
