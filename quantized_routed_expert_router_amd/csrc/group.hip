@@ -152,12 +152,7 @@ __global__ __launch_bounds__(GR_THREADS) void group_kernel(const int32_t *__rest
 
 // The same grouping over many workgroups, for prefill-sized T (bitwise the
 // same outputs): 1024-slot blocks count their experts in LDS
-// (group_count_kernel); one workgroup turns the per-block counts into each
-// block's start inside every expert, the offsets and the active list
-// (group_scan_kernel); the blocks then place their slots stably -- rank among
-// equal experts inside a wave by ballots over the id bits, plus the earlier
-// waves' counts, plus the block's start and the expert's offset
-// (group_scatter_kernel).
+// (group_count_kernel), then place their slots stably (group_place_kernel).
 constexpr int GS_BATCH = 40;    // per-block counts one scan thread loads at once (T = 2048: one round)
 
 __global__ __launch_bounds__(GB_SLOTS) void group_count_kernel(const int32_t *__restrict__ ids,
@@ -177,66 +172,69 @@ __global__ __launch_bounds__(GB_SLOTS) void group_count_kernel(const int32_t *__
         gcount[(size_t)b * E + i] = hist[i];
 }
 
-// With mlist given it also writes the prefill work list (as plan_kernel
-// does from offsets and active): expert e's chunks sit at the exclusive scan
-// of the chunk counts, which in ascending e is the active order.
-__global__ __launch_bounds__(E) void group_scan_kernel(int nb, int32_t *__restrict__ gcount,
-                                                       int32_t *__restrict__ offsets,
-                                                       int32_t *__restrict__ active, int max_items,
-                                                       int32_t *__restrict__ mlist,
-                                                       int32_t *__restrict__ nitems)
-{
-    __shared__ int tmp[8];
-    __shared__ int tot;
-    const int e = threadIdx.x;
-    int run = 0;   // expert e's slots in the blocks before b: block b's start
-    for (int b0 = 0; b0 < nb; b0 += GS_BATCH) {   // GS_BATCH counts in flight, then their starts
-        int c[GS_BATCH];
-#pragma unroll
-        for (int j = 0; j < GS_BATCH; ++j)
-            c[j] = b0 + j < nb ? gcount[(size_t)(b0 + j) * E + e] : 0;
-#pragma unroll
-        for (int j = 0; j < GS_BATCH; ++j) {
-            if (b0 + j < nb)
-                gcount[(size_t)(b0 + j) * E + e] = run;
-            run += c[j];
-        }
-    }
-    const int off = block_exclusive_scan_512(run, e, tmp, &tot);
-    offsets[e] = off;
-    if (e == 0)
-        offsets[E] = tot;
-    const int flag = run > 0 ? 1 : 0;
-    const int pos = block_exclusive_scan_512(flag, e, tmp, &tot);
-    if (flag)
-        active[1 + pos] = e;
-    if (e == 0)
-        active[0] = tot;
-    if (!mlist)
-        return;
-    const int nch = (run + PF_M - 1) / PF_M;
-    const int base = block_exclusive_scan_512(nch, e, tmp, &tot);
-    for (int c = 0; c < nch; ++c) {
-        const int it = base + c;
-        if (it < max_items) {
-            mlist[2 * it] = pos;
-            mlist[2 * it + 1] = c * PF_M;
-        }
-    }
-    if (e == 0)
-        nitems[0] = min(tot, max_items);
-}
-
-__global__ __launch_bounds__(GB_SLOTS) void group_scatter_kernel(const int32_t *__restrict__ ids,
-                                                                 int N,
-                                                                 const int32_t *__restrict__ gstart,
-                                                                 const int32_t *__restrict__ offsets,
-                                                                 int32_t *__restrict__ slots)
+// The blocks place their slots stably.  Each block first works out from the
+// per-block counts (threads e < E, one expert each) its own start inside
+// every expert's run and the expert totals, whose exclusive scan gives the
+// offsets -- every block does the same sums, so no separate scan launch is
+// needed; block 0 also writes the offsets, the active list and, with mlist
+// given, the prefill work list (expert e's chunks sit at the exclusive scan
+// of the chunk counts, which in ascending e is the active order).  Then each
+// slot's rank among equal experts inside its wave comes from ballots over the
+// id bits, plus the earlier waves' counts of that expert.
+__global__ __launch_bounds__(GB_SLOTS) void group_place_kernel(
+    const int32_t *__restrict__ ids, int N, int nb, const int32_t *__restrict__ gcount,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ active, int max_items,
+    int32_t *__restrict__ mlist, int32_t *__restrict__ nitems, int32_t *__restrict__ slots)
 {
     __shared__ int wc[GB_SLOTS / 64][E];   // per-wave counts of each expert
+    __shared__ int start[E];               // this block's first grouped position in expert e
+    __shared__ int tmp[8];
+    __shared__ int tot;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, b = blockIdx.x;
     for (int i = tid; i < (GB_SLOTS / 64) * E; i += GB_SLOTS)
         (&wc[0][0])[i] = 0;
+    int pre = 0, all = 0;   // expert tid's slots in the blocks before b, and in all
+    if (tid < E) {
+        for (int b0 = 0; b0 < nb; b0 += GS_BATCH) {   // GS_BATCH counts in flight
+            int c[GS_BATCH];
+#pragma unroll
+            for (int j = 0; j < GS_BATCH; ++j)
+                c[j] = b0 + j < nb ? gcount[(size_t)(b0 + j) * E + tid] : 0;
+#pragma unroll
+            for (int j = 0; j < GS_BATCH; ++j) {
+                pre += b0 + j < b ? c[j] : 0;
+                all += c[j];
+            }
+        }
+    }
+    const int off = block_exclusive_scan_512(all, tid, tmp, &tot);
+    if (tid < E)
+        start[tid] = off + pre;
+    if (b == 0) {   // uniform per block
+        if (tid < E)
+            offsets[tid] = off;
+        if (tid == 0)
+            offsets[E] = tot;
+        const int flag = tid < E && all > 0 ? 1 : 0;
+        const int pos = block_exclusive_scan_512(flag, tid, tmp, &tot);
+        if (flag)
+            active[1 + pos] = tid;
+        if (tid == 0)
+            active[0] = tot;
+        if (mlist) {
+            const int nch = tid < E ? (all + PF_M - 1) / PF_M : 0;
+            const int base = block_exclusive_scan_512(nch, tid, tmp, &tot);
+            for (int c = 0; c < nch; ++c) {
+                const int it = base + c;
+                if (it < max_items) {
+                    mlist[2 * it] = pos;
+                    mlist[2 * it + 1] = c * PF_M;
+                }
+            }
+            if (tid == 0)
+                nitems[0] = min(tot, max_items);
+        }
+    }
     const int s = b * GB_SLOTS + tid;
     const int v = s < N ? ids[s] : -1;
     const int e = (v >= 0 && v < E) ? v : -1;
@@ -249,7 +247,7 @@ __global__ __launch_bounds__(GB_SLOTS) void group_scatter_kernel(const int32_t *
         same &= ((e >> bit) & 1) ? bits : ~bits;
     }
     const int rank = __popcll(same & ((1ull << lane) - 1ull));
-    __syncthreads();   // the counts are zero
+    __syncthreads();   // the counts are zero; start is written
     if (e >= 0 && rank == 0)   // the first lane of each group records the group's size
         wc[wave][e] = __popcll(same);
     __syncthreads();
@@ -257,7 +255,7 @@ __global__ __launch_bounds__(GB_SLOTS) void group_scatter_kernel(const int32_t *
         int before = rank;
         for (int w = 0; w < wave; ++w)
             before += wc[w][e];
-        slots[offsets[e] + gstart[(size_t)b * E + e] + before] = s;
+        slots[start[e] + before] = s;
     }
 }
 
@@ -303,10 +301,8 @@ hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *sl
     }
     const int N = T * K, nb = (N + GB_SLOTS - 1) / GB_SLOTS;
     hipLaunchKernelGGL(group_count_kernel, dim3(nb), dim3(GB_SLOTS), 0, st, ids, N, gcount);
-    hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(E), 0, st, nb, gcount, offsets, active,
-                       max_items, mlist, nitems);
-    hipLaunchKernelGGL(group_scatter_kernel, dim3(nb), dim3(GB_SLOTS), 0, st, ids, N,
-                       (const int32_t *)gcount, (const int32_t *)offsets, slots);
+    hipLaunchKernelGGL(group_place_kernel, dim3(nb), dim3(GB_SLOTS), 0, st, ids, N, nb,
+                       (const int32_t *)gcount, offsets, active, max_items, mlist, nitems, slots);
     return hipGetLastError();
 }
 

@@ -52,22 +52,30 @@ __device__ inline uint16_t bf16_rn_bits(float v)
 constexpr int XEXP_TARGET = 13;
 constexpr int XEXP_MAX = 100;
 
+// Thread tid handles the column pairs (2 tid + 512 i, + 1), i = 0..4, so that
+// every load is 8 bytes and every store 4 (two bf16 or two fp16 values).
+constexpr int PREP_PAIRS = H / (2 * PREP_THREADS);   // 5
+static_assert(PREP_PAIRS * 2 * PREP_THREADS == H, "whole pairs");
+
+__device__ inline uint32_t pack16(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
+
 __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     const float *__restrict__ x, int rmsnorm, uint16_t *__restrict__ xsplit,
     __half *__restrict__ xperm, int32_t *__restrict__ xexp)
 {
-    __shared__ float xs[H];
+    __shared__ __attribute__((aligned(8))) float xs[H];
     __shared__ float wsum[PREP_THREADS / 64];
     __shared__ float wmax[PREP_THREADS / 64];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const float *xt = x + (size_t)t * H;
-    float v[H / PREP_THREADS];
+    float2 v[PREP_PAIRS];
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < H / PREP_THREADS; ++i) {
-        v[i] = xt[tid + PREP_THREADS * i];
-        ss = fmaf(v[i], v[i], ss);
+    for (int i = 0; i < PREP_PAIRS; ++i) {
+        v[i] = *reinterpret_cast<const float2 *>(xt + 2 * tid + 2 * PREP_THREADS * i);
+        ss = fmaf(v[i].x, v[i].x, ss);
+        ss = fmaf(v[i].y, v[i].y, ss);
     }
     float inv = 1.f;
     if (rmsnorm) {
@@ -80,21 +88,21 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
     }
     float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < H / PREP_THREADS; ++i) {
-        const float h = v[i] * inv;
-        mx = fmaxf(mx, fabsf(h));
-        const int c = tid + PREP_THREADS * i;
-        xs[c] = h;
+    for (int i = 0; i < PREP_PAIRS; ++i) {
+        const int c = 2 * tid + 2 * PREP_THREADS * i;
+        const float h0 = v[i].x * inv, h1 = v[i].y * inv;
+        mx = fmaxf(mx, fmaxf(fabsf(h0), fabsf(h1)));
+        *reinterpret_cast<float2 *>(xs + c) = make_float2(h0, h1);
         // the router's exact three-term bf16 split of xhat
-        const uint16_t b1 = bf16_rn_bits(h);
-        const float r1 = h - bf16_bits_to_float(b1);   // exact
-        const uint16_t b2 = bf16_rn_bits(r1);
-        const float r2 = r1 - bf16_bits_to_float(b2);  // exact
         if (xsplit) {
-            uint16_t *xo = xsplit + (size_t)t * 3 * H + c;
-            xo[0] = b1;
-            xo[H] = b2;
-            xo[2 * H] = bf16_rn_bits(r2);
+            const uint16_t a1 = bf16_rn_bits(h0), b1 = bf16_rn_bits(h1);
+            const float ra = h0 - bf16_bits_to_float(a1), rb = h1 - bf16_bits_to_float(b1);   // exact
+            const uint16_t a2 = bf16_rn_bits(ra), b2 = bf16_rn_bits(rb);
+            const float sa = ra - bf16_bits_to_float(a2), sb = rb - bf16_bits_to_float(b2);   // exact
+            uint32_t *xo = reinterpret_cast<uint32_t *>(xsplit + (size_t)t * 3 * H + c);
+            xo[0] = pack16(a1, b1);
+            xo[H / 2] = pack16(a2, b2);
+            xo[H] = pack16(bf16_rn_bits(sa), bf16_rn_bits(sb));
         }
     }
     mx = wave_max63(mx);
@@ -111,8 +119,15 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(
             k = hs = 0;
         if (tid == 0)
             xexp[t] = (int32_t)(((uint32_t)hs << 16) | ((uint32_t)k & 0xffffu));
-        for (int pos = tid; pos < H; pos += PREP_THREADS)
-            xperm[(size_t)t * H + pos] = __float2half_rn(ldexpf(xs[pg_col_of_pos(pos)], k));
+        // positions pos and pos + 1 (pos even) hold columns 8 apart
+#pragma unroll
+        for (int i = 0; i < PREP_PAIRS; ++i) {
+            const int pos = 2 * tid + 2 * PREP_THREADS * i;
+            const __half lo = __float2half_rn(ldexpf(xs[pg_col_of_pos(pos)], k));
+            const __half hi = __float2half_rn(ldexpf(xs[pg_col_of_pos(pos + 1)], k));
+            *reinterpret_cast<uint32_t *>(xperm + (size_t)t * H + pos) =
+                pack16(__half_as_ushort(lo), __half_as_ushort(hi));
+        }
     }
 }
 
