@@ -16,7 +16,7 @@ hipError_t launch_topk(const float *logits, int T, int32_t *ids, float *w, hipSt
 hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *slots,
                         int32_t *active, int32_t *gcount, int max_items, int32_t *mlist,
                         int32_t *nitems, hipStream_t st);
-hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_items,
+hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_items, int T,
                        int32_t *mlist, int32_t *nitems, hipStream_t st);
 hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const float *bias,
                                int rmsnorm, float *lraw, XQ xq, bool prep, int32_t *ids,
@@ -177,7 +177,7 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
                                          g_wait_limit.load(), e0, e1, st));
     } else {
         if (!planned)
-            STRATA_TRY(launch_plan(offsets, active, c.L.max_items, c.mlist, c.nitems, st));
+            STRATA_TRY(launch_plan(offsets, active, c.L.max_items, T, c.mlist, c.nitems, st));
         if (int8) {
             STRATA_TRY(launch_prefill_experts_i8(blobs, offsets, slots, active, c.mlist, c.nitems,
                                                  c.L.max_items, c.x8, c.xs8, c.xn8, c.h8, c.hs8,

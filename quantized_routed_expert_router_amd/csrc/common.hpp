@@ -44,6 +44,16 @@ constexpr int PF_NTILES_D = H / PF_NT_D;       // 10
 constexpr bool is_decode(int T) { return T <= DECODE_T_MAX; }
 
 constexpr int pf_max_items(int T) { return E + (T * K + PF_M - 1) / PF_M; }
+// A prefill work item, as the planners write it (four int32 per item):
+// rows gp0 .. gp0 + rows - 1 of the grouped order, all routed to expert e,
+// 1 <= rows <= PF_M.  The work list holds PF_LIST_PAD records more than items
+// so that every workgroup of a grid rounded up to the 8 XCDs can load its
+// record before it knows whether the record is in use.
+constexpr int PF_LIST_PAD = 8;
+__host__ __device__ inline bool pf_rec_ok(int e, int gp0, int rows, int T)
+{
+    return e >= 0 && e < E && rows > 0 && rows <= PF_M && gp0 >= 0 && gp0 <= T * K - rows;
+}
 
 // ---------------------------------------------------------------- device helpers
 __device__ inline float half_bits_to_float(uint32_t bits)

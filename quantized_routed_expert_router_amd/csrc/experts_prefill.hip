@@ -386,34 +386,23 @@ __device__ inline void pf_row_exps(const PfItem &it, int nt, const int32_t *__re
     }
 }
 
-__device__ inline PfItem pf_item(int item, const int32_t *mlist, const int32_t *nitems,
-                                 const int32_t *offsets, const int32_t *active, int T)
+// Work item `item` (rows of one expert, in grouped order) from the planner's
+// record; ok = 0 past the list's end or for a record that fails the checks.
+__device__ inline PfItem pf_item(int item, const int32_t *mlist, const int32_t *nitems, int T)
 {
     PfItem it{0, 0, 0, 0};
-    if (item >= nitems[0])
-        return it;
-    const int a = mlist[2 * item], m0 = mlist[2 * item + 1];
-    if (a < 0 || a >= active[0])
-        return it;
-    const int e = active[1 + a];
-    if (e < 0 || e >= E)
-        return it;
-    const int nslot = T * K;
-    const int beg = min(max(offsets[e], 0), nslot);
-    const int end = min(max(offsets[e + 1], beg), nslot);
-    const int rows = min(PF_M, end - beg - m0);
-    if (rows <= 0)
+    const int4 r = reinterpret_cast<const int4 *>(mlist)[item];   // padded: always in bounds
+    if (item >= nitems[0] || !pf_rec_ok(r.x, r.y, r.z, T))
         return it;
     it.ok = 1;
-    it.e = e;
-    it.gp0 = beg + m0;
-    it.rows = rows;
+    it.e = r.x;
+    it.gp0 = r.y;
+    it.rows = r.z;
     return it;
 }
 
 __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
-    const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ slots, const int32_t *__restrict__ active,
+    const uint8_t *__restrict__ blobs, const int32_t *__restrict__ slots,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
     const __half *__restrict__ xperm, const int32_t *__restrict__ xexp, __half *__restrict__ hperm,
     int32_t *__restrict__ hexp, int T)
@@ -423,7 +412,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int item = 8 * (idx / PF_NTILES_G) + xcd;
     const int nt = idx % PF_NTILES_G;
-    const PfItem it = pf_item(item, mlist, nitems, offsets, active, T);
+    const PfItem it = pf_item(item, mlist, nitems, T);
     if (!it.ok)
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -509,8 +498,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
 }
 
 __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
-    const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ slots, const int32_t *__restrict__ active,
+    const uint8_t *__restrict__ blobs, const int32_t *__restrict__ slots,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
     const int32_t *__restrict__ hexp, const __half *__restrict__ hperm, float *__restrict__ out,
     int T)
@@ -519,7 +507,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_down(
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int item = 8 * (idx / PF_NTILES_D) + xcd;
     const int nt = idx % PF_NTILES_D;
-    const PfItem it = pf_item(item, mlist, nitems, offsets, active, T);
+    const PfItem it = pf_item(item, mlist, nitems, T);
     if (!it.ok)
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -632,18 +620,17 @@ hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
     const int groups = (max_items + 7) / 8;
     const dim3 grid_g(8 * PF_NTILES_G * groups), block(PF_THREADS);
     if (ev0) {   // timed launch: the events carry the dispatch's own start and end
-        void *args[] = {&blobs, &offsets, &slots, &active, &mlist, &nitems, &xperm, &xexp, &hperm,
-                        &hexp, &T};
+        void *args[] = {&blobs, &slots, &mlist, &nitems, &xperm, &xexp, &hperm, &hexp, &T};
         const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&pf_gateup), grid_g,
                                                 block, args, 0, st, ev0, ev1, 0);
         if (e != hipSuccess)
             return e;
     } else {
-        hipLaunchKernelGGL(pf_gateup, grid_g, block, 0, st, blobs, offsets, slots, active, mlist,
-                           nitems, xperm, xexp, hperm, hexp, T);
+        hipLaunchKernelGGL(pf_gateup, grid_g, block, 0, st, blobs, slots, mlist, nitems, xperm,
+                           xexp, hperm, hexp, T);
     }
     hipLaunchKernelGGL(pf_down, dim3(8 * PF_NTILES_D * groups), dim3(PF_THREADS), 0, st, blobs,
-                       offsets, slots, active, mlist, nitems, hexp, hperm, out, T);
+                       slots, mlist, nitems, hexp, hperm, out, T);
     return hipGetLastError();
 }
 

@@ -100,28 +100,17 @@ struct PqItem {
     int ok, e, gp0, rows;
 };
 
-__device__ inline PqItem pq_item(int item, const int32_t *mlist, const int32_t *nitems,
-                                 const int32_t *offsets, const int32_t *active, int T)
+// Work item `item` from the planner's record (as the fp16 kernels read it).
+__device__ inline PqItem pq_item(int item, const int32_t *mlist, const int32_t *nitems, int T)
 {
     PqItem it{0, 0, 0, 0};
-    if (item >= nitems[0])
-        return it;
-    const int a = mlist[2 * item], m0 = mlist[2 * item + 1];
-    if (a < 0 || a >= active[0])
-        return it;
-    const int e = active[1 + a];
-    if (e < 0 || e >= E)
-        return it;
-    const int nslot = T * K;
-    const int beg = min(max(offsets[e], 0), nslot);
-    const int end = min(max(offsets[e + 1], beg), nslot);
-    const int rows = min(PF_M, end - beg - m0);
-    if (rows <= 0)
+    const int4 r = reinterpret_cast<const int4 *>(mlist)[item];   // padded: always in bounds
+    if (item >= nitems[0] || !pf_rec_ok(r.x, r.y, r.z, T))
         return it;
     it.ok = 1;
-    it.e = e;
-    it.gp0 = beg + m0;
-    it.rows = rows;
+    it.e = r.x;
+    it.gp0 = r.y;
+    it.rows = r.z;
     return it;
 }
 
@@ -208,8 +197,7 @@ __device__ inline void pq_gateup_group(const PqGLds &L, int wave, int q, int n, 
 }
 
 __global__ __launch_bounds__(PQ_THREADS) void pq_gateup(
-    const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ slots, const int32_t *__restrict__ active,
+    const uint8_t *__restrict__ blobs, const int32_t *__restrict__ slots,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
     const int8_t *__restrict__ x8, const float *__restrict__ xs8, const int32_t *__restrict__ xn8,
     int8_t *__restrict__ h8, float *__restrict__ hs8, int32_t *__restrict__ hn8, int T)
@@ -218,7 +206,7 @@ __global__ __launch_bounds__(PQ_THREADS) void pq_gateup(
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int item = 8 * (idx / PQ_NTILES_G) + xcd;
     const int nt = idx % PQ_NTILES_G;
-    const PqItem it = pq_item(item, mlist, nitems, offsets, active, T);
+    const PqItem it = pq_item(item, mlist, nitems, T);
     if (!it.ok)
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -375,8 +363,7 @@ __device__ inline void pq_down_group(const PqDLds &L, int wave, int q, int n, f3
 }
 
 __global__ __launch_bounds__(PQ_THREADS) void pq_down(
-    const uint8_t *__restrict__ blobs, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ slots, const int32_t *__restrict__ active,
+    const uint8_t *__restrict__ blobs, const int32_t *__restrict__ slots,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
     const int8_t *__restrict__ h8, const float *__restrict__ hs8, const int32_t *__restrict__ hn8,
     float *__restrict__ out, int T)
@@ -385,7 +372,7 @@ __global__ __launch_bounds__(PQ_THREADS) void pq_down(
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int item = 8 * (idx / PQ_NTILES_D) + xcd;
     const int nt = idx % PQ_NTILES_D;
-    const PqItem it = pq_item(item, mlist, nitems, offsets, active, T);
+    const PqItem it = pq_item(item, mlist, nitems, T);
     if (!it.ok)
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -488,18 +475,17 @@ hipError_t launch_prefill_experts_i8(const uint8_t *blobs, const int32_t *offset
     const int groups = (max_items + 7) / 8;
     const dim3 grid_g(8 * PQ_NTILES_G * groups), block(PQ_THREADS);
     if (ev0) {   // timed launch: the events carry the dispatch's own start and end
-        void *args[] = {&blobs, &offsets, &slots, &active, &mlist, &nitems, &x8,
-                        &xs8,   &xn8,     &h8,    &hs8,    &hn8,   &T};
+        void *args[] = {&blobs, &slots, &mlist, &nitems, &x8, &xs8, &xn8, &h8, &hs8, &hn8, &T};
         const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&pq_gateup), grid_g,
                                                 block, args, 0, st, ev0, ev1, 0);
         if (e != hipSuccess)
             return e;
     } else {
-        hipLaunchKernelGGL(pq_gateup, grid_g, block, 0, st, blobs, offsets, slots, active, mlist,
-                           nitems, x8, xs8, xn8, h8, hs8, hn8, T);
+        hipLaunchKernelGGL(pq_gateup, grid_g, block, 0, st, blobs, slots, mlist, nitems, x8, xs8,
+                           xn8, h8, hs8, hn8, T);
     }
-    hipLaunchKernelGGL(pq_down, dim3(8 * PQ_NTILES_D * groups), block, 0, st, blobs, offsets,
-                       slots, active, mlist, nitems, h8, hs8, hn8, out, T);
+    hipLaunchKernelGGL(pq_down, dim3(8 * PQ_NTILES_D * groups), block, 0, st, blobs, slots,
+                       mlist, nitems, h8, hs8, hn8, out, T);
     return hipGetLastError();
 }
 

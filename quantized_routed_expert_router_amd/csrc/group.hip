@@ -226,10 +226,9 @@ __global__ __launch_bounds__(GB_SLOTS) void group_place_kernel(
             const int base = block_exclusive_scan_512(nch, tid, tmp, &tot);
             for (int c = 0; c < nch; ++c) {
                 const int it = base + c;
-                if (it < max_items) {
-                    mlist[2 * it] = pos;
-                    mlist[2 * it + 1] = c * PF_M;
-                }
+                if (it < max_items)
+                    reinterpret_cast<int4 *>(mlist)[it] =
+                        make_int4(tid, off + c * PF_M, min(PF_M, all - c * PF_M), 0);
             }
             if (tid == 0)
                 nitems[0] = min(tot, max_items);
@@ -259,32 +258,34 @@ __global__ __launch_bounds__(GB_SLOTS) void group_place_kernel(
     }
 }
 
-// Prefill work list: one item per (active expert, 64-token chunk), in active
-// order; nitems[0] = item count.
+// Prefill work list from a caller's grouping: one record {e, gp0, rows} per
+// (active expert, 64-row chunk), in active order; offsets are clamped to the
+// slots as the grouping allows (an active entry out of range adds nothing);
+// nitems[0] = item count.
 __global__ __launch_bounds__(512) void plan_kernel(const int32_t *__restrict__ offsets,
                                                    const int32_t *__restrict__ active,
-                                                   int max_items, int32_t *__restrict__ mlist,
+                                                   int max_items, int nslot,
+                                                   int32_t *__restrict__ mlist,
                                                    int32_t *__restrict__ nitems)
 {
     __shared__ int tmp[8];
     __shared__ int tot;
     const int tid = threadIdx.x;
     const int na = active[0];
-    int nch = 0;
+    int nch = 0, e = 0, beg = 0, n = 0;
     if (tid < na) {
-        const int e = active[1 + tid];
+        e = active[1 + tid];
         if (e >= 0 && e < E) {
-            const int n = offsets[e + 1] - offsets[e];
-            nch = n > 0 ? (n + PF_M - 1) / PF_M : 0;
+            beg = min(max(offsets[e], 0), nslot);
+            n = min(max(offsets[e + 1], beg), nslot) - beg;
+            nch = (n + PF_M - 1) / PF_M;
         }
     }
     const int base = block_exclusive_scan_512(nch, tid, tmp, &tot);
     for (int c = 0; c < nch; ++c) {
         const int it = base + c;
-        if (it < max_items) {
-            mlist[2 * it] = tid;
-            mlist[2 * it + 1] = c * PF_M;
-        }
+        if (it < max_items)
+            reinterpret_cast<int4 *>(mlist)[it] = make_int4(e, beg + c * PF_M, min(PF_M, n - c * PF_M), 0);
     }
     if (tid == 0)
         nitems[0] = min(tot, max_items);
@@ -306,11 +307,11 @@ hipError_t launch_group(const int32_t *ids, int T, int32_t *offsets, int32_t *sl
     return hipGetLastError();
 }
 
-hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_items,
+hipError_t launch_plan(const int32_t *offsets, const int32_t *active, int max_items, int T,
                        int32_t *mlist, int32_t *nitems, hipStream_t st)
 {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(512), 0, st, offsets, active, max_items, mlist,
-                       nitems);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(512), 0, st, offsets, active, max_items, T * K,
+                       mlist, nitems);
     return hipGetLastError();
 }
 

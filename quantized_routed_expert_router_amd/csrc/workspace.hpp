@@ -23,7 +23,7 @@ struct Ws {
     size_t erec;       // i32x4 [1+E]        decode work records (header + one per active expert)
     size_t ids;        // i32 [T*K]
     size_t w;          // f32 [T*K]
-    size_t mlist;      // i32 [2][max items]
+    size_t mlist;      // i32 [max items + 8][4]  prefill work items {e, gp0, rows, 0}
     size_t nitems;     // i32 [4]
     size_t hq_dig;     // u32 [Td*K][10][32] 16-bit h per 16 values (64-value blocks)
     size_t hq_scale;   // f32 [Td*K][40]
@@ -79,7 +79,7 @@ constexpr Ws ws_layout(int T)
     L.ids = take((size_t)T * K * 4);
     L.w = take((size_t)T * K * 4);
     L.max_items = pf_max_items(T);
-    L.mlist = take((size_t)2 * L.max_items * 4);
+    L.mlist = take((size_t)4 * (L.max_items + PF_LIST_PAD) * 4);
     L.nitems = take(16);
     L.hq_dig = take(Td * K * (FF / QK) * 32 * 4);
     L.hq_scale = take(Td * K * ns * 4);
