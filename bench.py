@@ -21,7 +21,13 @@ replayed on one stream (single layers: one graph of exactly that many steps;
 stacks: one graph per step, replayed step by step), bracketed by device
 synchronisation; ms_per_step = the steps' event-timed total / steps.  Every
 graph is uploaded to the device (hipGraphUpload) after capture, so no timed
-replay includes that one-time transfer.  The
+replay includes that one-time transfer.  Before the warmup steps the
+workload runs untimed for --settle-ms of wall time (default 300; 0 turns it
+off; the value is in the JSON line): on a fresh GPU the first tens of
+milliseconds of this work run slower -- a T = 2048 prefill step 526 us
+against 447 us once settled, with the same kernels -- and the timed steps
+are meant to see the settled GPU a serving loop runs on.  A stack's residual
+input is restored after the settling.  The
 dominant kernel of a workload is timed live with HIP events attached to its
 own dispatch (strata_moe_time_next_kernel) over eager calls of the same
 steps: its mean duration prices the roofline object.
@@ -106,6 +112,8 @@ def parse():
     ap.add_argument("--cpu-seconds-also", type=float, default=6.0,
                     help="oracle time of each other workload's cpu_baseline")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graphs")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed wall-clock milliseconds of the workload before the warmup steps")
     ap.add_argument("--copies", type=int, default=0,
                     help="store copies cycled by single-layer workloads (default: the workload's; "
                          "1 keeps the layer's experts in cache between steps, a diagnostic)")
@@ -246,6 +254,19 @@ def measure(name, a, cpu_seconds):
             else:
                 graphs[key].replay()
 
+    if a.settle_ms > 0:   # untimed, before the warmup steps (see the module docstring)
+        key = "step" if stack else ("warmup" if a.warmup else "steps")
+        t_s = time.perf_counter()
+        while (time.perf_counter() - t_s) * 1e3 < a.settle_ms:
+            with torch.cuda.stream(stream):
+                if a.eager:
+                    one_step(0, stream=stream)
+                else:
+                    graphs[key].replay()
+            torch.cuda.synchronize()
+        if stack:
+            xd.copy_(x0)
+            torch.cuda.synchronize()
     run(a.warmup, "warmup", 0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -334,7 +355,7 @@ def measure(name, a, cpu_seconds):
                                f"512 Q2_0 experts, top-10",
                    "global_batch": T, "seq_len": T if prefill else 1,
                    "timing": "eager" if a.eager else "hipGraph replay",
-                   "store_copies": copies},
+                   "settle_ms": a.settle_ms, "store_copies": copies},
         "tok_per_s": tok_s, "layer_ms": ms / L, "distinct_experts": distinct,
         "expert_bytes_per_step": step_bytes, "wall_s": wall,
         "roofline": roof,
