@@ -64,6 +64,7 @@ extern "C" {
 #define STRATA_E_WORKSPACE (-3) /* workspace missing or smaller than required */
 #define STRATA_E_HIP (-4)       /* the HIP runtime reported a launch error */
 #define STRATA_E_ALIGN (-5)     /* a pointer breaks the alignment rule above */
+#define STRATA_E_CORRUPT (-6)   /* strata_moe_verify_blobs: a blob differs from its checksum */
 
 /* Bits of a workspace's status word (see strata_moe_read_status). */
 #define STRATA_STATUS_WAIT_TIMEOUT 1 /* a decode experts wait gave up: outputs of that call are NaN */
@@ -243,6 +244,39 @@ STRATA_API int strata_moe_clear_status(void *ws, size_t ws_bytes, void *stream);
  * thread.  Meant for tests of the failure path (a bound of 1 makes most waits
  * give up at once, so every kernel still ends). */
 STRATA_API int strata_moe_set_wait_limit(int polls);
+
+/* Blob-store integrity ([ZW], the passage on how the design differs from
+ * static offload, third point: every cache slot is read back after it is
+ * filled and a mismatch refuses to run).  Here the whole store sits in HBM,
+ * filled once, and each blob gets a 64-bit checksum:
+ *   checksum = sum over the blob's little-endian 64-bit words w_j
+ *              (j = 0 .. STRATA_MOE_BLOB / 8 - 1) of
+ *              mix(w_j + (j + 1) * 0x9E3779B97F4A7C15) mod 2^64,
+ * mix being SplitMix64's output function (z ^= z >> 30; z *= 0xBF58476D1CE4E5B9;
+ * z ^= z >> 27; z *= 0x94D049BB133111EB; z ^= z >> 31).
+ *
+ * strata_moe_blob_checksums: enqueues the checksums of nblobs consecutive
+ * device blobs (blobs 256-byte aligned, nblobs * STRATA_MOE_BLOB bytes) into
+ * sums [nblobs] (device, 8-byte aligned).  Capturable.  STRATA_E_SHAPE for
+ * nblobs outside 1..STRATA_MOE_CHECK_BLOBS_MAX.
+ *
+ * strata_moe_blob_checksum_host: the checksum of one blob in HOST memory
+ * (STRATA_MOE_BLOB bytes), computed on the CPU, for the expected values of a
+ * store at load time; 0 for a NULL pointer.
+ *
+ * strata_moe_verify_blobs: the checksums of nblobs device blobs (into the
+ * caller's device scratch sums [nblobs]) compared with expected [nblobs] in
+ * HOST memory.  Synchronises `stream` (a load-time check, not for graph
+ * capture).  Returns STRATA_OK with *first_bad = -1, or STRATA_E_CORRUPT with
+ * *first_bad (host) the lowest index whose checksum differs; the argument
+ * errors of strata_moe_blob_checksums, or STRATA_E_HIP. */
+#define STRATA_MOE_CHECK_BLOBS_MAX (1 << 24)
+STRATA_API int strata_moe_blob_checksums(const uint8_t *blobs, int64_t nblobs, uint64_t *sums,
+                                         void *stream);
+STRATA_API uint64_t strata_moe_blob_checksum_host(const uint8_t *blob);
+STRATA_API int strata_moe_verify_blobs(const uint8_t *blobs, int64_t nblobs,
+                                       const uint64_t *expected, uint64_t *sums,
+                                       int64_t *first_bad, void *stream);
 
 /* Human-readable text of a status code (static storage). */
 STRATA_API const char *strata_moe_status_string(int status);

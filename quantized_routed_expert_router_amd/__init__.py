@@ -18,13 +18,15 @@ BLOB = 1382400
 T_MAX = 8192
 LOOKAHEAD_T_MAX = 8
 RMSNORM, RESIDUAL, INT8 = 1, 2, 4
-OK, E_ARG, E_SHAPE, E_WORKSPACE, E_HIP, E_ALIGN = 0, -1, -2, -3, -4, -5
+OK, E_ARG, E_SHAPE, E_WORKSPACE, E_HIP, E_ALIGN, E_CORRUPT = 0, -1, -2, -3, -4, -5, -6
+CHECK_BLOBS_MAX = 1 << 24
 
 EXPORTS = ("strata_moe_blob_bytes", "strata_moe_workspace_bytes", "strata_moe_route",
            "strata_moe_group", "strata_moe_experts", "strata_moe_combine", "strata_moe_layer",
            "strata_moe_layer_lookahead", "strata_moe_time_next_kernel",
            "strata_moe_read_status", "strata_moe_clear_status", "strata_moe_set_wait_limit",
-           "strata_moe_layer_static", "strata_moe_status_string")
+           "strata_moe_layer_static", "strata_moe_status_string", "strata_moe_blob_checksums",
+           "strata_moe_blob_checksum_host", "strata_moe_verify_blobs")
 STATIC_T_MAX = 64
 STATUS_WAIT_TIMEOUT = 1
 
@@ -75,6 +77,13 @@ def lib():
         L.strata_moe_set_wait_limit.argtypes = [i32]
         L.strata_moe_status_string.restype = ctypes.c_char_p
         L.strata_moe_status_string.argtypes = [i32]
+        i64, u64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)
+        L.strata_moe_blob_checksums.restype = i32
+        L.strata_moe_blob_checksums.argtypes = [vp, i64, vp, vp]
+        L.strata_moe_blob_checksum_host.restype = ctypes.c_uint64
+        L.strata_moe_blob_checksum_host.argtypes = [vp]
+        L.strata_moe_verify_blobs.restype = i32
+        L.strata_moe_verify_blobs.argtypes = [vp, i64, u64p, vp, ctypes.POINTER(i64), vp]
         _lib = L
     return _lib
 
@@ -206,6 +215,64 @@ def strata_moe_clear_status(ws, stream=None):
 def strata_moe_set_wait_limit(polls):
     """Bound of the decode experts kernel's wait (0 restores the default)."""
     _check("strata_moe_set_wait_limit", lib().strata_moe_set_wait_limit(int(polls)))
+
+
+def _blob_count(blobs, nblobs):
+    """Check that the uint8 device tensor `blobs` holds nblobs blobs."""
+    import torch
+    if blobs is None or blobs.dtype != torch.uint8:
+        raise TypeError("blobs must be a uint8 tensor")
+    nblobs = int(nblobs)
+    if nblobs < 1 or nblobs > CHECK_BLOBS_MAX:
+        raise ValueError(f"nblobs must be in 1..{CHECK_BLOBS_MAX}, got {nblobs}")
+    if blobs.numel() < nblobs * BLOB:
+        raise ValueError(f"blobs holds {blobs.numel()} bytes, fewer than {nblobs} blobs")
+    return nblobs
+
+
+def strata_moe_blob_checksums(blobs, nblobs, sums, stream=None):
+    """Enqueue the 64-bit checksum of each of the first nblobs blobs of the
+    device store `blobs` into the int64 device tensor sums [nblobs] (bit
+    patterns of the uint64 checksums)."""
+    import torch
+    n = _blob_count(blobs, nblobs)
+    if sums.dtype != torch.int64:
+        raise TypeError("sums must be an int64 tensor (uint64 bit patterns)")
+    _min_numel("sums", sums, n)
+    _check("strata_moe_blob_checksums",
+           lib().strata_moe_blob_checksums(_p(blobs), n, _p(sums), _s(stream)))
+
+
+def strata_moe_blob_checksum_host(blob):
+    """Checksum of one blob in host memory (a numpy uint8 array of BLOB bytes)."""
+    import numpy as np
+    b = np.ascontiguousarray(blob, dtype=np.uint8)
+    if b.size != BLOB:
+        raise ValueError(f"a blob is {BLOB} bytes, got {b.size}")
+    return int(lib().strata_moe_blob_checksum_host(b.ctypes.data))
+
+
+def strata_moe_verify_blobs(blobs, nblobs, expected, sums, stream=None):
+    """Synchronously compare the first nblobs device blobs with `expected`
+    (host numpy uint64 [nblobs]); sums is device scratch (int64 [nblobs]).
+    Returns -1 if every checksum matches, else the first differing index
+    (the C call returned STRATA_E_CORRUPT); raises on any other error."""
+    import numpy as np
+    import torch
+    n = _blob_count(blobs, nblobs)
+    ex = np.ascontiguousarray(expected, dtype=np.uint64)
+    if ex.size < n:
+        raise ValueError(f"expected holds {ex.size} checksums, fewer than {n}")
+    if sums.dtype != torch.int64:
+        raise TypeError("sums must be an int64 tensor (uint64 bit patterns)")
+    _min_numel("sums", sums, n)
+    first = ctypes.c_int64(-2)
+    rc = lib().strata_moe_verify_blobs(_p(blobs), n, ex.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                       _p(sums), ctypes.byref(first), _s(stream))
+    if rc == E_CORRUPT:
+        return int(first.value)
+    _check("strata_moe_verify_blobs", rc)
+    return -1
 
 
 def strata_moe_route(x, router, ids, w, ws, bias=None, flags=0, stream=None):

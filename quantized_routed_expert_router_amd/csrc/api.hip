@@ -492,6 +492,8 @@ const char *strata_moe_status_string(int status)
         return "HIP launch error";
     case STRATA_E_ALIGN:
         return "pointer alignment violated";
+    case STRATA_E_CORRUPT:
+        return "a blob differs from its expected checksum";
     default:
         return "unknown status";
     }

@@ -31,7 +31,7 @@ def m():
 
 def test_exports_every_declared_symbol(m):
     names = declared()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     assert set(names) == set(m.EXPORTS)
     for n in names:
         assert hasattr(m.lib(), n), n
