@@ -21,8 +21,10 @@
  *  - Arguments are validated on the host before anything is enqueued: a call
  *    that returns an error enqueued nothing.  No call synchronises the host,
  *    reads device memory from the host, or uses memset, so calls may be
- *    captured into a HIP graph.  Device faults surface at the caller's next
- *    synchronisation.
+ *    captured into a HIP graph -- except strata_moe_read_status and
+ *    strata_moe_verify_blobs, a diagnostic and a load-time check that
+ *    synchronise their stream and say so below.  Device faults surface at
+ *    the caller's next synchronisation.
  *  - Results are deterministic: the same inputs and T give the same bits
  *    (no floating-point atomics anywhere).
  *  - Alignment: `blobs` and `ws` 256 bytes; x, y, out and router 16 bytes;
