@@ -128,7 +128,10 @@ __device__ inline void store_h(uint32_t *p, uint32_t v)
 }
 
 // Wave 0: h = silu(g) * u of one token's 16 FF rows from the partial sums
-// part [DG_WAVES][DG_ROWS], quantised and stored as segment seg of slot.
+// part [DG_WAVES][DG_ROWS], quantised and stored as segment seg of slot (at
+// agent scope when the down part of the same launch reads it, FUSED; plain
+// stores when a later launch does).
+template <bool FUSED>
 __device__ inline void emit_h(const float (*part)[DG_ROWS], int slot, int seg, const HQ &hq)
 {
     const int lane = threadIdx.x & 63;
@@ -141,17 +144,30 @@ __device__ inline void emit_h(const float (*part)[DG_ROWS], int slot, int seg, c
         uint32_t *blk = hq.dig + ((size_t)slot * HBLK + (seg >> 2)) * BLK_DWORDS;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            store_h(blk + dig_pos(8 * (seg & 3) + 4 * (lane - 12) + i), qo.pk[i]);
+        {
+            if (FUSED)
+                store_h(blk + dig_pos(8 * (seg & 3) + 4 * (lane - 12) + i), qo.pk[i]);
+            else
+                blk[dig_pos(8 * (seg & 3) + 4 * (lane - 12) + i)] = qo.pk[i];
+        }
     }
     if (lane == 0) {
-        store_h(reinterpret_cast<uint32_t *>(hq.scale) + (size_t)slot * HSEG16 + seg,
-                __float_as_uint(qo.scale));
-        store_h(reinterpret_cast<uint32_t *>(hq.nsum) + (size_t)slot * HSEG16 + seg,
-                (uint32_t)(-qo.sum));
+        if (FUSED) {
+            store_h(reinterpret_cast<uint32_t *>(hq.scale) + (size_t)slot * HSEG16 + seg,
+                    __float_as_uint(qo.scale));
+            store_h(reinterpret_cast<uint32_t *>(hq.nsum) + (size_t)slot * HSEG16 + seg,
+                    (uint32_t)(-qo.sum));
+        } else {
+            hq.scale[(size_t)slot * HSEG16 + seg] = qo.scale;
+            hq.nsum[(size_t)slot * HSEG16 + seg] = -qo.sum;
+        }
     }
 }
 
 // One gate/up item: LDS wl [DG_ROWS][DG_RS] dwords and part [2 DG_WAVES][DG_ROWS].
+// FUSED: h at agent scope and the item counted in gdone for the down groups of
+// the same launch.
+template <bool FUSED>
 __device__ void gateup_item(int item, const uint8_t *__restrict__ blobs,
                             const int4 *__restrict__ erec, const int32_t *__restrict__ slots,
                             const XQ &xq, const HQ &hq, int T, uint32_t *wl,
@@ -266,12 +282,12 @@ __device__ void gateup_item(int item, const uint8_t *__restrict__ blobs,
         __syncthreads();
         if (wave == 0) {
             if (slot >= 0 && slot < nslot)   // only a corrupt grouping fails this
-                emit_h(part, slot, seg, hq);
+                emit_h<FUSED>(part, slot, seg, hq);
             if (two && slot2 >= 0 && slot2 < nslot)
-                emit_h(part + DG_WAVES, slot2, seg, hq);
+                emit_h<FUSED>(part + DG_WAVES, slot2, seg, hq);
         }
     }
-    if (wave == 0) {   // every h value of the item is in memory: count the item
+    if (FUSED && wave == 0) {   // every h value of the item is in memory: count the item
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (lane == 0)
@@ -302,6 +318,17 @@ template <class V> __device__ inline V load_h(const V *p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// FUSED: agent-scope loads (h written in the same launch); else plain ones.
+template <bool FUSED> __device__ inline unsigned long long ld_h(const unsigned long long *p)
+{
+    if (FUSED)
+        return load_h(p);
+    return *p;
+}
+template <bool FUSED> __device__ inline float ld_h(const float *p) { return FUSED ? load_h(p) : *p; }
+template <bool FUSED> __device__ inline int32_t ld_h(const int32_t *p) { return FUSED ? load_h(p) : *p; }
+
+template <bool FUSED = true>
 __device__ inline HOps load_hops(const HQ &hq, int slot, int c0, int l)
 {
     HOps o;
@@ -309,16 +336,16 @@ __device__ inline HOps load_hops(const HQ &hq, int slot, int c0, int l)
         reinterpret_cast<const unsigned long long *>(hq.dig + (size_t)slot * HBLK * BLK_DWORDS) + l;
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
-        const unsigned long long v = load_h(dp + 16 * (2 * j + c0));
+        const unsigned long long v = ld_h<FUSED>(dp + 16 * (2 * j + c0));
         o.d[j] = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
     }
     const int seg0 = 4 * (2 * (l >> 2) + c0) + (l & 3);   // index l: j = l / 4, k = l % 4
     const int seg1 = 4 * (2 * 4 + c0) + (l & 3);          // index 16 + l (l < 4): j = 4
     const size_t sb = (size_t)slot * HSEG16;
-    o.sh0 = load_h(hq.scale + sb + seg0);
-    o.nq0 = load_h(hq.nsum + sb + seg0);
-    o.sh1 = l < 4 ? load_h(hq.scale + sb + seg1) : 0.f;
-    o.nq1 = l < 4 ? load_h(hq.nsum + sb + seg1) : 0;
+    o.sh0 = ld_h<FUSED>(hq.scale + sb + seg0);
+    o.nq0 = ld_h<FUSED>(hq.nsum + sb + seg0);
+    o.sh1 = l < 4 ? ld_h<FUSED>(hq.scale + sb + seg1) : 0.f;
+    o.nq1 = l < 4 ? ld_h<FUSED>(hq.nsum + sb + seg1) : 0;
     return o;
 }
 
@@ -635,7 +662,7 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
         uint32_t *wl = reinterpret_cast<uint32_t *>(lds);
         float(*part)[DG_ROWS] =
             reinterpret_cast<float(*)[DG_ROWS]>(lds + (size_t)DG_ROWS * DG_RS * 4);
-        gateup_item(b, blobs, erec, slots, xq, hq, T, wl, part, gdone);
+        gateup_item<true>(b, blobs, erec, slots, xq, hq, T, wl, part, gdone);
     } else if (b < amax * (DG_SEGS + EX_DN_PER_E)) {
         const int g = b - amax * DG_SEGS;
         if (g >= na * EX_DN_PER_E)
@@ -649,17 +676,167 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
     }
 }
 
+// ------------------------------------------------------- T = 1: two launches
+// For a single token the layer runs the experts as two launches in stream
+// order instead (the kernel boundary publishes h, so nothing waits inside a
+// kernel): dec_gateup runs the gate/up items above (plain stores of h, no
+// counters) and the lookahead workgroups; dec_down has one workgroup per 16
+// output rows of the token, 5 waves with two of its slots each, lane (r, l)
+// taking row l of slot 2 w + r % 2's expert and block columns 2 j + r / 2 from
+// five 20-byte windows loaded straight into registers.  The two halves of
+// each row are added, the ten slot rows meet in LDS and are summed in routing
+// order with fma from 0, the order of the fused combine, so a token's results
+// are bitwise those of the fused kernel.  Measured faster at T = 1 only (the
+// fused kernel's down groups read an expert's rows once for all the tokens
+// that share it).
+constexpr int DS_T_MAX = 1;                         // layer calls with T <= this split
+constexpr int DS_ROWS = 16;                         // output rows per workgroup
+constexpr int DS_WAVES = K / 2;                     // 5: two slots per wave
+constexpr int DS_THREADS = 64 * DS_WAVES;
+constexpr int DS_CHUNKS_PER_T = H / DS_ROWS;        // 160
+constexpr size_t DS_LDS_GU = (size_t)DG_ROWS * DG_RS * 4 + (size_t)2 * DG_WAVES * DG_ROWS * 4;
+
+// A lane's down weights: five 20-byte windows of its row (window j holds block
+// column 2 j + c0, starting 2 bytes in when c0 = 1).
+struct DnW {
+    uint4 lo[5];
+    uint32_t hi[5];
+};
+
+__device__ inline void dn_request(const uint8_t *__restrict__ blobs, int e, int row, int c0, DnW &w)
+{
+    const uint8_t *p = blobs + (size_t)e * BLOB + 2 * MAT + (size_t)row * ROW_D + 16 * c0;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        w.lo[j] = *reinterpret_cast<const uint4 *>(p + 36 * j);
+        w.hi[j] = *reinterpret_cast<const uint32_t *>(p + 36 * j + 16);
+    }
+}
+
+// down_block on a window held in registers (the same arithmetic).
+template <int N>
+__device__ inline float down_block_r(const uint4 lo, uint32_t v4, uint32_t sel, uint32_t sh, uint2 D,
+                                     float shr, int nqr)
+{
+    const uint32_t v0 = lo.x, v1 = lo.y, v2 = lo.z, v3 = lo.w;
+    const Codes c = split_codes(__builtin_amdgcn_perm(v1, v0, sel), __builtin_amdgcn_perm(v2, v1, sel),
+                                __builtin_amdgcn_perm(v3, v2, sel), __builtin_amdgcn_perm(v4, v3, sel));
+    const float d = half_bits_to_float(v0 >> sh);
+    const Quad qd = quarters_codes_dot(c, D.x, D.y);
+    float bacc = 0.f;
+    const float f0 = (float)(qd.q[0] + row_bcast_i<N>(nqr));
+    STRATA_FMA_BCAST(bacc, shr, f0, N);
+    const float f1 = (float)(qd.q[1] + row_bcast_i<N + 1>(nqr));
+    STRATA_FMA_BCAST(bacc, shr, f1, N + 1);
+    const float f2 = (float)(qd.q[2] + row_bcast_i<N + 2>(nqr));
+    STRATA_FMA_BCAST(bacc, shr, f2, N + 2);
+    const float f3 = (float)(qd.q[3] + row_bcast_i<N + 3>(nqr));
+    STRATA_FMA_BCAST(bacc, shr, f3, N + 3);
+    return d * bacc;
+}
+
+// down_row on register windows (the same blocks in the same order).
+__device__ inline float down_row_r(const DnW &w, int c0, const HOps &ho)
+{
+    const uint32_t sel = c0 ? 0x07060504u : 0x05040302u;
+    const uint32_t sh = c0 ? 16u : 0u;
+    float acc = down_block_r<0>(w.lo[0], w.hi[0], sel, sh, ho.d[0], ho.sh0, ho.nq0);
+    acc += down_block_r<4>(w.lo[1], w.hi[1], sel, sh, ho.d[1], ho.sh0, ho.nq0);
+    acc += down_block_r<8>(w.lo[2], w.hi[2], sel, sh, ho.d[2], ho.sh0, ho.nq0);
+    acc += down_block_r<12>(w.lo[3], w.hi[3], sel, sh, ho.d[3], ho.sh0, ho.nq0);
+    acc += down_block_r<0>(w.lo[4], w.hi[4], sel, sh, ho.d[4], ho.sh1, ho.nq1);
+    return acc;
+}
+
+// Workgroup b < 40 amax runs gate/up item b (items beyond the call's na
+// active experts exit at once); the lookahead workgroups follow.
+__global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restrict__ blobs,
+                                                         const int4 *__restrict__ erec,
+                                                         const int32_t *__restrict__ slots, XQ xq,
+                                                         HQ hq, int T,
+                                                         const int32_t *__restrict__ pred,
+                                                         const uint8_t *__restrict__ blobs_next)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[DS_LDS_GU];
+    const int na = active_count(erec, T);
+    const int amax = T * K < E ? T * K : E;
+    const int b = blockIdx.x;
+    if (b < amax * DG_SEGS) {
+        if (b >= na * DG_SEGS)
+            return;
+        uint32_t *wl = reinterpret_cast<uint32_t *>(lds);
+        float(*part)[DG_ROWS] =
+            reinterpret_cast<float(*)[DG_ROWS]>(lds + (size_t)DG_ROWS * DG_RS * 4);
+        gateup_item<false>(b, blobs, erec, slots, xq, hq, T, wl, part, nullptr);
+    } else {
+        touch_next(b - amax * DG_SEGS, T * K, pred, blobs_next);
+    }
+}
+
+// Workgroup b: token b / 160, output rows 16 (b % 160) .. + 15.  sexp[t K + k]
+// is the expert of slot (t, k) (a slot whose expert is outside 0..E-1 gives
+// zero rows).  y_t = sum_k w[t][k] o_k, stored and/or added to res.
+__global__ __launch_bounds__(DS_THREADS) void dec_down(const uint8_t *__restrict__ blobs,
+                                                       const int32_t *__restrict__ sexp, HQ hq,
+                                                       const float *__restrict__ w, float *y,
+                                                       float *res)
+{
+    __shared__ float orow[K][DS_ROWS];
+    const int t = blockIdx.x / DS_CHUNKS_PER_T, ch = blockIdx.x % DS_CHUNKS_PER_T;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane >> 4, l = lane & 15;
+    const int k = 2 * wave + (r & 1), c0 = r >> 1;
+    const int slot = t * K + k;
+    const int row = ch * DS_ROWS + l;
+    const int e = sexp[slot];
+    const bool ok = e >= 0 && e < E;
+    DnW dw;
+    dn_request(blobs, ok ? e : 0, row, c0, dw);
+    const HOps ho = load_hops<false>(hq, slot, c0, l);
+    float acc = down_row_r(dw, c0, ho);
+    acc += __shfl_xor(acc, 32, 64);   // the row's two halves
+    if (!ok)
+        acc = 0.f;
+    if (lane < 32)
+        orow[k][l] = acc;
+    __syncthreads();
+    if (threadIdx.x < DS_ROWS) {
+        float sum = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk)
+            sum = fmaf(w[(size_t)t * K + kk], orow[kk][threadIdx.x], sum);
+        const size_t at = (size_t)t * H + ch * DS_ROWS + threadIdx.x;
+        if (y)
+            y[at] = sum;
+        if (res)
+            res[at] += sum;
+    }
+}
+
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,
                                  XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
                                  const float *w, float *y, float *res, const int32_t *pred,
                                  const uint8_t *blobs_next, int32_t *status, int wait_limit,
-                                 hipEvent_t ev0, hipEvent_t ev1, hipStream_t st)
+                                 const int32_t *sexp, hipEvent_t ev0, hipEvent_t ev1,
+                                 hipStream_t st)
 {
     Combine cb{cdone, w, y, res};
     const int amax = T * K < E ? T * K : E;
     int32_t *gdone = sync + 1;
     if (!blobs_next)
         pred = nullptr;
+    if (sexp && cdone && T <= DS_T_MAX) {   // a layer call for one token: two launches
+        const dim3 grid(amax * DG_SEGS + (pred ? T * K * XT_PER_SLOT : 0));
+        void *args[] = {&blobs, &erec, &slots, &xq, &hq, &T, &pred, &blobs_next};
+        hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_gateup), grid,
+                                          dim3(DG_THREADS), args, 0, st, ev0, nullptr, 0);
+        if (e != hipSuccess)
+            return e;
+        void *dargs[] = {&blobs, &sexp, &hq, &w, &y, &res};
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_down),
+                                  dim3(T * DS_CHUNKS_PER_T), dim3(DS_THREADS), dargs, 0, st,
+                                  nullptr, ev1, 0);
+    }
     const dim3 grid(amax * (DG_SEGS + EX_DN_PER_E) + (pred ? T * K * XT_PER_SLOT : 0));
     const dim3 block(EX_THREADS);
     if (ev0) {   // timed launch: the events carry the dispatch's own start and end

@@ -1,7 +1,9 @@
 """The decode experts kernel's bounded wait: when it gives up, the outputs that
 depended on it are NaN and the workspace's status word says so; a normal call
 leaves the word clear.  The give-up is forced from the host with a wait bound
-of one poll (strata_moe_set_wait_limit), so every kernel still ends normally."""
+of one poll (strata_moe_set_wait_limit), so every kernel still ends normally.
+A one-token layer call runs its experts as two launches with no wait at all:
+the bound changes nothing there."""
 import numpy as np
 import pytest
 
@@ -22,7 +24,7 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [2, 4])
 def test_wait_give_up_poisons_outputs_and_sets_status(T):
     m = hz.qm()
     seed = 9100 + T
@@ -54,6 +56,24 @@ def test_wait_give_up_poisons_outputs_and_sets_status(T):
     ids3, w3, y3, _ = hz.gpu_layer(x, R, st, ws=ws)
     assert m.strata_moe_read_status(ws) == 0
     assert np.array_equal(y2, y0) and np.array_equal(y3, y0)
+
+
+def test_one_token_layer_has_no_wait():
+    m = hz.qm()
+    seed, T = 9101, 1
+    print("case: wait bound of one poll, layer T=1 (two launches)", flush=True)
+    x, R, _ = hz.single_layer_case(seed, T)
+    st = hz.store(seed)
+    ws = m.workspace(T)
+    ids0, w0, y0, _ = hz.gpu_layer(x, R, st, ws=ws)
+    m.strata_moe_set_wait_limit(1)
+    try:
+        ids1, w1, y1, _ = hz.gpu_layer(x, R, st, ws=ws)
+    finally:
+        m.strata_moe_set_wait_limit(0)
+    assert m.strata_moe_read_status(ws) == 0
+    assert np.array_equal(ids1, ids0) and np.array_equal(w1, w0) and np.array_equal(y1, y0)
+    assert np.all(np.isfinite(y1))
 
 
 def test_wait_give_up_in_the_experts_entry_point():
