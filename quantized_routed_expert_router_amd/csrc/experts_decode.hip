@@ -676,9 +676,9 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
     }
 }
 
-// ------------------------------------------------------- T = 1: two launches
-// For a single token the layer runs the experts as two launches in stream
-// order instead (the kernel boundary publishes h, so nothing waits inside a
+// ------------------------------------------------- T <= 3: two launches
+// For one to three tokens the layer runs the experts as two launches in
+// stream order instead (the kernel boundary publishes h, so nothing waits inside a
 // kernel): dec_gateup runs the gate/up items above (plain stores of h, no
 // counters) and the lookahead workgroups; dec_down has one workgroup per 16
 // output rows of the token, 5 waves with two of its slots each, lane (r, l)
@@ -686,10 +686,12 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
 // five 20-byte windows loaded straight into registers.  The two halves of
 // each row are added, the ten slot rows meet in LDS and are summed in routing
 // order with fma from 0, the order of the fused combine, so a token's results
-// are bitwise those of the fused kernel.  Measured faster at T = 1 only (the
-// fused kernel's down groups read an expert's rows once for all the tokens
-// that share it).
-constexpr int DS_T_MAX = 1;                         // layer calls with T <= this split
+// are bitwise those of the fused kernel.  Measured faster up to T = 3, with
+// or without experts shared by the window's tokens; at T = 4 the fused kernel
+// is faster for tokens that share few experts (its down groups read an
+// expert's rows once for all the tokens that share it; here each token reads
+// its own).
+constexpr int DS_T_MAX = 3;                         // layer calls with T <= this split
 constexpr int DS_ROWS = 16;                         // output rows per workgroup
 constexpr int DS_WAVES = K / 2;                     // 5: two slots per wave
 constexpr int DS_THREADS = 64 * DS_WAVES;
@@ -825,7 +827,7 @@ hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const i
     int32_t *gdone = sync + 1;
     if (!blobs_next)
         pred = nullptr;
-    if (sexp && cdone && T <= DS_T_MAX) {   // a layer call for one token: two launches
+    if (sexp && cdone && T <= DS_T_MAX) {   // a layer call for up to 3 tokens: two launches
         const dim3 grid(amax * DG_SEGS + (pred ? T * K * XT_PER_SLOT : 0));
         void *args[] = {&blobs, &erec, &slots, &xq, &hq, &T, &pred, &blobs_next};
         hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_gateup), grid,
