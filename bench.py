@@ -322,10 +322,12 @@ def measure(name, a, cpu_seconds):
         roof = {"bound": "hbm", "achieved": k_work / (k_ms / 1e3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    # A layer of up to 3 tokens runs its experts as dec_gateup then dec_down;
-    # the events then span both dispatches (the experts stage, all of its
-    # weight bytes).
+    # A layer of up to 3 tokens runs its experts as two launches, gate/up then
+    # dec_down; the events span both dispatches (the experts stage, all of its
+    # weight bytes).  For one token (no lookahead) the gate/up launch,
+    # dec_route_gateup, also routes the token, so the span includes that.
     roof["kernel"] = (("pq_gateup" if int8 else "pf_gateup") if prefill
+                      else "dec_route_gateup+dec_down" if T == 1 and not lookahead
                       else "dec_gateup+dec_down" if T <= 3 else "dec_experts")
     # HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or null
     roof["traffic"] = traffic_from_profile(roof["kernel"], name)

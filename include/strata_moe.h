@@ -170,8 +170,9 @@ STRATA_API int strata_moe_layer(float *x, int T, const uint16_t *router, const f
  * warm-up: the next layer's router is run on this layer's MoE input, because
  * the residual stream changes little between adjacent layers, to predict the
  * next layer's experts and warm their bytes without changing any result).
- * Does exactly what strata_moe_layer does with the first nine arguments, with
- * bitwise the same outputs, and in the same launches:
+ * Does what strata_moe_layer does with the first nine arguments, with
+ * bitwise the same outputs (for T = 1 through the top-k launch that the plain
+ * call folds into its gate/up launch), and also:
  *  - routes the same normalised input through router_next [E][H] bf16 (plus
  *    bias_next [E] fp32, or NULL) to that layer's ten ids per token, written
  *    to pred_ids [T][K] int32 (or kept in the workspace when NULL);
@@ -213,8 +214,11 @@ STRATA_API int strata_moe_layer_static(float *x, int T, const uint16_t *router, 
  * (hipEvent_t) attached to the dispatch itself (hipExtLaunchKernel), so that
  * hipEventElapsedTime(start, stop) is that kernel's own duration.  The kernel
  * is, for decode-sized T, the fused experts kernel (gate/up, down and, in the
- * layer call, the combine), and for larger T the gate/up GEMM.  The hook is
- * used by one call and disarmed.  Events are the caller's; pass both NULL to
+ * layer call, the combine), and for larger T the gate/up GEMM.  A layer call
+ * of 1..3 tokens runs its experts as two launches (gate/up, then down with the
+ * combine); there `start` is on the first and `stop` on the second, and for
+ * one token without the lookahead the first launch also routes the token.
+ * The hook is used by one call and disarmed.  Events are the caller's; pass both NULL to
  * disarm.  Returns STRATA_E_ARG if only one is NULL.  Not for use under graph
  * capture. */
 STRATA_API int strata_moe_time_next_kernel(void *start, void *stop);

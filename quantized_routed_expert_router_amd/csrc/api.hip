@@ -23,6 +23,11 @@ hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const f
                                float *w, int group, int32_t *slots, int4 *erec, int32_t *cdone,
                                int32_t *esync, const uint16_t *R2, const float *bias2,
                                float *lraw2, int32_t *pred, hipStream_t st);
+hipError_t launch_router_gemv(const float *x, int T, const uint16_t *R, int rmsnorm, float *lraw,
+                              XQ xq, hipStream_t st);
+hipError_t launch_decode_t1(const uint8_t *blobs, const float *lraw, const float *bias, XQ xq,
+                            HQ hq, int32_t *ids, float *w, float *y, float *res, hipEvent_t ev0,
+                            hipEvent_t ev1, hipStream_t st);
 hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const int32_t *offsets,
                               const int32_t *slots, const int32_t *active, int4 *erec,
                               int32_t *esync, hipStream_t st);
@@ -236,6 +241,14 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
     float *w_o = w ? w : c.w;
     int32_t *pred_o = pred ? pred : c.pred;
     const int rms = flags & STRATA_RMSNORM;
+    if (T == 1 && !router2) {   // one token: the gate/up launch routes it
+        STRATA_TRY(launch_router_gemv(x, T, router, rms, c.logits, c.xq, st));
+        hipEvent_t e0, e1;
+        take_events(e0, e1);
+        STRATA_TRY(launch_decode_t1(blobs, c.logits, bias, c.xq, c.hq, ids_o, w_o, y,
+                                    (flags & STRATA_RESIDUAL) ? x : nullptr, e0, e1, st));
+        return STRATA_OK;
+    }
     if (is_decode(T)) {
         STRATA_TRY(launch_route_decode(x, T, router, bias, rms, c.logits, c.xq, true, ids_o, w_o, 1,
                                        c.slots, c.erec, c.cdone, c.esync, router2, bias2, c.lraw2,

@@ -37,6 +37,7 @@
 // depend on the other tokens of the call.
 #include "common.hpp"
 #include "quant.hpp"
+#include "route_token.hpp"
 #include <hip/hip_ext.h>
 
 namespace strata {
@@ -164,22 +165,21 @@ __device__ inline void emit_h(const float (*part)[DG_ROWS], int slot, int seg, c
     }
 }
 
-// One gate/up item: LDS wl [DG_ROWS][DG_RS] dwords and part [2 DG_WAVES][DG_ROWS].
-// FUSED: h at agent scope and the item counted in gdone for the down groups of
-// the same launch.
+// One gate/up item, segment seg (FF rows 16 seg .. + 15) of the active
+// expert with record rec = {expert, first grouped slot, token count, first
+// slot}: LDS wl [DG_ROWS][DG_RS] dwords and part [2 DG_WAVES][DG_ROWS].
+// FUSED: h at agent scope and the item counted in gdone[SYNC_STRIDE a] for the
+// down groups of the same launch.
 template <bool FUSED>
-__device__ void gateup_item(int item, const uint8_t *__restrict__ blobs,
-                            const int4 *__restrict__ erec, const int32_t *__restrict__ slots,
-                            const XQ &xq, const HQ &hq, int T, uint32_t *wl,
-                            float (*part)[DG_ROWS], int32_t *gdone)
+__device__ void gateup_item(int4 rec, int seg, int a, const uint8_t *__restrict__ blobs,
+                            const int32_t *__restrict__ slots, const XQ &xq, const HQ &hq, int T,
+                            uint32_t *wl, float (*part)[DG_ROWS], int32_t *gdone)
 {
     const int nslot = T * K;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane >> 4, l = lane & 15;
     const int s = 2 * wave + (r >> 1);                 // column stream: columns 5s .. 5s+4
-    const int4 rec = erec[1 + item / DG_SEGS];
-    const int seg = item % DG_SEGS;
     int slot = rec.w;
     // token 0's operands are in flight with the weights
     XOps xo = load_xops(xq, slot >= 0 && slot < nslot ? slot / K : 0, s, l);
@@ -291,7 +291,7 @@ __device__ void gateup_item(int item, const uint8_t *__restrict__ blobs,
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (lane == 0)
-            __hip_atomic_fetch_add(gdone + SYNC_STRIDE * (item / DG_SEGS), 1, __ATOMIC_RELAXED,
+            __hip_atomic_fetch_add(gdone + SYNC_STRIDE * a, 1, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -662,7 +662,8 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
         uint32_t *wl = reinterpret_cast<uint32_t *>(lds);
         float(*part)[DG_ROWS] =
             reinterpret_cast<float(*)[DG_ROWS]>(lds + (size_t)DG_ROWS * DG_RS * 4);
-        gateup_item<true>(b, blobs, erec, slots, xq, hq, T, wl, part, gdone);
+        gateup_item<true>(erec[1 + b / DG_SEGS], b % DG_SEGS, b / DG_SEGS, blobs, slots, xq, hq, T,
+                          wl, part, gdone);
     } else if (b < amax * (DG_SEGS + EX_DN_PER_E)) {
         const int g = b - amax * DG_SEGS;
         if (g >= na * EX_DN_PER_E)
@@ -769,7 +770,8 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restri
         uint32_t *wl = reinterpret_cast<uint32_t *>(lds);
         float(*part)[DG_ROWS] =
             reinterpret_cast<float(*)[DG_ROWS]>(lds + (size_t)DG_ROWS * DG_RS * 4);
-        gateup_item<false>(b, blobs, erec, slots, xq, hq, T, wl, part, nullptr);
+        gateup_item<false>(erec[1 + b / DG_SEGS], b % DG_SEGS, 0, blobs, slots, xq, hq, T, wl,
+                           part, nullptr);
     } else {
         touch_next(b - amax * DG_SEGS, T * K, pred, blobs_next);
     }
@@ -813,6 +815,66 @@ __global__ __launch_bounds__(DS_THREADS) void dec_down(const uint8_t *__restrict
         if (res)
             res[at] += sum;
     }
+}
+
+// ------------------------------------------ T = 1: the routing in every item
+// A layer call for one token (without the lookahead) has no top-k launch:
+// wave 0 of every gate/up workgroup routes the token itself from the router's
+// logits -- the top-k kernel's code on the same inputs, so every workgroup
+// gets the same ten ids and weights, bitwise -- and the workgroup takes head
+// k = its index / 40: the k-th expert, segment index % 40.  One token's ten
+// experts are distinct, so there is nothing to group.  Workgroup 0 writes the
+// ids and weights, which the down launch (dec_down, above) and the caller read.
+__global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(const uint8_t *__restrict__ blobs,
+                                                               const float *__restrict__ lraw,
+                                                               const float *__restrict__ bias,
+                                                               XQ xq, HQ hq,
+                                                               int32_t *__restrict__ ids,
+                                                               float *__restrict__ wout)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[DS_LDS_GU];
+    __shared__ int head_e;
+    const int k = blockIdx.x / DG_SEGS, seg = blockIdx.x % DG_SEGS;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int my_id;
+        float my_p, sel;
+        route_token(lraw, xq.inv_rms[0], bias, my_id, my_p, sel);
+        // read lane k with every lane of the wave active: inside a branch on
+        // the lane the compiler may take my_id to be that lane's own value
+        const int he = __builtin_amdgcn_readlane(my_id, k);
+        if (blockIdx.x == 0 && lane < K) {
+            ids[lane] = my_id;
+            wout[lane] = my_p / renorm_den(sel);
+        }
+        if (lane == 0)
+            head_e = he;
+    }
+    __syncthreads();
+    const int e = head_e;
+    if (e < 0 || e >= E)   // not reached: the ten heads are expert ids
+        return;
+    uint32_t *wl = reinterpret_cast<uint32_t *>(lds);
+    float(*part)[DG_ROWS] = reinterpret_cast<float(*)[DG_ROWS]>(lds + (size_t)DG_ROWS * DG_RS * 4);
+    gateup_item<false>(make_int4(e, 0, 1, k), seg, 0, blobs, nullptr, xq, hq, 1, wl, part,
+                       nullptr);
+}
+
+hipError_t launch_decode_t1(const uint8_t *blobs, const float *lraw, const float *bias, XQ xq,
+                            HQ hq, int32_t *ids, float *w, float *y, float *res, hipEvent_t ev0,
+                            hipEvent_t ev1, hipStream_t st)
+{
+    void *args[] = {&blobs, &lraw, &bias, &xq, &hq, &ids, &w};
+    hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_route_gateup),
+                                      dim3(K * DG_SEGS), dim3(DG_THREADS), args, 0, st, ev0,
+                                      nullptr, 0);
+    if (e != hipSuccess)
+        return e;
+    const int32_t *sexp = ids;
+    const float *wc = w;
+    void *dargs[] = {&blobs, &sexp, &hq, &wc, &y, &res};
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_down), dim3(DS_CHUNKS_PER_T),
+                              dim3(DS_THREADS), dargs, 0, st, nullptr, ev1, 0);
 }
 
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,

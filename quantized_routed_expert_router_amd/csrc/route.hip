@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     int my_id;
     float my_p, sel_sum;
     route_token(logits + (size_t)t * E, 1.f, nullptr, my_id, my_p, sel_sum);
-    const float den = fmaxf(sel_sum, 6.103515625e-05f);   // clamp 2^-14
+    const float den = renorm_den(sel_sum);
     if (lane < K) {
         ids[(size_t)t * K + lane] = my_id;
         wout[(size_t)t * K + lane] = my_p / den;

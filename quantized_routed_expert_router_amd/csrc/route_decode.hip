@@ -307,7 +307,7 @@ __global__ __launch_bounds__(RT_THREADS) void rdec_topk(
         int my_id;
         float my_p, sel;
         route_token(lraw + (size_t)t * E, inv_rms[t], bias, my_id, my_p, sel);
-        const float den = fmaxf(sel, 6.103515625e-05f);   // clamp 2^-14
+        const float den = renorm_den(sel);
         if (lane < K) {
             ids[(size_t)t * K + lane] = my_id;
             wout[(size_t)t * K + lane] = my_p / den;
@@ -354,6 +354,17 @@ hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const f
     hipLaunchKernelGGL(rdec_topk, dim3(1), dim3(RT_THREADS), 0, st, lraw, xq.inv_rms, bias, T, ids,
                        w, group, slots, erec, cdone, esync, R2 ? lraw2 : nullptr, bias2,
                        R2 ? pred : nullptr);
+    return hipGetLastError();
+}
+
+// The router GEMV alone (with the 16-bit quantisation of x): the one-token
+// layer call routes inside its gate/up launch.
+hipError_t launch_router_gemv(const float *x, int T, const uint16_t *R, int rmsnorm, float *lraw,
+                              XQ xq, hipStream_t st)
+{
+    const GroupIn none{nullptr, nullptr, nullptr, nullptr, nullptr};
+    hipLaunchKernelGGL((rdec_gemv<true, true>), dim3(E), dim3(RG_THREADS), 0, st, x, T, R, lraw,
+                       xq, rmsnorm, none, (const uint16_t *)nullptr, (float *)nullptr);
     return hipGetLastError();
 }
 

@@ -37,6 +37,10 @@ __device__ inline int wave_max_i(int v)
     return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Denominator of the renormalised routing weights: the sum of the ten
+// selected probabilities, clamped below at 2^-14 (w_k = p_k / den).
+__device__ inline float renorm_den(float sel) { return fmaxf(sel, 6.103515625e-05f); }
+
 // One token's routing in one wave: softmax over the 512 logits
 // lrow * sc (+ bias), then the ten (p desc, id asc) heads in order.  Lane k
 // < K gets the k-th id and its p; sel (uniform) is the sum of the ten p.
