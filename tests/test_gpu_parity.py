@@ -200,7 +200,7 @@ def test_mixed_row_magnitudes_share_experts():
     hz.check(f"T={T} mixed row magnitudes", ids, w, y, oids, ow, oy)
 
 
-@pytest.mark.parametrize("T", [4, 100])
+@pytest.mark.parametrize("T", [1, 2, 4, 100])
 def test_layer_equals_composition_and_is_deterministic(T):
     seed = 4000 + T
     _say(f"case: layer vs composition T={T}")
@@ -227,7 +227,7 @@ def test_decode_batch_invariance():
         assert np.array_equal(y1[0], y[t]), t
 
 
-@pytest.mark.parametrize("T", [4, 64])
+@pytest.mark.parametrize("T", [1, 4, 64])
 def test_timing_hook_records_and_leaves_results_alone(T):
     """strata_moe_time_next_kernel: the armed call records both events around
     one kernel (positive elapsed time), gives bitwise the unarmed results, and
