@@ -30,7 +30,10 @@ are meant to see the settled GPU a serving loop runs on.  A stack's residual
 input is restored after the settling.  The
 dominant kernel of a workload is timed live with HIP events attached to its
 own dispatch (strata_moe_time_next_kernel) over eager calls of the same
-steps: its mean duration prices the roofline object.
+steps: its mean duration prices the roofline object.  Each such call is
+preceded by a spin kernel of ~80 us on the stream, so that the call's launches
+are queued before the GPU reaches them, as in a graph replay; otherwise the
+host's own launch gaps would fall inside a two-launch span.
 
 Prints one JSON line.  With --gpus > 1 it exits: the measurement is of one GPU.
 """
@@ -61,6 +64,8 @@ WORKLOADS = {
     "prefill-i8": dict(wl="layer-T2048-prefill", T=2048, layers=1, copies=4, int8=True),
     "stack-prefill": dict(wl="stack48-T32768-zipf", T=2048, layers=48, copies=1),
 }
+# cycles of the spin kernel ahead of each event-timed call (~80 us)
+SPIN_CYCLES = 200_000
 # measured beside the headline in a default run
 ALSO = ("token", "prefill", "prefill-i8", "stack-decode", "stack-prefill")
 
@@ -293,6 +298,7 @@ def measure(name, a, cpu_seconds):
             for i in range(L if stack else copies):
                 ev0 = torch.cuda.Event(enable_timing=True)
                 ev1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(SPIN_CYCLES)   # the call's launches queue behind it
                 ev0.record(stream)
                 ev1.record(stream)
                 m.strata_moe_time_next_kernel(ev0, ev1)
