@@ -1,5 +1,6 @@
 // route_token.hpp -- one token's routing in one wave, shared by the decode
-// top-k (route_decode.hip) and the prefill top-k (route.hip): the fused
+// top-k (route_decode.hip), the prefill top-k (route.hip) and the one-token
+// gate/up launch (experts_decode.hip), so all of them rank alike: the fused
 // 512-expert softmax, stable descending order and the first ten heads ("MoE
 // 遇上消费级显卡..." (zwxr.cn), the passage following one token through a
 // layer).  Device code only.
