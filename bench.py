@@ -190,13 +190,15 @@ def measure(name, a, cpu_seconds):
 
     def layer_call(l, i, ids_o, stream):
         """Layer l (store copy i for single layers); with the lookahead, layers
-        0 .. L-2 also predict layer l+1's experts and warm its blobs."""
+        0 .. L-2 also predict layer l+1's experts and warm its blobs, and take
+        the previous layer's prediction as their hint."""
         sto = store[i * per_layer:(i + 1) * per_layer]
         if lookahead and l + 1 < L:
             m.strata_moe_layer_lookahead(
                 xd, Rd[i], sto, ws, Rd[i + 1], store[(i + 1) * per_layer:(i + 2) * per_layer],
                 bias=None if bd is None else bd[l], bias_next=None if bd is None else bd[l + 1],
-                flags=flags, y=y, ids=ids_o, w=w, pred=pred_t[l], stream=stream)
+                flags=flags, y=y, ids=ids_o, w=w, pred=pred_t[l],
+                hint=pred_t[l - 1] if l > 0 else None, stream=stream)
         else:
             m.strata_moe_layer(xd, Rd[i], sto, ws, bias=None if bd is None else bd[l],
                                flags=flags, y=y, ids=ids_o, w=w, stream=stream)
@@ -330,10 +332,10 @@ def measure(name, a, cpu_seconds):
     roof["frac"] = roof["achieved"] / roof["peak"]
     # A layer of up to 3 tokens runs its experts as two launches, gate/up then
     # dec_down; the events span both dispatches (the experts stage, all of its
-    # weight bytes).  For one token (no lookahead) the gate/up launch,
-    # dec_route_gateup, also routes the token, so the span includes that.
+    # weight bytes).  For one token the gate/up launch, dec_route_gateup, also
+    # routes the token, so the span includes that.
     roof["kernel"] = (("pq_gateup" if int8 else "pf_gateup") if prefill
-                      else "dec_route_gateup+dec_down" if T == 1 and not lookahead
+                      else "dec_route_gateup+dec_down" if T == 1
                       else "dec_gateup+dec_down" if T <= 3 else "dec_experts")
     # HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or null
     roof["traffic"] = traffic_from_profile(roof["kernel"], name)

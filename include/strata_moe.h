@@ -171,22 +171,31 @@ STRATA_API int strata_moe_layer(float *x, int T, const uint16_t *router, const f
  * the residual stream changes little between adjacent layers, to predict the
  * next layer's experts and warm their bytes without changing any result).
  * Does what strata_moe_layer does with the first nine arguments, with
- * bitwise the same outputs (for T = 1 through the top-k launch that the plain
- * call folds into its gate/up launch), and also:
+ * bitwise the same outputs, and also:
  *  - routes the same normalised input through router_next [E][H] bf16 (plus
  *    bias_next [E] fp32, or NULL) to that layer's ten ids per token, written
  *    to pred_ids [T][K] int32 (or kept in the workspace when NULL);
  *  - reads the predicted experts' blobs in blobs_next (the next layer's store,
- *    [E][BLOB], 256-byte aligned) once, line by line, in the experts kernel's
- *    tail, so that they sit in the memory-side cache when the next layer runs.
- * Nothing is written to blobs_next and no result depends on it.
+ *    [E][BLOB], 256-byte aligned) once, line by line, in the experts
+ *    launch's tail, so that they sit in the memory-side cache when the next
+ *    layer runs;
+ *  - for T = 1, takes hint_ids [1][K] int32 (device memory, or NULL): the ids
+ *    this token is expected to route to, normally the previous lookahead
+ *    call's pred_ids.  The gate/up rows of the hinted experts are requested
+ *    before the token's own routing has finished, and used for the heads
+ *    whose expert they are; heads no hint names are read after the routing.
+ *    Any values are allowed (ids outside 0..E-1 and repeats are ignored).
+ *    Ignored for T > 1.
+ * Nothing is written to blobs_next, and no result depends on blobs_next or
+ * on hint_ids.
  * T must be 1..STRATA_LOOKAHEAD_T_MAX (decode); other T return STRATA_E_SHAPE.
  * router_next and blobs_next must not be NULL (STRATA_E_ARG). */
 STRATA_API int strata_moe_layer_lookahead(float *x, int T, const uint16_t *router,
                                const float *bias, const uint8_t *blobs, int flags, float *y,
                                int32_t *ids, float *w, const uint16_t *router_next,
                                const float *bias_next, const uint8_t *blobs_next,
-                               int32_t *pred_ids, void *ws, size_t ws_bytes, void *stream);
+                               int32_t *pred_ids, const int32_t *hint_ids, void *ws,
+                               size_t ws_bytes, void *stream);
 
 /* strata_moe_layer for callers that cannot allocate (code under HIP graph
  * capture, serving loops or harnesses that forbid hipMalloc): the same

@@ -64,7 +64,7 @@ def lib():
         L.strata_moe_layer.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         L.strata_moe_layer_lookahead.restype = i32
         L.strata_moe_layer_lookahead.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
-                                                 vp, vp, sz, vp]
+                                                 vp, vp, vp, sz, vp]
         L.strata_moe_time_next_kernel.restype = i32
         L.strata_moe_time_next_kernel.argtypes = [vp, vp]
         L.strata_moe_layer_static.restype = i32
@@ -385,7 +385,7 @@ def strata_moe_layer_static(x, router, blobs, bias=None, flags=0, y=None, ids=No
 
 def strata_moe_layer_lookahead(x, router, blobs, ws, router_next, blobs_next, bias=None,
                                bias_next=None, flags=0, y=None, ids=None, w=None, pred=None,
-                               stream=None):
+                               hint=None, stream=None):
     import torch
     T = _tokens(x)
     _router_shape("router", router)
@@ -398,10 +398,12 @@ def strata_moe_layer_lookahead(x, router, blobs, ws, router_next, blobs_next, bi
     _opt_shape("ids", ids, (T, K))
     _opt_shape("w", w, (T, K))
     _opt_shape("pred", pred, (T, K))
+    _opt_shape("hint", hint, (T, K))
     _ws_shape(ws, T)
     rc = lib().strata_moe_layer_lookahead(
         _p(x, torch.float32), T, _p_router(router), _p(bias, torch.float32),
         _p(blobs, torch.uint8), flags, _p(y, torch.float32), _p(ids, torch.int32),
         _p(w, torch.float32), _p_router(router_next), _p(bias_next, torch.float32),
-        _p(blobs_next, torch.uint8), _p(pred, torch.int32), _p(ws), _nbytes(ws), _s(stream))
+        _p(blobs_next, torch.uint8), _p(pred, torch.int32), _p(hint, torch.int32), _p(ws),
+        _nbytes(ws), _s(stream))
     _check("strata_moe_layer_lookahead", rc)

@@ -24,9 +24,11 @@ hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const f
                                int32_t *esync, const uint16_t *R2, const float *bias2,
                                float *lraw2, int32_t *pred, hipStream_t st);
 hipError_t launch_router_gemv(const float *x, int T, const uint16_t *R, int rmsnorm, float *lraw,
-                              XQ xq, hipStream_t st);
+                              XQ xq, const uint16_t *R2, float *lraw2, hipStream_t st);
 hipError_t launch_decode_t1(const uint8_t *blobs, const float *lraw, const float *bias, XQ xq,
-                            HQ hq, int32_t *ids, float *w, float *y, float *res, hipEvent_t ev0,
+                            HQ hq, int32_t *ids, float *w, float *y, float *res,
+                            const int32_t *hint, const float *lraw2, const float *bias2,
+                            int32_t *pred, const uint8_t *blobs_next, hipEvent_t ev0,
                             hipEvent_t ev1, hipStream_t st);
 hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const int32_t *offsets,
                               const int32_t *slots, const int32_t *active, int4 *erec,
@@ -217,8 +219,8 @@ int run_prep(const Carve &c, const float *x, int T, int rms, const int32_t *offs
 // reads their blobs (blobs2) into the memory-side cache.
 int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const uint8_t *blobs,
                int flags, float *y, int32_t *ids, float *w, const uint16_t *router2,
-               const float *bias2, const uint8_t *blobs2, int32_t *pred, void *ws,
-               size_t ws_bytes, void *stream)
+               const float *bias2, const uint8_t *blobs2, int32_t *pred, const int32_t *hint,
+               void *ws, size_t ws_bytes, void *stream)
 {
     int rc = check_T(T);
     if (rc)
@@ -230,7 +232,7 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
     if ((rc = check_ws(ws, ws_bytes, T)))
         return rc;
     if (!aligned(x, 16) || !aligned(router, 16) || !aligned(blobs, 256) || !aligned(y, 16) ||
-        !aligned(ids, 4) || !aligned(w, 4) || !aligned(bias, 4))
+        !aligned(ids, 4) || !aligned(w, 4) || !aligned(bias, 4) || !aligned(hint, 4))
         return STRATA_E_ALIGN;
     if (router2 && (!aligned(router2, 16) || !aligned(blobs2, 256) || !aligned(bias2, 4) ||
                     !aligned(pred, 4)))
@@ -241,12 +243,15 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
     float *w_o = w ? w : c.w;
     int32_t *pred_o = pred ? pred : c.pred;
     const int rms = flags & STRATA_RMSNORM;
-    if (T == 1 && !router2) {   // one token: the gate/up launch routes it
-        STRATA_TRY(launch_router_gemv(x, T, router, rms, c.logits, c.xq, st));
+    if (T == 1) {   // one token: the gate/up launch routes it
+        STRATA_TRY(launch_router_gemv(x, T, router, rms, c.logits, c.xq, router2, c.lraw2, st));
         hipEvent_t e0, e1;
         take_events(e0, e1);
         STRATA_TRY(launch_decode_t1(blobs, c.logits, bias, c.xq, c.hq, ids_o, w_o, y,
-                                    (flags & STRATA_RESIDUAL) ? x : nullptr, e0, e1, st));
+                                    (flags & STRATA_RESIDUAL) ? x : nullptr, hint,
+                                    router2 ? c.lraw2 : nullptr, bias2,
+                                    router2 ? pred_o : nullptr, router2 ? blobs2 : nullptr, e0,
+                                    e1, st));
         return STRATA_OK;
     }
     if (is_decode(T)) {
@@ -407,7 +412,7 @@ int strata_moe_layer(float *x, int T, const uint16_t *router, const float *bias,
                      void *ws, size_t ws_bytes, void *stream)
 {
     return strata::layer_impl(x, T, router, bias, blobs, flags, y, ids, w, nullptr, nullptr,
-                              nullptr, nullptr, ws, ws_bytes, stream);
+                              nullptr, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 static_assert(2 * STRATA_LOOKAHEAD_T_MAX <= strata::DECODE_T_MAX,
@@ -416,15 +421,16 @@ static_assert(2 * STRATA_LOOKAHEAD_T_MAX <= strata::DECODE_T_MAX,
 int strata_moe_layer_lookahead(float *x, int T, const uint16_t *router, const float *bias,
                                const uint8_t *blobs, int flags, float *y, int32_t *ids, float *w,
                                const uint16_t *router_next, const float *bias_next,
-                               const uint8_t *blobs_next, int32_t *pred_ids, void *ws,
-                               size_t ws_bytes, void *stream)
+                               const uint8_t *blobs_next, int32_t *pred_ids,
+                               const int32_t *hint_ids, void *ws, size_t ws_bytes, void *stream)
 {
     if (T < 1 || T > STRATA_LOOKAHEAD_T_MAX)
         return STRATA_E_SHAPE;
     if (!router_next || !blobs_next)
         return STRATA_E_ARG;
     return strata::layer_impl(x, T, router, bias, blobs, flags, y, ids, w, router_next, bias_next,
-                              blobs_next, pred_ids, ws, ws_bytes, stream);
+                              blobs_next, pred_ids, T == 1 ? hint_ids : nullptr, ws, ws_bytes,
+                              stream);
 }
 
 int strata_moe_time_next_kernel(void *start, void *stop)
@@ -488,7 +494,7 @@ int strata_moe_layer_static(float *x, int T, const uint16_t *router, const float
     if (!ws)
         return STRATA_E_HIP;
     return strata::layer_impl(x, T, router, bias, blobs, flags, y, ids, w, nullptr, nullptr,
-                              nullptr, nullptr, ws, STATIC_WS_BYTES, stream);
+                              nullptr, nullptr, nullptr, ws, STATIC_WS_BYTES, stream);
 }
 
 const char *strata_moe_status_string(int status)

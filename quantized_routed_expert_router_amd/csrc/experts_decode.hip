@@ -165,6 +165,55 @@ __device__ inline void emit_h(const float (*part)[DG_ROWS], int slot, int seg, c
     }
 }
 
+// The 23,040 bytes of one gate/up item in flight in a workgroup's registers:
+// thread tid holds 16-byte chunks tid + 256 i, i = 0..5 (the sixth only where
+// it exists).  Chunk q < 720 is of the 16 gate rows, the rest of the 16 up
+// rows; it goes to LDS row q / 45 at dword 4 (q % 45).
+struct GuChunks {
+    uint4 p[6];
+};
+
+// Request segment seg (FF rows 16 seg .. + 15) of expert e's gate and up rows.
+__device__ inline GuChunks gu_request(const uint8_t *__restrict__ blobs, int e, int seg)
+{
+    const int tid = threadIdx.x;
+    const uint8_t *blob = blobs + (size_t)e * BLOB + (size_t)seg * DG_SEG * ROW_G;
+    const uint4 *g = reinterpret_cast<const uint4 *>(blob);
+    const uint4 *u = reinterpret_cast<const uint4 *>(blob + MAT);
+    GuChunks c;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int q = tid + DG_THREADS * i;
+        c.p[i] = q < DG_CHUNKS / 2 ? g[q] : u[q - DG_CHUNKS / 2];
+    }
+    const bool has5 = tid + 5 * DG_THREADS < DG_CHUNKS;
+    c.p[5] = has5 ? u[tid + 5 * DG_THREADS - DG_CHUNKS / 2] : make_uint4(0, 0, 0, 0);
+    return c;
+}
+
+// Write the chunks to LDS wl [DG_ROWS][DG_RS] dwords (the caller's next
+// barrier publishes them).
+__device__ inline void gu_stage(const GuChunks &c, uint32_t *wl)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        const int q = tid + DG_THREADS * i;
+        if (i < 5 || q < DG_CHUNKS) {
+            uint32_t *d = wl + (q / DG_CPR) * DG_RS + 4 * (q % DG_CPR);
+            d[0] = c.p[i].x;
+            d[1] = c.p[i].y;
+            d[2] = c.p[i].z;
+            d[3] = c.p[i].w;
+        }
+    }
+}
+
+template <bool FUSED>
+__device__ void gateup_compute(int4 rec, int seg, int a, const int32_t *__restrict__ slots,
+                               const XQ &xq, const HQ &hq, int T, uint32_t *wl,
+                               float (*part)[DG_ROWS], int32_t *gdone, XOps xo);
+
 // One gate/up item, segment seg (FF rows 16 seg .. + 15) of the active
 // expert with record rec = {expert, first grouped slot, token count, first
 // slot}: LDS wl [DG_ROWS][DG_RS] dwords and part [2 DG_WAVES][DG_ROWS].
@@ -176,48 +225,28 @@ __device__ void gateup_item(int4 rec, int seg, int a, const uint8_t *__restrict_
                             uint32_t *wl, float (*part)[DG_ROWS], int32_t *gdone)
 {
     const int nslot = T * K;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int s = 2 * wave + ((lane >> 4) >> 1);       // column stream: columns 5s .. 5s+4
+    const int slot = rec.w;
+    // token 0's operands are in flight with the weights
+    const XOps xo = load_xops(xq, slot >= 0 && slot < nslot ? slot / K : 0, s, lane & 15);
+    gu_stage(gu_request(blobs, rec.x, seg), wl);
+    gateup_compute<FUSED>(rec, seg, a, slots, xq, hq, T, wl, part, gdone, xo);
+}
+
+// The item's arithmetic once its rows are written to LDS (the barrier below
+// publishes them): xo holds token rec.w / K's operands for this lane.
+template <bool FUSED>
+__device__ void gateup_compute(int4 rec, int seg, int a, const int32_t *__restrict__ slots,
+                               const XQ &xq, const HQ &hq, int T, uint32_t *wl,
+                               float (*part)[DG_ROWS], int32_t *gdone, XOps xo)
+{
+    const int nslot = T * K;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane >> 4, l = lane & 15;
     const int s = 2 * wave + (r >> 1);                 // column stream: columns 5s .. 5s+4
     int slot = rec.w;
-    // token 0's operands are in flight with the weights
-    XOps xo = load_xops(xq, slot >= 0 && slot < nslot ? slot / K : 0, s, l);
-    {
-        // chunk q (q < 720: gate rows, else up rows) goes to LDS row q / 45 at
-        // dword 4 (q % 45)
-        const uint8_t *blob = blobs + (size_t)rec.x * BLOB + (size_t)seg * DG_SEG * ROW_G;
-        const uint4 *g = reinterpret_cast<const uint4 *>(blob);
-        const uint4 *u = reinterpret_cast<const uint4 *>(blob + MAT);
-        const bool has5 = tid + 5 * DG_THREADS < DG_CHUNKS;
-#define STRATA_DG_LD(P, I)                                                                         \
-    const uint4 P = (tid + DG_THREADS * (I)) < DG_CHUNKS / 2 ? g[tid + DG_THREADS * (I)]           \
-                                                             : u[tid + DG_THREADS * (I) - DG_CHUNKS / 2];
-#define STRATA_DG_ST(P, I)                                                                         \
-    {                                                                                              \
-        const int q_ = tid + DG_THREADS * (I);                                                     \
-        uint32_t *d_ = wl + (q_ / DG_CPR) * DG_RS + 4 * (q_ % DG_CPR);                             \
-        d_[0] = P.x;                                                                               \
-        d_[1] = P.y;                                                                               \
-        d_[2] = P.z;                                                                               \
-        d_[3] = P.w;                                                                               \
-    }
-        STRATA_DG_LD(p0, 0)
-        STRATA_DG_LD(p1, 1)
-        STRATA_DG_LD(p2, 2)
-        STRATA_DG_LD(p3, 3)
-        STRATA_DG_LD(p4, 4)
-        const uint4 p5 = has5 ? u[tid + 5 * DG_THREADS - DG_CHUNKS / 2] : make_uint4(0, 0, 0, 0);
-        STRATA_DG_ST(p0, 0)
-        STRATA_DG_ST(p1, 1)
-        STRATA_DG_ST(p2, 2)
-        STRATA_DG_ST(p3, 3)
-        STRATA_DG_ST(p4, 4)
-        if (has5)
-            STRATA_DG_ST(p5, 5)
-#undef STRATA_DG_ST
-#undef STRATA_DG_LD
-    }
     // Block column 5 s + j starts at byte 90 s + 18 j of the row; its 5-dword
     // window starts 2 bytes earlier when the column is odd.
     const uint32_t *row = wl + ((r & 1) * DG_SEG + l) * DG_RS;
@@ -818,56 +847,147 @@ __global__ __launch_bounds__(DS_THREADS) void dec_down(const uint8_t *__restrict
 }
 
 // ------------------------------------------ T = 1: the routing in every item
-// A layer call for one token (without the lookahead) has no top-k launch:
-// wave 0 of every gate/up workgroup routes the token itself from the router's
-// logits -- the top-k kernel's code on the same inputs, so every workgroup
-// gets the same ten ids and weights, bitwise -- and the workgroup takes head
-// k = its index / 40: the k-th expert, segment index % 40.  One token's ten
-// experts are distinct, so there is nothing to group.  Workgroup 0 writes the
-// ids and weights, which the down launch (dec_down, above) and the caller read.
-__global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(const uint8_t *__restrict__ blobs,
-                                                               const float *__restrict__ lraw,
-                                                               const float *__restrict__ bias,
-                                                               XQ xq, HQ hq,
-                                                               int32_t *__restrict__ ids,
-                                                               float *__restrict__ wout)
+// A layer call for one token has no top-k launch: wave 0 of every gate/up
+// workgroup routes the token itself from the router's logits -- the top-k
+// kernel's code on the same inputs, so every workgroup gets the same ten ids
+// and weights, bitwise.  One token's ten experts are distinct, so there is
+// nothing to group: workgroup b of the 400 takes head m = b / 40 (the m-th
+// expert in routing order) and segment b % 40.  Workgroup 0 writes the ids and
+// weights, which the down launch (dec_down, above) and the caller read.
+//
+// With a hint -- ten expert ids expected for this token, e.g. the previous
+// layer's lookahead prediction -- 400 more workgroups come first: workgroup
+// (j, seg) requests segment seg of hinted expert j's rows before the routing
+// has finished (the ~2 us of routing overlap the loads), and afterwards
+// computes them for the head whose expert that is, or exits if no head is.
+// The 400 plain workgroups then cover, in routing order, only the heads whose
+// expert no hint names.  Every head's h is computed exactly once, with the
+// same arithmetic either way, so the results never depend on the hint.
+//
+// With the lookahead (lraw2: the next layer's raw logits of the same input),
+// wave 1 of workgroup 0 routes them to the next layer's predicted ids (pred),
+// and K * XT_PER_SLOT trailing workgroups, each routing them again, read the
+// predicted experts' blobs in blobs_next line by line.
+constexpr int DR_WG = K * DG_SEGS;   // 400 workgroups per set
+
+__global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
+    const uint8_t *__restrict__ blobs, const float *__restrict__ lraw,
+    const float *__restrict__ bias, XQ xq, HQ hq, int32_t *__restrict__ ids,
+    float *__restrict__ wout, const int32_t *__restrict__ hint, const float *__restrict__ lraw2,
+    const float *__restrict__ bias2, int32_t *__restrict__ pred,
+    const uint8_t *__restrict__ blobs_next)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[DS_LDS_GU];
-    __shared__ int head_e;
-    const int k = blockIdx.x / DG_SEGS, seg = blockIdx.x % DG_SEGS;
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
+    __shared__ int head[K];
+    const int nh = hint ? DR_WG : 0;
+    const int b = blockIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (b >= nh + DR_WG) {   // lookahead reads
+        if (wave == 0) {
+            int my_id;
+            float my_p, sel;
+            route_token(lraw2, xq.inv_rms[0], bias2, my_id, my_p, sel);
+            if (lane < K)
+                head[lane] = my_id;
+        }
+        __syncthreads();
+        touch_next(b - nh - DR_WG, K, head, blobs_next);
+        return;
+    }
+    const bool hinted = b < nh;
+    const int j = (b - (hinted ? 0 : nh)) / DG_SEGS, seg = b % DG_SEGS;
+    // the hinted expert: a valid id and the first of its value in the hint
+    int eh = -1;
+    if (hinted) {
+        const int v = hint[j];
+        bool first = v >= 0 && v < E;
+        for (int i = 0; i < j; ++i)
+            first = first && hint[i] != v;
+        eh = first ? v : -1;
+    }
+    // the logits first, so that waiting for them does not wait for the rows
+    TokLogits tl, tl2;
+    if (wave == 0)
+        tl = load_logits(lraw, bias);
+    const bool predict = b == 0 && pred != nullptr;
+    if (wave == 1 && predict)
+        tl2 = load_logits(lraw2, bias2);
+    const float sc = xq.inv_rms[0];
+    const int s = 2 * wave + ((lane >> 4) >> 1);
+    XOps xo;
+    GuChunks ch;
+    if (eh >= 0) {
+        xo = load_xops(xq, 0, s, lane & 15);
+        ch = gu_request(blobs, eh, seg);
+    }
+    if (wave == 0) {
         int my_id;
         float my_p, sel;
-        route_token(lraw, xq.inv_rms[0], bias, my_id, my_p, sel);
-        // read lane k with every lane of the wave active: inside a branch on
-        // the lane the compiler may take my_id to be that lane's own value
-        const int he = __builtin_amdgcn_readlane(my_id, k);
-        if (blockIdx.x == 0 && lane < K) {
+        route_logits(tl, sc, bias != nullptr, my_id, my_p, sel);
+        if (b == 0 && lane < K) {
             ids[lane] = my_id;
             wout[lane] = my_p / renorm_den(sel);
         }
-        if (lane == 0)
-            head_e = he;
+        if (lane < K)
+            head[lane] = my_id;
+    } else if (wave == 1 && predict) {
+        int my_id;
+        float my_p, sel;
+        route_logits(tl2, sc, bias2 != nullptr, my_id, my_p, sel);
+        if (lane < K)
+            pred[lane] = my_id;
     }
-    __syncthreads();
-    const int e = head_e;
-    if (e < 0 || e >= E)   // not reached: the ten heads are expert ids
-        return;
     uint32_t *wl = reinterpret_cast<uint32_t *>(lds);
     float(*part)[DG_ROWS] = reinterpret_cast<float(*)[DG_ROWS]>(lds + (size_t)DG_ROWS * DG_RS * 4);
+    if (eh >= 0)
+        gu_stage(ch, wl);
+    __syncthreads();   // head, and the hinted rows
+    if (hinted) {
+        int k = -1;
+        for (int i = 0; i < K; ++i)
+            k = head[i] == eh ? i : k;
+        if (eh < 0 || k < 0)
+            return;
+        gateup_compute<false>(make_int4(eh, 0, 1, k), seg, 0, nullptr, xq, hq, 1, wl, part,
+                              nullptr, xo);
+        return;
+    }
+    // the j-th head, in routing order, whose expert no hint names
+    int k = -1, n = 0;
+    for (int i = 0; i < K; ++i) {
+        bool named = false;
+        if (hint)
+            for (int h = 0; h < K; ++h)
+                named = named || hint[h] == head[i];
+        if (!named) {
+            k = n == j ? i : k;
+            ++n;
+        }
+    }
+    if (k < 0)
+        return;
+    const int e = head[k];
+    if (e < 0 || e >= E)   // not reached: the ten heads are expert ids
+        return;
     gateup_item<false>(make_int4(e, 0, 1, k), seg, 0, blobs, nullptr, xq, hq, 1, wl, part,
                        nullptr);
 }
 
 hipError_t launch_decode_t1(const uint8_t *blobs, const float *lraw, const float *bias, XQ xq,
-                            HQ hq, int32_t *ids, float *w, float *y, float *res, hipEvent_t ev0,
+                            HQ hq, int32_t *ids, float *w, float *y, float *res,
+                            const int32_t *hint, const float *lraw2, const float *bias2,
+                            int32_t *pred, const uint8_t *blobs_next, hipEvent_t ev0,
                             hipEvent_t ev1, hipStream_t st)
 {
-    void *args[] = {&blobs, &lraw, &bias, &xq, &hq, &ids, &w};
+    if (!lraw2)
+        pred = nullptr;
+    if (!pred)
+        blobs_next = nullptr;
+    const int nwg = (hint ? 2 : 1) * DR_WG + (blobs_next ? K * XT_PER_SLOT : 0);
+    void *args[] = {&blobs, &lraw, &bias, &xq, &hq, &ids, &w, &hint, &lraw2, &bias2, &pred,
+                    &blobs_next};
     hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_route_gateup),
-                                      dim3(K * DG_SEGS), dim3(DG_THREADS), args, 0, st, ev0,
-                                      nullptr, 0);
+                                      dim3(nwg), dim3(DG_THREADS), args, 0, st, ev0, nullptr, 0);
     if (e != hipSuccess)
         return e;
     const int32_t *sexp = ids;

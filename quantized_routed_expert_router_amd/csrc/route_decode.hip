@@ -357,14 +357,15 @@ hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const f
     return hipGetLastError();
 }
 
-// The router GEMV alone (with the 16-bit quantisation of x): the one-token
-// layer call routes inside its gate/up launch.
+// The router GEMV alone (with the 16-bit quantisation of x; with R2, the
+// second router's raw logits too): the one-token layer call routes inside its
+// gate/up launch.
 hipError_t launch_router_gemv(const float *x, int T, const uint16_t *R, int rmsnorm, float *lraw,
-                              XQ xq, hipStream_t st)
+                              XQ xq, const uint16_t *R2, float *lraw2, hipStream_t st)
 {
     const GroupIn none{nullptr, nullptr, nullptr, nullptr, nullptr};
-    hipLaunchKernelGGL((rdec_gemv<true, true>), dim3(E), dim3(RG_THREADS), 0, st, x, T, R, lraw,
-                       xq, rmsnorm, none, (const uint16_t *)nullptr, (float *)nullptr);
+    hipLaunchKernelGGL((rdec_gemv<true, true>), dim3(R2 ? 2 * E : E), dim3(RG_THREADS), 0, st, x,
+                       T, R, lraw, xq, rmsnorm, none, R2, lraw2);
     return hipGetLastError();
 }
 

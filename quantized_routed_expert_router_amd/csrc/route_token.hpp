@@ -42,25 +42,40 @@ __device__ inline int wave_max_i(int v)
 // selected probabilities, clamped below at 2^-14 (w_k = p_k / den).
 __device__ inline float renorm_den(float sel) { return fmaxf(sel, 6.103515625e-05f); }
 
+// The lane's eight raw logits of one token (experts lane + 64 i) and, with a
+// bias, its eight bias values (zero without one): loaded apart from the
+// routing so that a caller can put other requests in flight between the two.
+struct TokLogits {
+    float l[8], b[8];
+};
+__device__ inline TokLogits load_logits(const float *lrow, const float *bias)
+{
+    const int lane = threadIdx.x & 63;
+    TokLogits t;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        t.l[i] = lrow[lane + 64 * i];
+        t.b[i] = bias ? bias[lane + 64 * i] : 0.f;
+    }
+    return t;
+}
+
 // One token's routing in one wave: softmax over the 512 logits
 // lrow * sc (+ bias), then the ten (p desc, id asc) heads in order.  Lane k
 // < K gets the k-th id and its p; sel (uniform) is the sum of the ten p.
-__device__ inline void route_token(const float *lrow, float sc, const float *bias, int &my_id,
-                                   float &my_p, float &sel)
+__device__ inline void route_logits(const TokLogits &t, float sc, bool has_bias, int &my_id,
+                                    float &my_p, float &sel)
 {
     const int lane = threadIdx.x & 63;
     float l[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        l[i] = lrow[lane + 64 * i];
-    if (bias) {
+    if (has_bias) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            l[i] = l[i] * sc + bias[lane + 64 * i];
+            l[i] = t.l[i] * sc + t.b[i];
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            l[i] = l[i] * sc;
+            l[i] = t.l[i] * sc;
     }
     float m = l[0];
 #pragma unroll
@@ -125,6 +140,12 @@ __device__ inline void route_token(const float *lrow, float sc, const float *bia
         }
         sel += bp;
     }
+}
+
+__device__ inline void route_token(const float *lrow, float sc, const float *bias, int &my_id,
+                                   float &my_p, float &sel)
+{
+    route_logits(load_logits(lrow, bias), sc, bias != nullptr, my_id, my_p, sel);
 }
 
 } // namespace strata

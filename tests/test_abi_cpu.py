@@ -72,18 +72,21 @@ def test_host_validation_rejects_before_launch(m):
     assert L.strata_moe_layer(fake, 4, fake, None, fake, 3, None, None, None, fake, 0, None) == m.E_WORKSPACE
     # lookahead: decode sizes only, and both next-layer pointers required
     LA = L.strata_moe_layer_lookahead
-    assert LA(fake, 9, fake, None, fake, 2, None, None, None, fake, None, fake, None, fake,
+    assert LA(fake, 9, fake, None, fake, 2, None, None, None, fake, None, fake, None, None, fake,
               m.strata_moe_workspace_bytes(9), None) == m.E_SHAPE
-    assert LA(fake, 0, fake, None, fake, 2, None, None, None, fake, None, fake, None, fake,
+    assert LA(fake, 0, fake, None, fake, 2, None, None, None, fake, None, fake, None, None, fake,
               ws_need, None) == m.E_SHAPE
-    assert LA(fake, 4, fake, None, fake, 2, None, None, None, None, None, fake, None, fake,
+    assert LA(fake, 4, fake, None, fake, 2, None, None, None, None, None, fake, None, None, fake,
               ws_need, None) == m.E_ARG
-    assert LA(fake, 4, fake, None, fake, 2, None, None, None, fake, None, None, None, fake,
+    assert LA(fake, 4, fake, None, fake, 2, None, None, None, fake, None, None, None, None, fake,
               ws_need, None) == m.E_ARG
-    assert LA(fake, 4, fake, None, fake, 2, None, None, None, fake, None, fake + 16, None, fake,
-              ws_need, None) == m.E_ALIGN
-    assert LA(fake, 4, fake, None, fake, 2, None, None, None, fake, None, fake, None, fake,
+    assert LA(fake, 4, fake, None, fake, 2, None, None, None, fake, None, fake + 16, None, None,
+              fake, ws_need, None) == m.E_ALIGN
+    assert LA(fake, 4, fake, None, fake, 2, None, None, None, fake, None, fake, None, None, fake,
               ws_need - 1, None) == m.E_WORKSPACE
+    # a misaligned hint at T = 1 (the only size that reads one)
+    assert LA(fake, 1, fake, None, fake, 2, None, None, None, fake, None, fake, None, fake + 2,
+              fake, m.strata_moe_workspace_bytes(1), None) == m.E_ALIGN
     # the timing hook takes both events or neither (arming touches no device)
     assert L.strata_moe_time_next_kernel(fake, None) == m.E_ARG
     assert L.strata_moe_time_next_kernel(None, fake) == m.E_ARG
@@ -154,6 +157,8 @@ def test_binding_checks_sizes_before_the_call(m):
     bad(m.strata_moe_layer_lookahead, x, R, store, ws, R, store[:5], y=x, what="blobs_next")
     bad(m.strata_moe_layer_lookahead, x, R, store, ws, R, store, y=x, pred=ids[:2],
         what="pred")
+    bad(m.strata_moe_layer_lookahead, x, R, store, ws, R, store, y=x, hint=ids[:2],
+        what="hint")
     # right sizes, host memory: refused for not being on the GPU
     bad(m.strata_moe_route, x, R, ids, w, ws, what="GPU")
     bad(m.strata_moe_layer, x, R, store, ws, y=x, ids=ids, w=w, what="GPU")

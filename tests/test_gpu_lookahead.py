@@ -86,3 +86,57 @@ def test_lookahead_layer_equals_layer_and_predicts_the_next_route(T, flags, with
                        bias=None if b2 is None else hz.cuda(b2), flags=flags & m.RMSNORM)
     torch.cuda.synchronize()
     assert np.array_equal(p, qids.cpu().numpy())
+
+
+@pytest.mark.parametrize("flags,with_bias", [(0, False), (3, True)])
+def test_hints_change_no_result(flags, with_bias):
+    """At T = 1 the lookahead layer takes a hint (the ids the token is expected
+    to route to) and requests the hinted experts' rows before its routing has
+    finished.  Whatever the hint -- exact, in another order, partly wrong, with
+    repeats and ids outside 0..E-1, or all wrong -- the outputs are bitwise
+    those of the plain layer, and the prediction is the same."""
+    import torch
+    m = hz.qm()
+    seed = 7300 + flags
+    print(f"case: hints T=1 flags={flags} bias={with_bias}", flush=True)
+    st_ = inputs.Streams(seed)
+    R = inputs.draw_router(st_.router)
+    R2 = inputs.draw_router(st_.router)
+    b = inputs.draw_zipf_bias(st_.bias) if with_bias else None
+    b2 = inputs.draw_zipf_bias(st_.bias) if with_bias else None
+    rms = bool(flags & 1)
+    x, _ = scr.screened_x(st_, 1, R, bias=b, rmsnorm=rms, extra=[(R2, b2)])
+    st, st2 = hz.store(seed, 0), hz.store(seed, 1)
+    ws = m.workspace(1)
+    ids0, w0, y0, x0 = hz.gpu_layer(x, R, st, bias=b, flags=flags, ws=ws)
+    others = [e for e in range(512) if e not in set(ids0[0].tolist())]
+    hints = {
+        "exact": ids0[0].copy(),
+        "reversed": ids0[0][::-1].copy(),
+        "half wrong": np.concatenate([ids0[0][:5], np.array(others[:5])]),
+        "repeats and junk": np.array([ids0[0][3], ids0[0][3], -1, 512, 99999, ids0[0][0],
+                                      others[0], others[0], ids0[0][9], -7]),
+        "all wrong": np.array(others[10:20]),
+    }
+    preds = []
+    for name, hv in hints.items():
+        xd = hz.cuda(x)
+        y = torch.empty_like(xd)
+        ids = torch.empty((1, 10), dtype=torch.int32, device="cuda")
+        w = torch.empty((1, 10), dtype=torch.float32, device="cuda")
+        pred = torch.full((1, 10), -1, dtype=torch.int32, device="cuda")
+        hint = torch.from_numpy(np.asarray(hv, dtype=np.int32).reshape(1, 10)).cuda()
+        m.strata_moe_layer_lookahead(xd, hz.router_dev(R), st, ws, hz.router_dev(R2), st2,
+                                     bias=None if b is None else hz.cuda(b),
+                                     bias_next=None if b2 is None else hz.cuda(b2), flags=flags,
+                                     y=y, ids=ids, w=w, pred=pred, hint=hint)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy(), ids0), name
+        assert np.array_equal(w.cpu().numpy(), w0), name
+        assert np.array_equal(y.cpu().numpy(), y0), name
+        assert np.array_equal(xd.cpu().numpy(), x0), name
+        preds.append(pred.cpu().numpy())
+    for p in preds[1:]:
+        assert np.array_equal(p, preds[0])
+    pids, _, _ = oracle.route(x, R2, 10, bias=b2, rmsnorm_flag=rms)
+    assert np.array_equal(preds[0], pids)
