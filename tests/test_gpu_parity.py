@@ -401,15 +401,34 @@ def test_zero_input_and_zero_experts():
     _say("case: zero activations; all-zero-weight experts")
     R = inputs.draw_router(np.random.default_rng(1))
     zero_store = torch.full((512 * inputs.blob_bytes(),), 0x55, dtype=torch.uint8, device="cuda")
-    x = np.zeros((T, 2560), dtype=np.float32)
-    for flags in (0, 1):
-        ids, w, y, _ = hz.gpu_layer(x, R, hz.store(0), flags=flags)
-        assert np.all(ids == np.arange(10)) and np.allclose(w, 0.1, atol=1e-7)
-        assert np.all(y == 0.0)
+    for Tz in (1, T):   # one token takes its own path (the routing in the gate/up launch)
+        x = np.zeros((Tz, 2560), dtype=np.float32)
+        for flags in (0, 1):
+            ids, w, y, _ = hz.gpu_layer(x, R, hz.store(0), flags=flags)
+            assert np.all(ids == np.arange(10)) and np.allclose(w, 0.1, atol=1e-7)
+            assert np.all(y == 0.0)
     xr = np.random.default_rng(2).standard_normal((20, 2560)).astype(np.float32)
     for T2 in (2, 20):
         _, _, y, _ = hz.gpu_layer(xr[:T2], R, zero_store)
         assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("T", [1, 4, 64])
+def test_layer_keeps_ids_and_weights_in_the_workspace(T):
+    """ids and w may be NULL: the layer keeps them in its workspace and its
+    output is bitwise that of a call that returns them."""
+    import torch
+    m = hz.qm()
+    seed = 4300 + T
+    _say(f"case: layer without ids / w outputs, T={T}")
+    x, R, _ = hz.single_layer_case(seed, T)
+    st = hz.store(seed)
+    ids, w, y, _ = hz.gpu_layer(x, R, st)
+    xd = hz.cuda(x)
+    y2 = torch.full_like(xd, float("nan"))
+    m.strata_moe_layer(xd, hz.router_dev(R), st, m.workspace(T), y=y2)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.cpu().numpy(), y)
 
 
 def test_graph_capture_replays_match_eager():
