@@ -52,31 +52,29 @@ __device__ inline TokLogits load_logits(const float *lrow, const float *bias)
 {
     const int lane = threadIdx.x & 63;
     TokLogits t;
+    if (bias) {   // one uniform branch around all sixteen loads
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        t.l[i] = lrow[lane + 64 * i];
-        t.b[i] = bias ? bias[lane + 64 * i] : 0.f;
+        for (int i = 0; i < 8; ++i) {
+            t.l[i] = lrow[lane + 64 * i];
+            t.b[i] = bias[lane + 64 * i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            t.l[i] = lrow[lane + 64 * i];
+            t.b[i] = 0.f;
+        }
     }
     return t;
 }
 
-// One token's routing in one wave: softmax over the 512 logits
-// lrow * sc (+ bias), then the ten (p desc, id asc) heads in order.  Lane k
-// < K gets the k-th id and its p; sel (uniform) is the sum of the ten p.
-__device__ inline void route_logits(const TokLogits &t, float sc, bool has_bias, int &my_id,
-                                    float &my_p, float &sel)
+// One token's routing in one wave from its scaled logits l (expert
+// lane + 64 i in l[i], bias included): softmax over the 512, then the ten
+// (p desc, id asc) heads in order.  Lane k < K gets the k-th id and its p;
+// sel (uniform) is the sum of the ten p.
+__device__ inline void route_scaled(float l[8], int &my_id, float &my_p, float &sel)
 {
     const int lane = threadIdx.x & 63;
-    float l[8];
-    if (has_bias) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            l[i] = t.l[i] * sc + t.b[i];
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            l[i] = t.l[i] * sc;
-    }
     float m = l[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i)
@@ -142,10 +140,45 @@ __device__ inline void route_logits(const TokLogits &t, float sc, bool has_bias,
     }
 }
 
+// The routing of logits loaded by load_logits: l = raw * sc (+ bias).
+__device__ inline void route_logits(const TokLogits &t, float sc, bool has_bias, int &my_id,
+                                    float &my_p, float &sel)
+{
+    float l[8];
+    if (has_bias) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            l[i] = t.l[i] * sc + t.b[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            l[i] = t.l[i] * sc;
+    }
+    route_scaled(l, my_id, my_p, sel);
+}
+
+// One token's routing from its raw logits lrow[512]: l = lrow * sc (+ bias).
+// The same arithmetic as route_logits; the loads are laid out apart (the
+// bias read only when there is one), which the latency of the decode top-k
+// kernel is sensitive to.
 __device__ inline void route_token(const float *lrow, float sc, const float *bias, int &my_id,
                                    float &my_p, float &sel)
 {
-    route_logits(load_logits(lrow, bias), sc, bias != nullptr, my_id, my_p, sel);
+    const int lane = threadIdx.x & 63;
+    float l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        l[i] = lrow[lane + 64 * i];
+    if (bias) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            l[i] = l[i] * sc + bias[lane + 64 * i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            l[i] = l[i] * sc;
+    }
+    route_scaled(l, my_id, my_p, sel);
 }
 
 } // namespace strata
