@@ -641,8 +641,11 @@ constexpr int XT_LINES = BLOB / 128;                                   // 10,800
 constexpr int XT_LINES_PER_WG = (XT_LINES + XT_PER_SLOT - 1) / XT_PER_SLOT;   // 675
 static_assert(BLOB % 128 == 0, "whole lines");
 
+// Each lane's 4 bytes of a line go straight into the workgroup's LDS (lds:
+// 1 KB it does not otherwise use, one 256-byte row per wave), so no register
+// is written by a load still in flight.
 __device__ void touch_next(int b, int nslot, const int32_t *__restrict__ pred,
-                           const uint8_t *__restrict__ blobs_next)
+                           const uint8_t *__restrict__ blobs_next, uint8_t *lds)
 {
     const int s = b / XT_PER_SLOT, part = b % XT_PER_SLOT;
     if (s >= nslot)
@@ -655,10 +658,9 @@ __device__ void touch_next(int b, int nslot, const int32_t *__restrict__ pred,
             return;
     const uint8_t *base = blobs_next + (size_t)e * BLOB + (size_t)part * XT_LINES_PER_WG * 128;
     const int n = min(XT_LINES_PER_WG, XT_LINES - part * XT_LINES_PER_WG);
-    for (int i = threadIdx.x; i < n; i += EX_THREADS) {
-        uint32_t v;
-        asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(base + (size_t)i * 128) : "memory");
-    }
+    uint8_t *row = lds + 256 * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int i = threadIdx.x; i < n; i += EX_THREADS)
+        __builtin_amdgcn_global_load_lds(base + (size_t)i * 128, row, 4, 0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -702,7 +704,7 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
         down_group(g, blobs, erec, slots, hq, out, T, cb, wl, gdone, status, wait_limit,
                    reinterpret_cast<int *>(lds + EX_LDS_MAX));
     } else {
-        touch_next(b - amax * (DG_SEGS + EX_DN_PER_E), T * K, pred, blobs_next);
+        touch_next(b - amax * (DG_SEGS + EX_DN_PER_E), T * K, pred, blobs_next, lds);
     }
 }
 
@@ -727,6 +729,8 @@ constexpr int DS_WAVES = K / 2;                     // 5: two slots per wave
 constexpr int DS_THREADS = 64 * DS_WAVES;
 constexpr int DS_CHUNKS_PER_T = H / DS_ROWS;        // 160
 constexpr size_t DS_LDS_GU = (size_t)DG_ROWS * DG_RS * 4 + (size_t)2 * DG_WAVES * DG_ROWS * 4;
+static_assert(DG_WAVES * 256 <= DS_LDS_GU && DG_WAVES * 256 <= EX_LDS,
+              "the line reads' LDS rows fit in every kernel that makes them");
 
 // A lane's down weights: five 20-byte windows of its row (window j holds block
 // column 2 j + c0, starting 2 bytes in when c0 = 1).
@@ -802,7 +806,7 @@ __global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restri
         gateup_item<false>(erec[1 + b / DG_SEGS], b % DG_SEGS, 0, blobs, slots, xq, hq, T, wl,
                            part, nullptr);
     } else {
-        touch_next(b - amax * DG_SEGS, T * K, pred, blobs_next);
+        touch_next(b - amax * DG_SEGS, T * K, pred, blobs_next, lds);
     }
 }
 
@@ -891,7 +895,7 @@ __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
                 head[lane] = my_id;
         }
         __syncthreads();
-        touch_next(b - nh - DR_WG, K, head, blobs_next);
+        touch_next(b - nh - DR_WG, K, head, blobs_next, lds);
         return;
     }
     const bool hinted = b < nh;
