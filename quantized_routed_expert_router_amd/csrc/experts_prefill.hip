@@ -119,31 +119,42 @@ struct PgAct {
     }
 };
 
-// One group's weight bytes for the wave's four 16-row subtiles.
+// One group's weight bytes for the wave's NS 16-row subtiles.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-struct PgW {
-    u32x4 lo[4];
-    uint32_t hi[4];
+template <int NS> struct PgWn {
+    u32x4 lo[NS];
+    uint32_t hi[NS];
 };
+using PgW = PgWn<4>;
 
 // Waits for all of this wave's loads; the compiler then sees r as ready (its
 // own wait for them would otherwise also wait for the loads issued since).
-__device__ inline void pg_wait_all(PgW &r)
+template <int NS> __device__ inline void pg_wait_all(PgWn<NS> &r)
 {
-    u32x4 a = r.lo[0], b = r.lo[1], c = r.lo[2], d = r.lo[3];
-    uint32_t e = r.hi[0], f = r.hi[1], g = r.hi[2], h = r.hi[3];
-    asm volatile("s_waitcnt vmcnt(0)"
-                 : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
-                 :
-                 : "memory");
-    r.lo[0] = a, r.lo[1] = b, r.lo[2] = c, r.lo[3] = d;
-    r.hi[0] = e, r.hi[1] = f, r.hi[2] = g, r.hi[3] = h;
+    static_assert(NS == 2 || NS == 4, "two or four subtiles");
+    if constexpr (NS == 4) {
+        u32x4 a = r.lo[0], b = r.lo[1], c = r.lo[2], d = r.lo[3];
+        uint32_t e = r.hi[0], f = r.hi[1], g = r.hi[2], h = r.hi[3];
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
+                     :
+                     : "memory");
+        r.lo[0] = a, r.lo[1] = b, r.lo[2] = c, r.lo[3] = d;
+        r.hi[0] = e, r.hi[1] = f, r.hi[2] = g, r.hi[3] = h;
+    } else {
+        u32x4 a = r.lo[0], b = r.lo[1];
+        uint32_t e = r.hi[0], f = r.hi[1];
+        asm volatile("s_waitcnt vmcnt(0)" : "+v"(a), "+v"(b), "+v"(e), "+v"(f) : : "memory");
+        r.lo[0] = a, r.lo[1] = b;
+        r.hi[0] = e, r.hi[1] = f;
+    }
 }
 
-__device__ inline void pg_wload(const uint8_t *blob, const uint32_t woff[4], int g, PgW &r)
+template <int NS>
+__device__ inline void pg_wload(const uint8_t *blob, const uint32_t woff[NS], int g, PgWn<NS> &r)
 {
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
+    for (int ns = 0; ns < NS; ++ns) {
         const uint8_t *p = blob + woff[ns] + PG_BLK * BB * g;
         r.lo[ns] = *reinterpret_cast<const u32x4 *>(p);
         r.hi[ns] = *reinterpret_cast<const uint32_t *>(p + 16);
@@ -191,18 +202,18 @@ __device__ inline void pg_await(half8 af[4])
 // AOFF (16-row groups MSTR bytes apart): issue the reads of step J + 1,
 // dequantise this step's four weight fragments, issue its 4 x MS MFMAs, wait
 // for the reads.
-template <int AOFF, int MSTR, int NSTEP, int MS, int J>
-__device__ inline void pg_step(uint32_t ae, uint32_t ao, const uint32_t d2[4], const uint32_t cw[4][4],
-                               half8 af[2][4], floatx4 acc[4][4])
+template <int AOFF, int MSTR, int NSTEP, int MS, int J, int NS = 4>
+__device__ inline void pg_step(uint32_t ae, uint32_t ao, const uint32_t d2[NS],
+                               const uint32_t cw[NS][4], half8 af[2][4], floatx4 acc[NS][4])
 {
     if constexpr (J + 1 < NSTEP)
         pg_aread<AOFF + 128 * (J + 1), MSTR, MS>(((J + 1) & 1) ? ao : ae, af[(J + 1) & 1]);
-    uint32_t pr[4][4];
+    uint32_t pr[NS][4];
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns)
+    for (int ns = 0; ns < NS; ++ns)
         dequant_half<J & 1>(cw[ns][J >> 1], d2[ns], pr[ns]);
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
+    for (int ns = 0; ns < NS; ++ns) {
         const half8 bf = __builtin_bit_cast(half8, make_uint4(pr[ns][0], pr[ns][1], pr[ns][2], pr[ns][3]));
 #pragma unroll
         for (int mi = 0; mi < MS; ++mi)   // only the 16-row groups holding item rows
@@ -214,11 +225,12 @@ __device__ inline void pg_step(uint32_t ae, uint32_t ao, const uint32_t d2[4], c
 
 // The scale pairs and code dwords of one group, picked out of its loaded
 // bytes (sel_d, sel_c: the byte selections for this lane's block offset).
-__device__ inline void pg_extract(const PgW &wr, uint32_t sel_c, uint32_t sel_d, uint32_t d2[4],
-                                  uint32_t cw[4][4])
+template <int NS>
+__device__ inline void pg_extract(const PgWn<NS> &wr, uint32_t sel_c, uint32_t sel_d, uint32_t d2[NS],
+                                  uint32_t cw[NS][4])
 {
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
+    for (int ns = 0; ns < NS; ++ns) {
         const uint32_t L[5] = {wr.lo[ns].x, wr.lo[ns].y, wr.lo[ns].z, wr.lo[ns].w, wr.hi[ns]};
         d2[ns] = __builtin_amdgcn_perm(L[0], L[0], sel_d);
 #pragma unroll
@@ -232,24 +244,24 @@ __device__ inline void pg_extract(const PgW &wr, uint32_t sel_c, uint32_t sel_d,
 // activation fragments (the next step's reads run during this step's math),
 // dequantises its four weight fragments and issues 4 x MS MFMAs.
 // ae / ao: this lane's fragment read address for even / odd steps.
-template <int BUF, int MS>
-__device__ inline void pg_group(uint32_t ae, uint32_t ao, const PgW &wr, uint32_t sel_c,
-                                uint32_t sel_d, floatx4 acc[4][4])
+template <int BUF, int MS, int NS = 4>
+__device__ inline void pg_group(uint32_t ae, uint32_t ao, const PgWn<NS> &wr, uint32_t sel_c,
+                                uint32_t sel_d, floatx4 acc[NS][4])
 {
-    uint32_t d2[4], cw[4][4];
+    uint32_t d2[NS], cw[NS][4];
     pg_extract(wr, sel_c, sel_d, d2, cw);
     constexpr int A0 = BUF * PG_ABYTES;
     half8 af[2][4];
     pg_aread<A0, 8192, MS>(ae, af[0]);
     pg_await<MS>(af[0]);
-    pg_step<A0, 8192, 8, MS, 0>(ae, ao, d2, cw, af, acc);
-    pg_step<A0, 8192, 8, MS, 1>(ae, ao, d2, cw, af, acc);
-    pg_step<A0, 8192, 8, MS, 2>(ae, ao, d2, cw, af, acc);
-    pg_step<A0, 8192, 8, MS, 3>(ae, ao, d2, cw, af, acc);
-    pg_step<A0, 8192, 8, MS, 4>(ae, ao, d2, cw, af, acc);
-    pg_step<A0, 8192, 8, MS, 5>(ae, ao, d2, cw, af, acc);
-    pg_step<A0, 8192, 8, MS, 6>(ae, ao, d2, cw, af, acc);
-    pg_step<A0, 8192, 8, MS, 7>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 0, NS>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 1, NS>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 2, NS>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 3, NS>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 4, NS>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 5, NS>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 6, NS>(ae, ao, d2, cw, af, acc);
+    pg_step<A0, 8192, 8, MS, 7, NS>(ae, ao, d2, cw, af, acc);
 }
 
 // Gate/up K loop over the 10 groups: group g computes from LDS buffer g % 2
@@ -258,12 +270,12 @@ __device__ inline void pg_group(uint32_t ae, uint32_t ao, const PgW &wr, uint32_
 // earlier) and passes the barrier (every wave's share has landed; every wave
 // is done reading the other buffer), then requests group g + 1 into the
 // other buffer and register set and computes group g.
-template <int MS>
-__device__ inline void pg_gateup_loop(const uint8_t *blob, const uint32_t woff[4], const PgAct &act,
+template <int MS, int NS, class ACT>
+__device__ inline void pg_gateup_loop(const uint8_t *blob, const uint32_t woff[NS], const ACT &act,
                                       uint8_t *lds, uint32_t ae, uint32_t ao, uint32_t sel_c,
-                                      uint32_t sel_d, floatx4 acc[4][4])
+                                      uint32_t sel_d, floatx4 acc[NS][4])
 {
-    PgW w0, w1;
+    PgWn<NS> w0, w1;
     act.request(lds, 0);
     pg_wload(blob, woff, 0, w0);
 #pragma unroll 1
@@ -272,14 +284,14 @@ __device__ inline void pg_gateup_loop(const uint8_t *blob, const uint32_t woff[4
         __builtin_amdgcn_s_barrier();
         act.request(lds + PG_ABYTES, g + 1);
         pg_wload(blob, woff, g + 1, w1);
-        pg_group<0, MS>(ae, ao, w0, sel_c, sel_d, acc);
+        pg_group<0, MS, NS>(ae, ao, w0, sel_c, sel_d, acc);
         pg_wait_all(w1);
         __builtin_amdgcn_s_barrier();
         if (g + 2 < PG_NG) {
             act.request(lds, g + 2);
             pg_wload(blob, woff, g + 2, w0);
         }
-        pg_group<1, MS>(ae, ao, w1, sel_c, sel_d, acc);
+        pg_group<1, MS, NS>(ae, ao, w1, sel_c, sel_d, acc);
     }
 }
 
@@ -401,7 +413,31 @@ __device__ inline PfItem pf_item(int item, const int32_t *mlist, const int32_t *
     return it;
 }
 
-__global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
+// Gate/up runs eight waves per workgroup, each on 16 FF rows (one gate and one
+// up subtile), so that two workgroups per CU put four waves on every SIMD:
+// while some wait at a group's loads or barrier, others compute.  Wave w
+// requests the activations of row group w.
+constexpr int PG_WAVES = 8;
+constexpr int PG_THREADS = 64 * PG_WAVES;
+constexpr int PG_NS = 2;                                // subtiles per wave
+static_assert(PG_WAVES * 16 == PF_NT_G && PG_WAVES * 8 == PF_M, "a wave per 16 FF rows and 8 item rows");
+
+// Activation requests of gate/up group g for this wave: 4 requests of 1 KB,
+// request i filling row group w, chunk octet i.
+struct PgAct8 {
+    const uint8_t *row;   // row 8 w + lane % 8 (valid memory for every lane)
+    uint32_t coff;        // byte offset of this lane's chunk in the octet
+    __device__ void request(uint8_t *abuf, int g) const
+    {
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds(row + PG_GBYTES * g + 128 * i + coff,
+                                             abuf + (4 * w + i) * 1024, 16, 0, 0);
+    }
+};
+
+__global__ __launch_bounds__(PG_THREADS, 4) void pf_gateup(
     const uint8_t *__restrict__ blobs, const int32_t *__restrict__ slots,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ nitems,
     const __half *__restrict__ xperm, const int32_t *__restrict__ xexp, __half *__restrict__ hperm,
@@ -416,29 +452,27 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
     if (!it.ok)
         return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int jw = nt * PF_NT_G + 32 * wave;   // this wave's first FF row
+    const int jw = nt * PF_NT_G + 16 * wave;   // this wave's first FF row
     pf_row_exps(it, nt, slots, xexp, hexp, T, kx);
     const uint8_t *blob = blobs + (size_t)it.e * BLOB;
-    // Activation rows this lane requests (rows past the item's end read its
-    // first row; their results are never stored): rows 16 w + 8 h + lane % 8,
-    // chunk (lane / 8) ^ h of each octet.
-    PgAct act;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = 16 * wave + 8 * h + (lane & 7);
+    // Activation row this lane requests (rows past the item's end read its
+    // first row; their results are never stored): row 8 w + lane % 8, chunk
+    // (lane / 8) ^ (w % 2) of each octet.
+    PgAct8 act;
+    {
+        const int r = 8 * wave + (lane & 7);
         const int sl = slots[it.gp0 + (r < it.rows ? r : 0)];
         const int t = (sl >= 0 && sl < T * K) ? sl / K : 0;
-        act.row[h] = reinterpret_cast<const uint8_t *>(xperm + (size_t)t * H);
-        act.coff[h] = 16 * ((lane >> 3) ^ h);
+        act.row = reinterpret_cast<const uint8_t *>(xperm + (size_t)t * H);
+        act.coff = 16 * ((lane >> 3) ^ (wave & 1));
     }
-    // Weight bytes: subtile ns is gate (ns < 2) or up rows jw + 16 (ns % 2) +
-    // lane % 16; quarter q loads from the dword at or below block q's start.
+    // Weight bytes: subtile 0 is gate rows jw + lane % 16, subtile 1 the same
+    // up rows; quarter q loads from the dword at or below block q's start.
     const int q = lane >> 4, odd = q & 1;
-    uint32_t woff[4];
+    uint32_t woff[PG_NS];
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns)
-        woff[ns] = (uint32_t)((ns >= 2 ? MAT : 0) + (size_t)(jw + 16 * (ns & 1) + (lane & 15)) * ROW_G +
-                              BB * q - 2 * odd);
+    for (int ns = 0; ns < PG_NS; ++ns)
+        woff[ns] = (uint32_t)((ns ? MAT : 0) + (size_t)(jw + (lane & 15)) * ROW_G + BB * q - 2 * odd);
     const uint32_t sel_c = odd ? 0x07060504u : 0x05040302u;   // code dword i: bytes 2..5 or 4..7 of L[i], L[i+1]
     const uint32_t sel_d = odd ? 0x03020302u : 0x01000100u;   // (d, d) from bytes 0, 1 or 2, 3 of L[0]
     // Fragment reads: row 16 mi + lane % 16 (row group 2 mi + b), chunk 8 q + j at
@@ -446,52 +480,49 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gateup(
     const int b = (lane >> 3) & 1;
     const uint32_t abase = lds_addr(lds) + (32 * b + 8 * q) * 128 + 16 * (lane & 7);
     const uint32_t ae = abase + 128 * b, ao = abase - 128 * b;
-    floatx4 acc[4][4];
+    floatx4 acc[PG_NS][4];
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns)
+    for (int ns = 0; ns < PG_NS; ++ns)
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
             acc[ns][mi] = (floatx4){0.f, 0.f, 0.f, 0.f};
     // one straight-line loop per number of 16-row groups holding item rows
     switch ((it.rows + 15) >> 4) {
     case 1:
-        pg_gateup_loop<1>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
+        pg_gateup_loop<1, PG_NS>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
         break;
     case 2:
-        pg_gateup_loop<2>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
+        pg_gateup_loop<2, PG_NS>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
         break;
     case 3:
-        pg_gateup_loop<3>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
+        pg_gateup_loop<3, PG_NS>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
         break;
     default:
-        pg_gateup_loop<4>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
+        pg_gateup_loop<4, PG_NS>(blob, woff, act, lds, ae, ao, sel_c, sel_d, acc);
         break;
     }
     __syncthreads();   // kx
-    // Epilogue: h = silu(g) * u for FF rows jw + 16 h2 + lane%16, stored
-    // times 2^hs: g = acc 2^-k, and silu(g) acc_u = silu(g) u 2^k.  Items whose
-    // rows are all unscaled skip the exponents.
+    // Epilogue: h = silu(g) * u for FF row jw + lane%16, stored times 2^hs:
+    // g = acc 2^-k, and silu(g) acc_u = silu(g) u 2^k.  Items whose rows are
+    // all unscaled skip the exponents.
     const bool scaled = kx[PF_M] != 0;
+    const int j = jw + (lane & 15);
+    const int col = pd_pos_of_col(j);
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-        const int j = jw + 16 * h2 + (lane & 15);
-        const int col = pd_pos_of_col(j);
+    for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 16 * mi + 4 * (lane >> 4) + r;
-                if (m < it.rows) {
-                    float h;
-                    if (scaled) {
-                        const int v = kx[m], k = pf_k(v);
-                        const float g = ldexpf(acc[h2][mi][r], -k);
-                        h = ldexpf(pf_silu_mul(g, acc[2 + h2][mi][r]), pf_hs(v) - k);
-                    } else {
-                        h = pf_silu_mul(acc[h2][mi][r], acc[2 + h2][mi][r]);
-                    }
-                    hperm[(size_t)(it.gp0 + m) * FF + col] = __float2half_rn(h);
+        for (int r = 0; r < 4; ++r) {
+            const int m = 16 * mi + 4 * (lane >> 4) + r;
+            if (m < it.rows) {
+                float h;
+                if (scaled) {
+                    const int v = kx[m], k = pf_k(v);
+                    const float g = ldexpf(acc[0][mi][r], -k);
+                    h = ldexpf(pf_silu_mul(g, acc[1][mi][r]), pf_hs(v) - k);
+                } else {
+                    h = pf_silu_mul(acc[0][mi][r], acc[1][mi][r]);
                 }
+                hperm[(size_t)(it.gp0 + m) * FF + col] = __float2half_rn(h);
             }
         }
     }
@@ -618,7 +649,7 @@ hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   hipStream_t st)
 {
     const int groups = (max_items + 7) / 8;
-    const dim3 grid_g(8 * PF_NTILES_G * groups), block(PF_THREADS);
+    const dim3 grid_g(8 * PF_NTILES_G * groups), block(PG_THREADS);
     if (ev0) {   // timed launch: the events carry the dispatch's own start and end
         void *args[] = {&blobs, &slots, &mlist, &nitems, &xperm, &xexp, &hperm, &hexp, &T};
         const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&pf_gateup), grid_g,
