@@ -83,8 +83,8 @@ __device__ inline void dequant_half(uint32_t w, uint32_t d2bits, uint32_t out[4]
 // stores the activations in that order, as 16-byte chunk 8 q + j of each
 // 512-byte group.
 // Activations: one group (64 rows x 512 bytes) per LDS buffer, two buffers,
-// filled by direct global->LDS loads one group ahead, and read by all four
-// waves.  A 1 KB request fills 8 rows (row group r = row / 8) x 8 chunks of
+// filled by direct global->LDS loads one group ahead, and read by every wave
+// of the workgroup.  A 1 KB request fills 8 rows (row group r = row / 8) x 8 chunks of
 // one octet; inside the row group chunk c sits at position c ^ (r & 1), so
 // the two row groups of a 16-row fragment read fall on different banks.
 // One barrier per group.
@@ -104,7 +104,8 @@ __device__ inline uint32_t lds_addr(uint8_t *p)
     return (uint32_t)(uintptr_t)(lds_u8 *)p;
 }
 
-// Activation requests of gate/up group g for this wave: 8 requests of 1 KB,
+// Activation requests of a group for a wave of a four-wave workgroup (the
+// down kernel's groups 0 and 1): 8 requests of 1 KB,
 // request i filling row group 2 w + i / 4, chunk octet i % 4.
 struct PgAct {
     const uint8_t *row[2];   // rows 16 w + 8 h + lane % 8 (valid memory for every lane)
