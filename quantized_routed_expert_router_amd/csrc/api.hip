@@ -25,11 +25,11 @@ hipError_t launch_route_decode(const float *x, int T, const uint16_t *R, const f
                                float *lraw2, int32_t *pred, hipStream_t st);
 hipError_t launch_router_gemv(const float *x, int T, const uint16_t *R, int rmsnorm, float *lraw,
                               XQ xq, const uint16_t *R2, float *lraw2, hipStream_t st);
-hipError_t launch_decode_t1(const uint8_t *blobs, const float *lraw, const float *bias, XQ xq,
-                            HQ hq, int32_t *ids, float *w, float *y, float *res,
-                            const int32_t *hint, const float *lraw2, const float *bias2,
-                            int32_t *pred, const uint8_t *blobs_next, hipEvent_t ev0,
-                            hipEvent_t ev1, hipStream_t st);
+hipError_t launch_decode_routed(const uint8_t *blobs, const float *lraw, int T, const float *bias,
+                                XQ xq, HQ hq, int32_t *ids, float *w, float *y, float *res,
+                                const int32_t *hint, const float *lraw2, const float *bias2,
+                                int32_t *pred, const uint8_t *blobs_next, hipEvent_t ev0,
+                                hipEvent_t ev1, hipStream_t st);
 hipError_t launch_prep_decode(const float *x, int T, int rmsnorm, XQ xq, const int32_t *offsets,
                               const int32_t *slots, const int32_t *active, int4 *erec,
                               int32_t *esync, hipStream_t st);
@@ -243,15 +243,15 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
     float *w_o = w ? w : c.w;
     int32_t *pred_o = pred ? pred : c.pred;
     const int rms = flags & STRATA_RMSNORM;
-    if (T == 1) {   // one token: the gate/up launch routes it
+    if (T == 1 || (T <= ROUTED_T_MAX && !router2)) {   // the gate/up launch routes each token
         STRATA_TRY(launch_router_gemv(x, T, router, rms, c.logits, c.xq, router2, c.lraw2, st));
         hipEvent_t e0, e1;
         take_events(e0, e1);
-        STRATA_TRY(launch_decode_t1(blobs, c.logits, bias, c.xq, c.hq, ids_o, w_o, y,
-                                    (flags & STRATA_RESIDUAL) ? x : nullptr, hint,
-                                    router2 ? c.lraw2 : nullptr, bias2,
-                                    router2 ? pred_o : nullptr, router2 ? blobs2 : nullptr, e0,
-                                    e1, st));
+        STRATA_TRY(launch_decode_routed(blobs, c.logits, T, bias, c.xq, c.hq, ids_o, w_o, y,
+                                        (flags & STRATA_RESIDUAL) ? x : nullptr, hint,
+                                        router2 ? c.lraw2 : nullptr, bias2,
+                                        router2 ? pred_o : nullptr, router2 ? blobs2 : nullptr,
+                                        e0, e1, st));
         return STRATA_OK;
     }
     if (is_decode(T)) {

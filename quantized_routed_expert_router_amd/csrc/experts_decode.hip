@@ -711,8 +711,10 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
 // ------------------------------------------------- T <= 3: two launches
 // For one to three tokens the layer runs the experts as two launches in
 // stream order instead (the kernel boundary publishes h, so nothing waits inside a
-// kernel): dec_gateup runs the gate/up items above (plain stores of h, no
-// counters) and the lookahead workgroups; dec_down has one workgroup per 16
+// kernel): with the lookahead, dec_gateup runs the gate/up items above (plain
+// stores of h, no counters) and the lookahead workgroups, and without it
+// dec_route_gateup (below) routes each token and runs its ten heads' items;
+// then dec_down, with one workgroup per 16
 // output rows of the token, 5 waves with two of its slots each, lane (r, l)
 // taking row l of slot 2 w + r % 2's expert and block columns 2 j + r / 2 from
 // five 20-byte windows loaded straight into registers.  The two halves of
@@ -723,7 +725,7 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
 // is faster for tokens that share few experts (its down groups read an
 // expert's rows once for all the tokens that share it; here each token reads
 // its own).
-constexpr int DS_T_MAX = 3;                         // layer calls with T <= this split
+constexpr int DS_T_MAX = 3;                         // lookahead layer calls with T <= this split
 constexpr int DS_ROWS = 16;                         // output rows per workgroup
 constexpr int DS_WAVES = K / 2;                     // 5: two slots per wave
 constexpr int DS_THREADS = 64 * DS_WAVES;
@@ -850,14 +852,20 @@ __global__ __launch_bounds__(DS_THREADS) void dec_down(const uint8_t *__restrict
     }
 }
 
-// ------------------------------------------ T = 1: the routing in every item
-// A layer call for one token has no top-k launch: wave 0 of every gate/up
-// workgroup routes the token itself from the router's logits -- the top-k
-// kernel's code on the same inputs, so every workgroup gets the same ten ids
-// and weights, bitwise.  One token's ten experts are distinct, so there is
-// nothing to group: workgroup b of the 400 takes head m = b / 40 (the m-th
-// expert in routing order) and segment b % 40.  Workgroup 0 writes the ids and
-// weights, which the down launch (dec_down, above) and the caller read.
+// ------------------------------- T <= ROUTED_T_MAX: the routing in every item
+// A layer call for up to ROUTED_T_MAX tokens without the lookahead (and one
+// token with it) has no top-k launch: each token gets 400 gate/up workgroups,
+// and wave 0 of every one of them routes that token itself from the router's
+// logits -- the top-k kernel's code on the same inputs, so every workgroup of
+// a token gets the same ten ids and weights, bitwise.  A token's ten experts
+// are distinct, so there is nothing to group: workgroup b of token t's 400
+// takes head m = b / 40 (the m-th expert in routing order) and segment b % 40,
+// slot t K + m.  An expert two tokens share is read once per token (each
+// token's items are its own); against the grouped launches that read it once,
+// this was faster at T = 2 and 3 (20.7 vs 22.9 us, 22.1 vs 25.0 us per layer
+// step) and slower from T = 4 (28.5 vs 27.4 us).  The first workgroup of each
+// token writes its ids and weights, which the down launch (dec_down, above)
+// and the caller read.
 //
 // With a hint -- ten expert ids expected for this token, e.g. the previous
 // layer's lookahead prediction -- 400 more workgroups come first: workgroup
@@ -879,14 +887,14 @@ __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
     const float *__restrict__ bias, XQ xq, HQ hq, int32_t *__restrict__ ids,
     float *__restrict__ wout, const int32_t *__restrict__ hint, const float *__restrict__ lraw2,
     const float *__restrict__ bias2, int32_t *__restrict__ pred,
-    const uint8_t *__restrict__ blobs_next)
+    const uint8_t *__restrict__ blobs_next, int T)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[DS_LDS_GU];
     __shared__ int head[K];
     const int nh = hint ? DR_WG : 0;
     const int b = blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (b >= nh + DR_WG) {   // lookahead reads
+    if (b >= nh + T * DR_WG) {   // lookahead reads
         if (wave == 0) {
             int my_id;
             float my_p, sel;
@@ -899,7 +907,11 @@ __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
         return;
     }
     const bool hinted = b < nh;
-    const int j = (b - (hinted ? 0 : nh)) / DG_SEGS, seg = b % DG_SEGS;
+    // token t of the plain sets (hints and the lookahead come with one token)
+    const int t = hinted ? 0 : (b - nh) / DR_WG;
+    const int bb = hinted ? b : (b - nh) % DR_WG;
+    const int j = bb / DG_SEGS, seg = bb % DG_SEGS;
+    const bool writer = bb == 0 && (hinted || !hint);   // writes token t's ids and weights
     // the hinted expert: a valid id and the first of its value in the hint
     int eh = -1;
     if (hinted) {
@@ -912,11 +924,11 @@ __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
     // the logits first, so that waiting for them does not wait for the rows
     TokLogits tl, tl2;
     if (wave == 0)
-        tl = load_logits(lraw, bias);
+        tl = load_logits(lraw + (size_t)t * E, bias);
     const bool predict = b == 0 && pred != nullptr;
     if (wave == 1 && predict)
         tl2 = load_logits(lraw2, bias2);
-    const float sc = xq.inv_rms[0];
+    const float sc = xq.inv_rms[t];
     const int s = 2 * wave + ((lane >> 4) >> 1);
     XOps xo;
     GuChunks ch;
@@ -928,9 +940,9 @@ __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
         int my_id;
         float my_p, sel;
         route_logits(tl, sc, bias != nullptr, my_id, my_p, sel);
-        if (b == 0 && lane < K) {
-            ids[lane] = my_id;
-            wout[lane] = my_p / renorm_den(sel);
+        if (writer && lane < K) {
+            ids[t * K + lane] = my_id;
+            wout[t * K + lane] = my_p / renorm_den(sel);
         }
         if (lane < K)
             head[lane] = my_id;
@@ -973,23 +985,25 @@ __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
     const int e = head[k];
     if (e < 0 || e >= E)   // not reached: the ten heads are expert ids
         return;
-    gateup_item<false>(make_int4(e, 0, 1, k), seg, 0, blobs, nullptr, xq, hq, 1, wl, part,
+    gateup_item<false>(make_int4(e, 0, 1, t * K + k), seg, 0, blobs, nullptr, xq, hq, T, wl, part,
                        nullptr);
 }
 
-hipError_t launch_decode_t1(const uint8_t *blobs, const float *lraw, const float *bias, XQ xq,
-                            HQ hq, int32_t *ids, float *w, float *y, float *res,
-                            const int32_t *hint, const float *lraw2, const float *bias2,
-                            int32_t *pred, const uint8_t *blobs_next, hipEvent_t ev0,
-                            hipEvent_t ev1, hipStream_t st)
+hipError_t launch_decode_routed(const uint8_t *blobs, const float *lraw, int T, const float *bias,
+                                XQ xq, HQ hq, int32_t *ids, float *w, float *y, float *res,
+                                const int32_t *hint, const float *lraw2, const float *bias2,
+                                int32_t *pred, const uint8_t *blobs_next, hipEvent_t ev0,
+                                hipEvent_t ev1, hipStream_t st)
 {
+    if (T > 1)   // hints and the lookahead come with one token only
+        hint = nullptr, lraw2 = nullptr;
     if (!lraw2)
         pred = nullptr;
     if (!pred)
         blobs_next = nullptr;
-    const int nwg = (hint ? 2 : 1) * DR_WG + (blobs_next ? K * XT_PER_SLOT : 0);
+    const int nwg = (hint ? DR_WG : 0) + T * DR_WG + (blobs_next ? K * XT_PER_SLOT : 0);
     void *args[] = {&blobs, &lraw, &bias, &xq, &hq, &ids, &w, &hint, &lraw2, &bias2, &pred,
-                    &blobs_next};
+                    &blobs_next, &T};
     hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_route_gateup),
                                       dim3(nwg), dim3(DG_THREADS), args, 0, st, ev0, nullptr, 0);
     if (e != hipSuccess)
@@ -997,8 +1011,9 @@ hipError_t launch_decode_t1(const uint8_t *blobs, const float *lraw, const float
     const int32_t *sexp = ids;
     const float *wc = w;
     void *dargs[] = {&blobs, &sexp, &hq, &wc, &y, &res};
-    return hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_down), dim3(DS_CHUNKS_PER_T),
-                              dim3(DS_THREADS), dargs, 0, st, nullptr, ev1, 0);
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_down),
+                              dim3(T * DS_CHUNKS_PER_T), dim3(DS_THREADS), dargs, 0, st, nullptr,
+                              ev1, 0);
 }
 
 hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const int32_t *slots,

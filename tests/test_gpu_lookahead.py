@@ -31,8 +31,9 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T,flags,with_bias", [(1, 0, False), (4, 0, False), (8, 0, False),
-                                               (1, 3, True), (4, 3, False), (8, 3, True)])
+@pytest.mark.parametrize("T,flags,with_bias", [(1, 0, False), (2, 0, False), (4, 0, False),
+                                               (8, 0, False), (1, 3, True), (3, 3, True),
+                                               (4, 3, False), (8, 3, True)])
 def test_lookahead_layer_equals_layer_and_predicts_the_next_route(T, flags, with_bias):
     import torch
     m = hz.qm()
