@@ -332,11 +332,10 @@ def measure(name, a, cpu_seconds):
     roof["frac"] = roof["achieved"] / roof["peak"]
     # A layer of up to 3 tokens runs its experts as two launches, gate/up then
     # dec_down; the events span both dispatches (the experts stage, all of its
-    # weight bytes).  For one token the gate/up launch, dec_route_gateup, also
-    # routes the token, so the span includes that.
+    # weight bytes).  The gate/up launch, dec_route_gateup, also routes the
+    # tokens, so the span includes that.
     roof["kernel"] = (("pq_gateup" if int8 else "pf_gateup") if prefill
-                      else "dec_route_gateup+dec_down" if T == 1
-                      else "dec_gateup+dec_down" if T <= 3 else "dec_experts")
+                      else "dec_route_gateup+dec_down" if T <= 3 else "dec_experts")
     # HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or null
     roof["traffic"] = traffic_from_profile(roof["kernel"], name)
     if roof["traffic"] is not None and not prefill:

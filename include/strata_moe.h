@@ -225,9 +225,8 @@ STRATA_API int strata_moe_layer_static(float *x, int T, const uint16_t *router, 
  * is, for decode-sized T, the fused experts kernel (gate/up, down and, in the
  * layer call, the combine), and for larger T the gate/up GEMM.  A layer call
  * of 1..3 tokens runs its experts as two launches (gate/up, then down with the
- * combine); there `start` is on the first and `stop` on the second, and
- * without the lookahead (or, for one token, with it) the first launch also
- * routes the tokens.
+ * combine); there `start` is on the first and `stop` on the second, and the
+ * first launch also routes the tokens.
  * The hook is used by one call and disarmed.  Events are the caller's; pass both NULL to
  * disarm.  Returns STRATA_E_ARG if only one is NULL.  Not for use under graph
  * capture. */

@@ -37,8 +37,7 @@ hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const i
                                  XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
                                  const float *w, float *y, float *res, const int32_t *pred,
                                  const uint8_t *blobs_next, int32_t *status, int wait_limit,
-                                 const int32_t *sexp, hipEvent_t ev0, hipEvent_t ev1,
-                                 hipStream_t st);
+                                 hipEvent_t ev0, hipEvent_t ev1, hipStream_t st);
 hipError_t launch_prefill_experts(const uint8_t *blobs, const int32_t *offsets,
                                   const int32_t *slots, const int32_t *active,
                                   const int32_t *mlist, const int32_t *nitems, int max_items,
@@ -182,7 +181,7 @@ int run_experts(const Carve &c, const uint8_t *blobs, const int32_t *offsets,
     if (is_decode(T)) {
         STRATA_TRY(launch_decode_experts(blobs, c.erec, slots, c.xq, c.hq, out, T, c.esync, nullptr,
                                          nullptr, nullptr, nullptr, nullptr, nullptr, c.status,
-                                         g_wait_limit.load(), nullptr, e0, e1, st));
+                                         g_wait_limit.load(), e0, e1, st));
     } else {
         if (!planned)
             STRATA_TRY(launch_plan(offsets, active, c.L.max_items, T, c.mlist, c.nitems, st));
@@ -243,7 +242,7 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
     float *w_o = w ? w : c.w;
     int32_t *pred_o = pred ? pred : c.pred;
     const int rms = flags & STRATA_RMSNORM;
-    if (T == 1 || (T <= ROUTED_T_MAX && !router2)) {   // the gate/up launch routes each token
+    if (T <= ROUTED_T_MAX) {   // the gate/up launch routes each token
         STRATA_TRY(launch_router_gemv(x, T, router, rms, c.logits, c.xq, router2, c.lraw2, st));
         hipEvent_t e0, e1;
         take_events(e0, e1);
@@ -275,7 +274,7 @@ int layer_impl(float *x, int T, const uint16_t *router, const float *bias, const
         STRATA_TRY(launch_decode_experts(blobs, c.erec, c.slots, c.xq, c.hq, c.out, T, c.esync,
                                          c.cdone, w_o, y, res ? x : nullptr,
                                          router2 ? pred_o : nullptr, router2 ? blobs2 : nullptr,
-                                         c.status, g_wait_limit.load(), ids_o, e0, e1, st));
+                                         c.status, g_wait_limit.load(), e0, e1, st));
         return STRATA_OK;
     }
     if ((rc = run_experts(c, blobs, c.offsets, c.slots, c.active, c.out, T, st, true,

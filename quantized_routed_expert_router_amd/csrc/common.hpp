@@ -41,9 +41,9 @@ constexpr int PF_NT_D = 256;                   // output rows per down work item
 constexpr int PF_NTILES_G = FF / PF_NT_G;      // 5
 constexpr int PF_NTILES_D = H / PF_NT_D;       // 10
 
-// Layer calls without the lookahead for T <= ROUTED_T_MAX route every token in
-// the gate/up launch (400 workgroups per token) instead of a top-k launch
-// (measured faster up to three tokens).
+// Layer calls for T <= ROUTED_T_MAX route every token in the gate/up launch
+// (400 workgroups per token) instead of a top-k launch (measured faster up to
+// three tokens).
 constexpr int ROUTED_T_MAX = 3;
 
 constexpr bool is_decode(int T) { return T <= DECODE_T_MAX; }

@@ -708,24 +708,20 @@ __global__ __launch_bounds__(EX_THREADS) void dec_experts(const uint8_t *__restr
     }
 }
 
-// ------------------------------------------------- T <= 3: two launches
-// For one to three tokens the layer runs the experts as two launches in
-// stream order instead (the kernel boundary publishes h, so nothing waits inside a
-// kernel): with the lookahead, dec_gateup runs the gate/up items above (plain
-// stores of h, no counters) and the lookahead workgroups, and without it
-// dec_route_gateup (below) routes each token and runs its ten heads' items;
-// then dec_down, with one workgroup per 16
-// output rows of the token, 5 waves with two of its slots each, lane (r, l)
-// taking row l of slot 2 w + r % 2's expert and block columns 2 j + r / 2 from
-// five 20-byte windows loaded straight into registers.  The two halves of
-// each row are added, the ten slot rows meet in LDS and are summed in routing
-// order with fma from 0, the order of the fused combine, so a token's results
-// are bitwise those of the fused kernel.  Measured faster up to T = 3, with
-// or without experts shared by the window's tokens; at T = 4 the fused kernel
-// is faster for tokens that share few experts (its down groups read an
-// expert's rows once for all the tokens that share it; here each token reads
-// its own).
-constexpr int DS_T_MAX = 3;                         // lookahead layer calls with T <= this split
+// ------------------------------- T <= ROUTED_T_MAX: two launches, no wait
+// For up to ROUTED_T_MAX tokens the layer runs the experts as two launches in
+// stream order instead (the kernel boundary publishes h, so nothing waits
+// inside a kernel): dec_route_gateup (below) routes each token and runs its
+// ten heads' gate/up items (plain stores of h, no counters), then dec_down,
+// with one workgroup per 16 output rows of a token, 5 waves with two of its
+// slots each, lane (r, l) taking row l of slot 2 w + r % 2's expert and block
+// columns 2 j + r / 2 from five 20-byte windows loaded straight into
+// registers.  The two halves of each row are added, the ten slot rows meet in
+// LDS and are summed in routing order with fma from 0, the order of the fused
+// combine, so a token's results are bitwise those of the fused kernel.  At
+// T = 4 the fused kernel is faster for tokens that share few experts (its
+// down groups read an expert's rows once for all the tokens that share it;
+// here each token reads its own).
 constexpr int DS_ROWS = 16;                         // output rows per workgroup
 constexpr int DS_WAVES = K / 2;                     // 5: two slots per wave
 constexpr int DS_THREADS = 64 * DS_WAVES;
@@ -786,32 +782,6 @@ __device__ inline float down_row_r(const DnW &w, int c0, const HOps &ho)
     return acc;
 }
 
-// Workgroup b < 40 amax runs gate/up item b (items beyond the call's na
-// active experts exit at once); the lookahead workgroups follow.
-__global__ __launch_bounds__(DG_THREADS) void dec_gateup(const uint8_t *__restrict__ blobs,
-                                                         const int4 *__restrict__ erec,
-                                                         const int32_t *__restrict__ slots, XQ xq,
-                                                         HQ hq, int T,
-                                                         const int32_t *__restrict__ pred,
-                                                         const uint8_t *__restrict__ blobs_next)
-{
-    __shared__ __attribute__((aligned(16))) uint8_t lds[DS_LDS_GU];
-    const int na = active_count(erec, T);
-    const int amax = T * K < E ? T * K : E;
-    const int b = blockIdx.x;
-    if (b < amax * DG_SEGS) {
-        if (b >= na * DG_SEGS)
-            return;
-        uint32_t *wl = reinterpret_cast<uint32_t *>(lds);
-        float(*part)[DG_ROWS] =
-            reinterpret_cast<float(*)[DG_ROWS]>(lds + (size_t)DG_ROWS * DG_RS * 4);
-        gateup_item<false>(erec[1 + b / DG_SEGS], b % DG_SEGS, 0, blobs, slots, xq, hq, T, wl,
-                           part, nullptr);
-    } else {
-        touch_next(b - amax * DG_SEGS, T * K, pred, blobs_next, lds);
-    }
-}
-
 // Workgroup b: token b / 160, output rows 16 (b % 160) .. + 15.  sexp[t K + k]
 // is the expert of slot (t, k) (a slot whose expert is outside 0..E-1 gives
 // zero rows).  y_t = sum_k w[t][k] o_k, stored and/or added to res.
@@ -853,8 +823,8 @@ __global__ __launch_bounds__(DS_THREADS) void dec_down(const uint8_t *__restrict
 }
 
 // ------------------------------- T <= ROUTED_T_MAX: the routing in every item
-// A layer call for up to ROUTED_T_MAX tokens without the lookahead (and one
-// token with it) has no top-k launch: each token gets 400 gate/up workgroups,
+// A layer call for up to ROUTED_T_MAX tokens has no top-k launch: each token
+// gets 400 gate/up workgroups,
 // and wave 0 of every one of them routes that token itself from the router's
 // logits -- the top-k kernel's code on the same inputs, so every workgroup of
 // a token gets the same ten ids and weights, bitwise.  A token's ten experts
@@ -877,9 +847,10 @@ __global__ __launch_bounds__(DS_THREADS) void dec_down(const uint8_t *__restrict
 // same arithmetic either way, so the results never depend on the hint.
 //
 // With the lookahead (lraw2: the next layer's raw logits of the same input),
-// wave 1 of workgroup 0 routes them to the next layer's predicted ids (pred),
-// and K * XT_PER_SLOT trailing workgroups, each routing them again, read the
-// predicted experts' blobs in blobs_next line by line.
+// wave 1 of each token's first workgroup routes them to the token's predicted
+// ids for the next layer (pred), and K * XT_PER_SLOT trailing workgroups per
+// token, each routing them again, read the predicted experts' blobs in
+// blobs_next line by line (an expert two tokens predict is read for each).
 constexpr int DR_WG = K * DG_SEGS;   // 400 workgroups per set
 
 __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
@@ -894,16 +865,17 @@ __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
     const int nh = hint ? DR_WG : 0;
     const int b = blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (b >= nh + T * DR_WG) {   // lookahead reads
+    if (b >= nh + T * DR_WG) {   // lookahead reads: K * XT_PER_SLOT workgroups per token
+        const int i = b - nh - T * DR_WG, tt = i / (K * XT_PER_SLOT);
         if (wave == 0) {
             int my_id;
             float my_p, sel;
-            route_token(lraw2, xq.inv_rms[0], bias2, my_id, my_p, sel);
+            route_token(lraw2 + (size_t)tt * E, xq.inv_rms[tt], bias2, my_id, my_p, sel);
             if (lane < K)
                 head[lane] = my_id;
         }
         __syncthreads();
-        touch_next(b - nh - DR_WG, K, head, blobs_next, lds);
+        touch_next(i % (K * XT_PER_SLOT), K, head, blobs_next, lds);
         return;
     }
     const bool hinted = b < nh;
@@ -925,9 +897,9 @@ __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
     TokLogits tl, tl2;
     if (wave == 0)
         tl = load_logits(lraw + (size_t)t * E, bias);
-    const bool predict = b == 0 && pred != nullptr;
+    const bool predict = writer && pred != nullptr;
     if (wave == 1 && predict)
-        tl2 = load_logits(lraw2, bias2);
+        tl2 = load_logits(lraw2 + (size_t)t * E, bias2);
     const float sc = xq.inv_rms[t];
     const int s = 2 * wave + ((lane >> 4) >> 1);
     XOps xo;
@@ -951,7 +923,7 @@ __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
         float my_p, sel;
         route_logits(tl2, sc, bias2 != nullptr, my_id, my_p, sel);
         if (lane < K)
-            pred[lane] = my_id;
+            pred[t * K + lane] = my_id;
     }
     uint32_t *wl = reinterpret_cast<uint32_t *>(lds);
     float(*part)[DG_ROWS] = reinterpret_cast<float(*)[DG_ROWS]>(lds + (size_t)DG_ROWS * DG_RS * 4);
@@ -995,13 +967,13 @@ hipError_t launch_decode_routed(const uint8_t *blobs, const float *lraw, int T, 
                                 int32_t *pred, const uint8_t *blobs_next, hipEvent_t ev0,
                                 hipEvent_t ev1, hipStream_t st)
 {
-    if (T > 1)   // hints and the lookahead come with one token only
-        hint = nullptr, lraw2 = nullptr;
+    if (T > 1)   // hints come with one token only
+        hint = nullptr;
     if (!lraw2)
         pred = nullptr;
     if (!pred)
         blobs_next = nullptr;
-    const int nwg = (hint ? DR_WG : 0) + T * DR_WG + (blobs_next ? K * XT_PER_SLOT : 0);
+    const int nwg = (hint ? DR_WG : 0) + T * DR_WG + (blobs_next ? T * K * XT_PER_SLOT : 0);
     void *args[] = {&blobs, &lraw, &bias, &xq, &hq, &ids, &w, &hint, &lraw2, &bias2, &pred,
                     &blobs_next, &T};
     hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_route_gateup),
@@ -1020,26 +992,13 @@ hipError_t launch_decode_experts(const uint8_t *blobs, const int4 *erec, const i
                                  XQ xq, HQ hq, float *out, int T, int32_t *sync, int32_t *cdone,
                                  const float *w, float *y, float *res, const int32_t *pred,
                                  const uint8_t *blobs_next, int32_t *status, int wait_limit,
-                                 const int32_t *sexp, hipEvent_t ev0, hipEvent_t ev1,
-                                 hipStream_t st)
+                                 hipEvent_t ev0, hipEvent_t ev1, hipStream_t st)
 {
     Combine cb{cdone, w, y, res};
     const int amax = T * K < E ? T * K : E;
     int32_t *gdone = sync + 1;
     if (!blobs_next)
         pred = nullptr;
-    if (sexp && cdone && T <= DS_T_MAX) {   // a layer call for up to 3 tokens: two launches
-        const dim3 grid(amax * DG_SEGS + (pred ? T * K * XT_PER_SLOT : 0));
-        void *args[] = {&blobs, &erec, &slots, &xq, &hq, &T, &pred, &blobs_next};
-        hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_gateup), grid,
-                                          dim3(DG_THREADS), args, 0, st, ev0, nullptr, 0);
-        if (e != hipSuccess)
-            return e;
-        void *dargs[] = {&blobs, &sexp, &hq, &w, &y, &res};
-        return hipExtLaunchKernel(reinterpret_cast<const void *>(&dec_down),
-                                  dim3(T * DS_CHUNKS_PER_T), dim3(DS_THREADS), dargs, 0, st,
-                                  nullptr, ev1, 0);
-    }
     const dim3 grid(amax * (DG_SEGS + EX_DN_PER_E) + (pred ? T * K * XT_PER_SLOT : 0));
     const dim3 block(EX_THREADS);
     if (ev0) {   // timed launch: the events carry the dispatch's own start and end

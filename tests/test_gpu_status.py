@@ -3,8 +3,8 @@ depended on it are NaN and the workspace's status word says so; a normal call
 leaves the word clear.  The give-up is forced from the host with a wait bound
 of one poll (strata_moe_set_wait_limit), so every kernel still ends normally.
 A layer call of up to three tokens runs its experts as two launches with no
-wait at all (without the lookahead, the first also routes the tokens): the
-bound changes nothing there."""
+wait at all (the first also routes the tokens): the bound changes nothing
+there."""
 import numpy as np
 import pytest
 
