@@ -909,9 +909,12 @@ __global__ __launch_bounds__(DG_THREADS) void dec_route_gateup(
         ch = gu_request(blobs, eh, seg);
     }
     if (wave == 0) {
+        // the writer needs all ten heads, and so does every workgroup of a
+        // hinted call; a plain workgroup needs heads 0 .. j only, so it can
+        // request its rows sooner
         int my_id;
         float my_p, sel;
-        route_logits(tl, sc, bias != nullptr, my_id, my_p, sel);
+        route_logits(tl, sc, bias != nullptr, my_id, my_p, sel, (writer || hint) ? K - 1 : j);
         if (writer && lane < K) {
             ids[t * K + lane] = my_id;
             wout[t * K + lane] = my_p / renorm_den(sel);

@@ -71,8 +71,11 @@ __device__ inline TokLogits load_logits(const float *lrow, const float *bias)
 // One token's routing in one wave from its scaled logits l (expert
 // lane + 64 i in l[i], bias included): softmax over the 512, then the ten
 // (p desc, id asc) heads in order.  Lane k < K gets the k-th id and its p;
-// sel (uniform) is the sum of the ten p.
-__device__ inline void route_scaled(float l[8], int &my_id, float &my_p, float &sel)
+// sel (uniform) is the sum of the ten p.  With kmax < K - 1 (uniform) the
+// selection stops after head kmax: lanes up to kmax hold the same ids and p
+// as a full routing, the others 0, and sel is incomplete.
+__device__ inline void route_scaled(float l[8], int &my_id, float &my_p, float &sel,
+                                    int kmax = K - 1)
 {
     const int lane = threadIdx.x & 63;
     float m = l[0];
@@ -115,6 +118,8 @@ __device__ inline void route_scaled(float l[8], int &my_id, float &my_p, float &
     sel = 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
+        if (k > kmax)
+            break;
         // the best head: the largest p, and among equal p the lowest id
         // (the one lane holding the maximum, else a reduction over ids)
         const int hb = __float_as_int(p[0]);
@@ -140,9 +145,10 @@ __device__ inline void route_scaled(float l[8], int &my_id, float &my_p, float &
     }
 }
 
-// The routing of logits loaded by load_logits: l = raw * sc (+ bias).
+// The routing of logits loaded by load_logits: l = raw * sc (+ bias), heads
+// up to kmax (route_scaled).
 __device__ inline void route_logits(const TokLogits &t, float sc, bool has_bias, int &my_id,
-                                    float &my_p, float &sel)
+                                    float &my_p, float &sel, int kmax = K - 1)
 {
     float l[8];
     if (has_bias) {
@@ -154,7 +160,7 @@ __device__ inline void route_logits(const TokLogits &t, float sc, bool has_bias,
         for (int i = 0; i < 8; ++i)
             l[i] = t.l[i] * sc;
     }
-    route_scaled(l, my_id, my_p, sel);
+    route_scaled(l, my_id, my_p, sel, kmax);
 }
 
 // One token's routing from its raw logits lrow[512]: l = lrow * sc (+ bias).
