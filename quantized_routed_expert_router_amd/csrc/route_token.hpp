@@ -19,9 +19,12 @@ __device__ inline bool ranks_before(float p, int e, float q, int f)
 // bits of floats that are >= 0 or negative (a removed candidate is -1) the
 // integer order is the float order, and the integer maximum needs no NaN
 // canonicalisation: each step is one v_max_i32 with the DPP operand folded in.
+// The block opens with a full window of 5 wait states (the DPP hazards: 2
+// after a VALU write of the source, 5 after one of EXEC), as it may be reached
+// by a branch whose other path it cannot see.
 __device__ inline int wave_max_i(int v)
 {
-    asm("s_nop 1\n\t"
+    asm("s_nop 4\n\t"
         "v_max_i32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
         "s_nop 1\n\t"
         "v_max_i32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
